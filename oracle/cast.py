@@ -1,0 +1,68 @@
+"""Scaled down-cast with amax capture (oracle).
+
+Test infrastructure only (see ``oracle/__init__``).
+
+What is computed (page "FP8 혼합 정밀도 LLM 학습" (hwlabs), sections
+"FP8이 어려운 이유" and "Delayed Scaling 동작 원리"; page "혼합 정밀도 학습"
+(itwiki), section "FP16 학습 루프", where the 16-bit working copy is made just
+before each op):
+
+* ``amax = max_i |x_i|`` of the *unscaled* input, recorded for the
+  delayed-scaling history.  It is computed as an unsigned maximum over the
+  FP32 bit patterns with the sign bit cleared, so the result is exact and
+  independent of reduction order, and NaN > inf > any finite value.  Every NaN
+  is first replaced by the canonical quiet NaN 0x7FC00000 (reading: the pages
+  are silent on NaN).  The result is max-accumulated into the caller's value.
+* ``t_i = fl32(x_i * scale)`` -- one FP32 multiply (16-bit inputs widen to FP32
+  exactly first).  Reading of the page's contradictory formula: the scale is a
+  multiplier, because ``scale = fp8_max / (margin * amax)`` only brings a
+  tensor into range as a multiplier.
+* ``y_i = round_fmt(t_i)``: FP16/BF16 round to nearest even and overflow to
+  +-inf (an overflowing FP16 gradient must surface as inf so that the step is
+  skipped); E4M3/E5M2 saturate, i.e. ``clip(t, -max, max)`` then round.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import formats as F
+
+CANON_NAN_BITS = np.uint32(0x7FC00000)
+
+
+def widen_to_f32_bits(codes, in_fmt: F.Fmt) -> np.ndarray:
+    """FP32 bit patterns of 16/32-bit input codes (exact widening)."""
+    codes = np.asarray(codes)
+    if in_fmt is F.F32:
+        return codes.astype(np.uint32)
+    v = F.decode(codes, in_fmt)
+    return F.encode_exact(v, F.F32)
+
+
+def amax_bits(f32_bits) -> np.uint32:
+    """Unsigned max of |x| bit patterns, NaN canonicalised (0 for empty)."""
+    a = np.asarray(f32_bits, dtype=np.uint32) & np.uint32(0x7FFFFFFF)
+    a = np.where(a > np.uint32(0x7F800000), CANON_NAN_BITS, a)
+    return np.uint32(a.max()) if a.size else np.uint32(0)
+
+
+def cast(codes, in_fmt: F.Fmt, out_fmt: F.Fmt, scale: float | None = None,
+         amax_prior_bits: int = 0):
+    """Scaled cast of an array of input codes.
+
+    Returns ``(out_codes, amax_bits)`` where ``amax_bits`` is
+    ``max(amax_prior_bits, amax(|x|))`` as an FP32 bit pattern.
+    """
+    bits = widen_to_f32_bits(codes, in_fmt)
+    am = np.uint32(max(int(amax_prior_bits), int(amax_bits(bits))))
+    x = F.decode(bits, F.F32)
+    t = x if scale is None else F.f32(x * np.float64(scale))
+    return F.encode(t, out_fmt), am
+
+
+def cast_values(x_f32_values, out_fmt: F.Fmt, scale: float | None = None):
+    """Convenience: cast FP32 values (float64 holding FP32-representable
+    numbers) and return the rounded output values (float64)."""
+    x = np.asarray(x_f32_values, dtype=np.float64)
+    t = x if scale is None else F.f32(x * np.float64(scale))
+    return F.round_to(t, out_fmt)

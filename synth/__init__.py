@@ -1,0 +1,97 @@
+"""Seeded synthetic inputs shared by the oracle-side tests and the GPU side.
+
+This module draws random numbers and stores them in the input formats of the
+workloads (FP32, and 16-bit codes made with NumPy / PyTorch's own
+conversions).  It holds none of the mixed-precision method's arithmetic: no
+scaled casts, no amax, no recipe, no optimizer, no quantizer.  Both the oracle
+and the HIP path consume the bytes it returns.
+
+Workload shapes and laws (each documented where the workload is defined):
+* mlp:      x ~ N(0,1) [64 x 512] FP32, labels U{0..9}, nn.Linear-default
+            uniform init U(+-1/sqrt(fan_in)) for weights and biases.
+* adam:     theta ~ N(0, 0.02) FP32, grads 1e-4 * N(0,1) * exp(2 Z) scaled by the
+            live loss scale and stored FP16, 4 injected non-finite steps of 200.
+* gemm:     activations ~ N(0,1) BF16, weights ~ N(0, 0.02) FP32,
+            output gradients ~ N(0,1) BF16.
+* fp8:      activations sigma_t * Student-t(3) BF16 with sigma_t = 1.02^t,
+            output gradients 1e-3 * Student-t(3) BF16.
+* nvfp4:    N(0,1) BF16 with 0.1 % of entries set to +-50.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "rng", "normal_f32", "student_t_f32", "to_bf16_codes", "to_f16_codes",
+    "f32_bits", "bf16_codes_normal", "outlier_bf16_codes", "edge_f32_values",
+    "injection_schedule",
+]
+
+
+def rng(seed: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def normal_f32(seed: int, shape, std: float = 1.0, mean: float = 0.0) -> np.ndarray:
+    return (rng(seed).standard_normal(shape, dtype=np.float64) * std + mean).astype(np.float32)
+
+
+def student_t_f32(seed: int, shape, nu: float = 3.0, scale: float = 1.0) -> np.ndarray:
+    return (rng(seed).standard_t(nu, size=shape) * scale).astype(np.float32)
+
+
+def to_bf16_codes(x_f32: np.ndarray) -> np.ndarray:
+    """BF16 codes of FP32 data via PyTorch's CPU conversion (input making only)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x_f32, dtype=np.float32))
+    return t.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def to_f16_codes(x_f32: np.ndarray) -> np.ndarray:
+    """FP16 codes via NumPy's IEEE conversion (input making only)."""
+    return np.asarray(x_f32, dtype=np.float32).astype(np.float16).view(np.uint16)
+
+
+def f32_bits(x_f32: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(x_f32, dtype=np.float32).view(np.uint32)
+
+
+def bf16_codes_normal(seed: int, shape, std: float = 1.0) -> np.ndarray:
+    return to_bf16_codes(normal_f32(seed, shape, std))
+
+
+def outlier_bf16_codes(seed: int, shape, frac: float = 1e-3, mag: float = 50.0) -> np.ndarray:
+    """N(0,1) with a seeded fraction of entries replaced by +-mag."""
+    g = rng(seed)
+    x = g.standard_normal(shape).astype(np.float32)
+    n = x.size
+    k = int(round(frac * n))
+    idx = g.choice(n, size=k, replace=False)
+    sgn = np.where(g.random(k) < 0.5, -1.0, 1.0).astype(np.float32)
+    x.reshape(-1)[idx] = sgn * np.float32(mag)
+    return to_bf16_codes(x)
+
+
+def edge_f32_values() -> np.ndarray:
+    """Special FP32 inputs: signed zeros, subnormals, format boundaries and
+    rounding ties of the 16- and 8-bit formats, inf and NaN."""
+    v = [0.0, -0.0, 1.0, -1.0, 2.0 ** -149, -2.0 ** -149, 2.0 ** -126,
+         2.0 ** -24, 2.0 ** -25, 1.5 * 2.0 ** -25, 2.0 ** -14, 65504.0, 65519.0,
+         65520.0, -65520.0, 448.0, 464.0, 465.0, 480.0, 2.0 ** -9, 2.0 ** -10,
+         1.5 * 2.0 ** -10, 57344.0, 61440.0, 1e30, -1e30, 3.4e38,
+         1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, 1.0 + 2.0 ** -11, 1.0 + 2.0 ** -12,
+         np.inf, -np.inf, np.nan, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0,
+         7.0, 2.0 ** -6, 2.0 ** -7 * 1.5, 0.1, -0.1, 3.14159]
+    return np.array(v, dtype=np.float32)
+
+
+def injection_schedule(seed: int, n_steps: int = 200, n_inject: int = 4,
+                       n_params: int = 1 << 31):
+    """(step, index, value) triples for injected non-finite gradients: exactly
+    ``n_inject`` steps drawn without replacement; the k-th writes
+    (+inf, NaN, -inf, NaN)[k % 4] at one seeded index."""
+    g = rng(seed)
+    steps = np.sort(g.choice(n_steps, size=n_inject, replace=False))
+    vals = [np.inf, np.nan, -np.inf, np.nan]
+    return [(int(s), int(g.integers(0, n_params)), vals[k % 4])
+            for k, s in enumerate(steps)]

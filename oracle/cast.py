@@ -13,7 +13,7 @@ before each op):
   independent of reduction order, and NaN > inf > any finite value.  Every NaN
   is first replaced by the canonical quiet NaN 0x7FC00000 (reading: the pages
   are silent on NaN).  The result is max-accumulated into the caller's value.
-* ``t_i = fl32(x_i * scale)`` -- one FP32 multiply (16-bit inputs widen to FP32
+* ``t_i = fl32(x_i * scale)`` with ``scale`` an FP32 value -- one FP32 multiply (16-bit inputs widen to FP32
   exactly first).  Reading of the page's contradictory formula: the scale is a
   multiplier, because ``scale = fp8_max / (margin * amax)`` only brings a
   tensor into range as a multiplier.
@@ -56,7 +56,8 @@ def cast(codes, in_fmt: F.Fmt, out_fmt: F.Fmt, scale: float | None = None,
     bits = widen_to_f32_bits(codes, in_fmt)
     am = np.uint32(max(int(amax_prior_bits), int(amax_bits(bits))))
     x = F.decode(bits, F.F32)
-    t = x if scale is None else F.f32(x * np.float64(scale))
+    # the scale is an FP32 value (a device-resident FP32 multiplier)
+    t = x if scale is None else F.f32(x * F.f32(np.float64(scale)))
     return F.encode(t, out_fmt), am
 
 
@@ -64,5 +65,5 @@ def cast_values(x_f32_values, out_fmt: F.Fmt, scale: float | None = None):
     """Convenience: cast FP32 values (float64 holding FP32-representable
     numbers) and return the rounded output values (float64)."""
     x = np.asarray(x_f32_values, dtype=np.float64)
-    t = x if scale is None else F.f32(x * np.float64(scale))
+    t = x if scale is None else F.f32(x * F.f32(np.float64(scale)))
     return F.round_to(t, out_fmt)

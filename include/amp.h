@@ -1,0 +1,251 @@
+/*
+ * amp.h -- C ABI of the MI355X (gfx950) mixed-precision training hot path.
+ *
+ * Three parts, as the pages describe mixed-precision training:
+ *   1. scaled down-casts to FP16 / BF16 / FP8 (E4M3 forward, E5M2 backward)
+ *      with amax capture and a delayed-scaling history, plus the NVFP4
+ *      two-level quantizer;
+ *   2. low-precision GEMM with FP32 accumulation (forward, dgrad, wgrad);
+ *   3. the fused FP32-master AdamW step with dynamic loss scaling.
+ *
+ * Conventions for every call
+ * --------------------------
+ *  - All tensor arguments are DEVICE pointers owned by the caller; the
+ *    library never allocates, frees or retains them.  Host structs passed by
+ *    pointer are read during the call only.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *    enqueues work on that stream and never synchronises the host.
+ *  - Matrices are row-major with a leading dimension (row stride) given in
+ *    ELEMENTS (for AMP_E2M1X2: in bytes, i.e. pairs of elements).
+ *  - Arguments are validated before anything is enqueued; on error nothing
+ *    is launched and a negative amp_status is returned.  AMP_EHIP reports a
+ *    failed launch; amp_last_hip_error() gives the hipError_t of the calling
+ *    thread's last failure.  No C++ exception crosses this boundary.
+ *  - Numerical events (inf/NaN, saturation) are data, not errors.
+ *  - Scalar state (loss scale, overflow flag, Adam step, FP8 scales) lives in
+ *    device memory so that no step needs a host round trip.
+ *  - Calls that share state buffers must be ordered on one stream (or
+ *    synchronised by the caller); concurrent calls on distinct buffers are
+ *    independent.
+ */
+#ifndef AMP_H_
+#define AMP_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AMP_ABI_VERSION 1
+
+typedef enum {
+  AMP_OK = 0,
+  AMP_EINVAL = -1,       /* bad pointer, size, stride or enum value        */
+  AMP_EUNSUPPORTED = -2, /* valid but unsupported dtype/layout combination */
+  AMP_EHIP = -3,         /* a HIP runtime call or kernel launch failed     */
+  AMP_ENODEVICE = -4     /* the current device is not a gfx950 GPU         */
+} amp_status;
+
+typedef enum {
+  AMP_F32 = 0,
+  AMP_F16 = 1,   /* IEEE binary16, 1/5/10                         */
+  AMP_BF16 = 2,  /* bfloat16, 1/8/7                               */
+  AMP_E4M3 = 3,  /* OCP FP8 E4M3 "FN": max 448, no inf            */
+  AMP_E5M2 = 4,  /* OCP FP8 E5M2: max 57344, IEEE-style inf/NaN   */
+  AMP_E2M1X2 = 5 /* two FP4 E2M1 codes per byte, low nibble first */
+} amp_dtype;
+
+typedef enum { AMP_OP_N = 0, AMP_OP_T = 1 } amp_op;
+typedef enum { AMP_ROUND_RNE = 0, AMP_ROUND_SR = 1 } amp_round;
+
+/* Device-resident loss-scaler + Adam counter state (40 bytes).
+ * Page "혼합 정밀도 학습" (itwiki), section "손실 스케일링": start at 2^16, halve
+ * and skip on inf/NaN, double after 2000 clean steps. */
+typedef struct {
+  float scale;            /* loss scale S (a power of two in practice)     */
+  int32_t growth_tracker; /* clean steps since the last change of S        */
+  int32_t found_inf;      /* set to 1 by the overflow check, 0 by update   */
+  int32_t pad_;
+  int64_t adam_step;      /* applied optimizer steps                       */
+  double beta1_pow;       /* beta1^adam_step (running float64 product)     */
+  double beta2_pow;       /* beta2^adam_step                               */
+} amp_scaler_state;
+
+typedef struct {
+  float growth_factor;     /* 2.0   */
+  float backoff_factor;    /* 0.5   */
+  int32_t growth_interval; /* 2000  */
+} amp_scaler_params;
+
+typedef struct {
+  double lr, beta1, beta2, eps, weight_decay;
+} amp_adamw_hparams;
+
+/* Device-resident per-tensor FP8 metadata (16 bytes); the amax history is a
+ * separate float array of `history_len` entries per tensor.
+ * Page "FP8 혼합 정밀도 LLM 학습" (hwlabs), section "Delayed Scaling 동작 원리". */
+typedef struct {
+  float amax_cur;  /* max |x| accumulated by this step's casts (bit-max)   */
+  float scale;     /* multiplier used by the casts of the next step        */
+  float scale_inv; /* 1/scale, the dequantisation factor for GEMM epilogue */
+  int32_t pos;     /* ring position of the next history entry              */
+} amp_fp8_meta;
+
+typedef enum { AMP_AMAX_MAX = 0, AMP_AMAX_MOST_RECENT = 1 } amp_amax_algo;
+
+typedef struct {
+  float fp8_max;       /* 448 (E4M3) or 57344 (E5M2)  */
+  float margin;        /* 1.0 recommended             */
+  int32_t history_len; /* 1024 by default             */
+  int32_t algo;        /* amp_amax_algo               */
+} amp_delayed_recipe;
+
+/* NVFP4 block scales of one GEMM operand (the quantizer's output). */
+typedef struct {
+  const uint8_t* scales; /* E4M3 codes: [rows, K/16], or [rows/16, K/16] if block2d */
+  int64_t ld;            /* row stride of `scales` in bytes                        */
+  int32_t block2d;       /* 1: one scale per 16x16 tile                             */
+  int32_t pad_;
+} amp_block_scales;
+
+/* ------------------------------------------------------------------------ */
+
+/* Library version, status text and the calling thread's last HIP error. */
+int amp_abi_version(void);
+const char* amp_status_string(int status);
+int amp_last_hip_error(void);
+
+/* amp_cast -- scaled down-cast with amax capture.
+ * Sources: itwiki "FP16 학습 루프" (the 16-bit copy made just before each op);
+ * hwlabs "FP8이 어려운 이유" (per-tensor scale, clip to [-448, 448]) and
+ * "Delayed Scaling 동작 원리" (amax recorded each step, tensor read once).
+ *
+ *   y[i][j]   = round_yt( fl32(x[i][j] * scale) )
+ *   y_t[j][i] = the same value (optional transposed copy)
+ *   *d_amax   = max(*d_amax, max |x|)   (unscaled input; FP32 bit-pattern max,
+ *                                        NaN dominates, canonical 0x7FC00000)
+ *
+ * x:      [rows, cols] of xt in {F32, F16, BF16}, row stride ldx >= cols.
+ * y:      [rows, cols] of yt in {F16, BF16, E4M3, E5M2}, stride ldy; may be NULL
+ *         if y_t is given.
+ * y_t:    [cols, rows] of yt, stride ldy_t >= rows; NULL for none.
+ * d_scale: device FP32 multiplier; NULL means 1 (no multiply).
+ * d_amax:  device FP32 accumulated with max; NULL skips the reduction.  The
+ *          caller (or amp_delayed_scaling_update) resets it.
+ * Rounding: nearest-even.  FP16/BF16 overflow to +-inf and NaN -> canonical
+ * quiet NaN; E4M3/E5M2 saturate to +-max (inf included) and NaN -> 0x7F.
+ * rows or cols == 0 is a no-op. */
+int amp_cast(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
+             void* y, int yt, int64_t ldy, void* y_t, int64_t ldy_t,
+             const float* d_scale, float* d_amax, void* stream);
+
+/* amp_gemm -- C = out_cast( alpha_A * alpha_B * op(A) @ op(B) ), FP32 accumulate.
+ * Sources: itwiki "FP32 누산과 연산별 정밀도"; hwlabs "GEMM 누적 정밀도 문제";
+ * marovi "La receta de precisión mixta".
+ *
+ * op(A) is [M, K]: opA == N: A stored [M, K] (stride lda >= K);
+ *                  opA == T: A stored [K, M] (stride lda >= M).
+ * op(B) is [K, N]: opB == N: B stored [K, N] (stride ldb >= N);
+ *                  opB == T: B stored [N, K] (stride ldb >= K).
+ * C is [M, N] of ct in {F32, F16, BF16}, stride ldc >= N.
+ * Supported operand types:
+ *   at == bt in {F16, BF16}           any opA/opB;
+ *   at, bt in {E4M3, E5M2}            opA == N, opB == T (K-contiguous; the
+ *                                      cast's transposed copy provides it);
+ *   at == bt == E2M1X2 (NVFP4)        opA == N, opB == T, with bsA/bsB block
+ *                                      scales; K % 16 == 0.
+ * d_alphaA / d_alphaB: device FP32 factors (FP8: the tensors' scale_inv;
+ * NVFP4: 1/tensor_enc); NULL means 1.  bsA/bsB must be NULL unless NVFP4.
+ * M, N or K == 0 is handled (K == 0 writes zeros). */
+int amp_gemm(int opA, int opB, int64_t M, int64_t N, int64_t K,
+             const void* A, int at, int64_t lda, const float* d_alphaA,
+             const void* B, int bt, int64_t ldb, const float* d_alphaB,
+             void* C, int ct, int64_t ldc,
+             const amp_block_scales* bsA, const amp_block_scales* bsB,
+             void* stream);
+
+/* amp_scaler_init -- sets scale = init_scale, growth_tracker = found_inf = 0,
+ * adam_step = 0, beta pows = 1 (GradScaler(init_scale) + fresh AdamW). */
+int amp_scaler_init(amp_scaler_state* d_state, float init_scale, void* stream);
+
+/* amp_optimizer_step -- unscale by 1/S, check every gradient for inf/NaN,
+ * and, only if none is found, apply AdamW to the FP32 master weights and
+ * moments and re-round the 16-bit working copy.
+ * Sources: itwiki "FP32 마스터 가중치" (update the FP32 copy, round16 from it;
+ * 16 bytes/parameter), "손실 스케일링" (g = fp32(grad)/S; skip on inf/NaN);
+ * marovi "Escalado dinámico de pérdida", "Operaciones que permanecen en FP32".
+ *
+ * master, m, v: [n] FP32, updated in place.
+ * grads: [n] of gt in {F16, BF16, F32} (scaled by S).
+ * w16:   [n] of wt in {F16, BF16}, overwritten with round(master); may be NULL.
+ * flags: AMP_OPT_SKIP_CHECK -- the caller already OR-ed the overflow flag into
+ *        d_state->found_inf (e.g. from its own gradient producer); no sweep.
+ * Per element (FP32, no fused multiply-add):
+ *   g = f32(grad) * (1/S); m = b1*m + (1-b1)*g; v = b2*v + (1-b2)*(g*g);
+ *   d = sqrt(v) * rbc2 + eps; master = master*(1-lr*wd) - step*(m/d)
+ * with step = lr/(1-b1^t), rbc2 = 1/sqrt(1-b2^t) from float64 state.
+ * On overflow nothing is written and adam_step is unchanged.  Follow with
+ * amp_scaler_update, which consumes and clears found_inf. */
+#define AMP_OPT_SKIP_CHECK 1
+int amp_optimizer_step(float* master, float* m, float* v, const void* grads, int gt,
+                       void* w16, int wt, int64_t n, const amp_adamw_hparams* hp,
+                       amp_scaler_state* d_state, int flags, void* stream);
+
+/* amp_check_overflow -- OR (any non-finite element of x) into
+ * d_state->found_inf.  x: [n] of xt in {F16, BF16, F32}.  Used when several
+ * gradient buffers feed one optimizer step (then step with SKIP_CHECK). */
+int amp_check_overflow(const void* x, int xt, int64_t n, amp_scaler_state* d_state,
+                       void* stream);
+
+/* amp_scaler_update -- on found_inf: scale *= backoff, tracker = 0; else
+ * tracker += 1 and at growth_interval: scale *= growth, tracker = 0.  Then
+ * found_inf = 0.  No floor on the scale.  p == NULL uses (2, 0.5, 2000). */
+int amp_scaler_update(amp_scaler_state* d_state, const amp_scaler_params* p, void* stream);
+
+/* amp_fp8_meta_init -- n metas: amax_cur 0, scale = scale_inv = 1, pos 0,
+ * and d_history[n * history_len] zero-filled. */
+int amp_fp8_meta_init(amp_fp8_meta* d_metas, float* d_history, int32_t n,
+                      int32_t history_len, void* stream);
+
+/* amp_delayed_scaling_update -- for each of n metas (history of meta i at
+ * d_history + i*history_len):
+ *   history[pos] = amax_cur;
+ *   amax_max = max(history) (AMP_AMAX_MAX) or history[pos] (MOST_RECENT);
+ *   if amax_max is finite and > 0:
+ *       scale = fp8_max / (margin * amax_max); scale_inv = 1/scale;
+ *   pos = (pos + 1) % history_len; amax_cur = 0.
+ * Source: hwlabs "Delayed Scaling 동작 원리" and "도입 체크리스트". */
+int amp_delayed_scaling_update(amp_fp8_meta* d_metas, float* d_history, int32_t n,
+                               const amp_delayed_recipe* r, void* stream);
+
+/* amp_nvfp4_quantize -- NVFP4 two-level quantization of one GEMM operand.
+ * Source: page "Pretraining Large Language Models with NVFP4", sections 2.1
+ * (E2M1 elements, 16-element E4M3 block scales, FP32 tensor scale) and 2.2
+ * items 2-4 (16x16 random Hadamard transform on weight-gradient inputs,
+ * 16x16 weight blocks, stochastic rounding of gradients).
+ *
+ * x: [rows, cols] of xt in {BF16, F32}, stride ldx.  The quantized operand is
+ *    op = x (transpose == 0) or x^T (transpose == 1), of shape [R, K]; blocks
+ *    and the optional RHT run along K.  R and K must be multiples of 16.
+ * rht: apply z = H16 diag(s) / 4 to each 16-chunk along K, s from Philox4x32-10
+ *    (key rht_seed, counter (0,0,1,0), word 0).
+ * block2d: one scale per 16x16 tile of op (weights) instead of per 1x16.
+ * rnd: AMP_ROUND_RNE or AMP_ROUND_SR (Philox4x32-10, key sr_seed, element
+ *    index idx = r*K + k: counter (idx>>2), word idx&3, u = (w>>8)*2^-24).
+ * q: [R, K/2] bytes, two E2M1 codes per byte, low nibble = lower k.
+ * scales: E4M3 codes [R, K/16] (or [R/16, K/16]), contiguous.
+ * d_tensor: 3 device floats written as {amax of z, enc = 2688/amax (1 if the
+ *    amax is 0 or not finite), dec = 1/enc}; pass &d_tensor[2] as the GEMM
+ *    alpha.
+ * Element: b = block amax; S = E4M3(fl32(fl32(b/6)*enc)); y = fl32(z*fl32(enc/S));
+ *    code = E2M1(y) saturating at 6 (S == 0 gives code 0). */
+int amp_nvfp4_quantize(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
+                       int transpose, int block2d, int rht, uint64_t rht_seed,
+                       int rnd, uint64_t sr_seed, uint8_t* q, uint8_t* scales,
+                       float* d_tensor, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* AMP_H_ */

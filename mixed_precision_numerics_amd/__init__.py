@@ -1,0 +1,203 @@
+"""MI355X (gfx950) mixed-precision training hot path.
+
+A thin ctypes binding of ``libamp.so`` (built from ``csrc/`` by
+``mixed_precision_numerics_amd.build``).  Every function has the name and
+argument order of the C entry point declared in ``include/amp.h``; this module
+only marshals arguments (device pointers from torch tensors or ints, host
+structs, the stream handle) and turns a negative status into ``AmpError``.
+All arithmetic runs in the HIP kernels.  There is no CPU fallback: when the
+library is missing or no gfx950 device is current, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+__all__ = [
+    "F32", "F16", "BF16", "E4M3", "E5M2", "E2M1X2", "OP_N", "OP_T", "ROUND_RNE", "ROUND_SR",
+    "AMAX_MAX", "AMAX_MOST_RECENT", "OPT_SKIP_CHECK", "AmpError", "AdamWHParams",
+    "ScalerParams", "DelayedRecipe", "BlockScales", "SCALER_STATE_DTYPE", "FP8_META_DTYPE",
+    "lib_path", "load", "amp_abi_version", "amp_status_string", "amp_last_hip_error",
+    "amp_cast", "amp_gemm", "amp_scaler_init", "amp_optimizer_step", "amp_check_overflow",
+    "amp_scaler_update", "amp_fp8_meta_init", "amp_delayed_scaling_update",
+    "amp_nvfp4_quantize",
+]
+
+F32, F16, BF16, E4M3, E5M2, E2M1X2 = 0, 1, 2, 3, 4, 5
+OP_N, OP_T = 0, 1
+ROUND_RNE, ROUND_SR = 0, 1
+AMAX_MAX, AMAX_MOST_RECENT = 0, 1
+OPT_SKIP_CHECK = 1
+
+# Device-resident state layouts (mirror the C structs; for reading back).
+SCALER_STATE_DTYPE = np.dtype([("scale", "<f4"), ("growth_tracker", "<i4"),
+                               ("found_inf", "<i4"), ("pad", "<i4"), ("adam_step", "<i8"),
+                               ("beta1_pow", "<f8"), ("beta2_pow", "<f8")])
+FP8_META_DTYPE = np.dtype([("amax_cur", "<f4"), ("scale", "<f4"), ("scale_inv", "<f4"),
+                           ("pos", "<i4")])
+assert SCALER_STATE_DTYPE.itemsize == 40 and FP8_META_DTYPE.itemsize == 16
+
+
+class AmpError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        lib = load()
+        msg = lib.amp_status_string(status).decode()
+        if status == -3:
+            msg += f" (hipError_t {lib.amp_last_hip_error()})"
+        super().__init__(f"{fn}: {msg} [{status}]")
+        self.status = status
+
+
+class AdamWHParams(ctypes.Structure):
+    _fields_ = [("lr", ctypes.c_double), ("beta1", ctypes.c_double), ("beta2", ctypes.c_double),
+                ("eps", ctypes.c_double), ("weight_decay", ctypes.c_double)]
+
+
+class ScalerParams(ctypes.Structure):
+    _fields_ = [("growth_factor", ctypes.c_float), ("backoff_factor", ctypes.c_float),
+                ("growth_interval", ctypes.c_int32)]
+
+
+class DelayedRecipe(ctypes.Structure):
+    _fields_ = [("fp8_max", ctypes.c_float), ("margin", ctypes.c_float),
+                ("history_len", ctypes.c_int32), ("algo", ctypes.c_int32)]
+
+
+class BlockScales(ctypes.Structure):
+    _fields_ = [("scales", ctypes.c_void_p), ("ld", ctypes.c_int64),
+                ("block2d", ctypes.c_int32), ("pad_", ctypes.c_int32)]
+
+
+_P, _I, _I64, _U64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_uint64
+_SIGS = {
+    "amp_abi_version": ([], _I),
+    "amp_status_string": ([_I], ctypes.c_char_p),
+    "amp_last_hip_error": ([], _I),
+    "amp_cast": ([_P, _I, _I64, _I64, _I64, _P, _I, _I64, _P, _I64, _P, _P, _P], _I),
+    "amp_gemm": ([_I, _I, _I64, _I64, _I64, _P, _I, _I64, _P, _P, _I, _I64, _P, _P, _I, _I64,
+                  _P, _P, _P], _I),
+    "amp_scaler_init": ([_P, ctypes.c_float, _P], _I),
+    "amp_optimizer_step": ([_P, _P, _P, _P, _I, _P, _I, _I64, _P, _P, _I, _P], _I),
+    "amp_check_overflow": ([_P, _I, _I64, _P, _P], _I),
+    "amp_scaler_update": ([_P, _P, _P], _I),
+    "amp_fp8_meta_init": ([_P, _P, ctypes.c_int32, ctypes.c_int32, _P], _I),
+    "amp_delayed_scaling_update": ([_P, _P, ctypes.c_int32, _P, _P], _I),
+    "amp_nvfp4_quantize": ([_P, _I, _I64, _I64, _I64, _I, _I, _I, _U64, _I, _U64, _P, _P, _P,
+                            _P], _I),
+}
+
+_lib = None
+
+
+def lib_path() -> str:
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libamp.so")
+
+
+def load():
+    """Load ``libamp.so`` (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        p = lib_path()
+        if not os.path.exists(p):
+            raise RuntimeError(f"{p} is missing: build it with "
+                               "`python -m mixed_precision_numerics_amd.build`")
+        lib = ctypes.CDLL(p)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = lib
+    return _lib
+
+
+def _ptr(x) -> int | None:
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    if isinstance(x, ctypes.Structure):
+        return ctypes.addressof(x)
+    raise TypeError(f"cannot take a device pointer from {type(x)!r}")
+
+
+def _stream(s) -> int | None:
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise AmpError(fn, status)
+
+
+def amp_abi_version() -> int:
+    return load().amp_abi_version()
+
+
+def amp_status_string(status: int) -> str:
+    return load().amp_status_string(status).decode()
+
+
+def amp_last_hip_error() -> int:
+    return load().amp_last_hip_error()
+
+
+def amp_cast(x, xt, rows, cols, ldx, y, yt, ldy, y_t=None, ldy_t=0, d_scale=None, d_amax=None,
+             stream=None):
+    _check("amp_cast", load().amp_cast(_ptr(x), xt, rows, cols, ldx, _ptr(y), yt, ldy,
+                                       _ptr(y_t), ldy_t, _ptr(d_scale), _ptr(d_amax),
+                                       _stream(stream)))
+
+
+def amp_gemm(opA, opB, M, N, K, A, at, lda, d_alphaA, B, bt, ldb, d_alphaB, C, ct, ldc,
+             bsA=None, bsB=None, stream=None):
+    _check("amp_gemm", load().amp_gemm(
+        opA, opB, M, N, K, _ptr(A), at, lda, _ptr(d_alphaA), _ptr(B), bt, ldb, _ptr(d_alphaB),
+        _ptr(C), ct, ldc, ctypes.byref(bsA) if bsA is not None else None,
+        ctypes.byref(bsB) if bsB is not None else None, _stream(stream)))
+
+
+def amp_scaler_init(d_state, init_scale=65536.0, stream=None):
+    _check("amp_scaler_init", load().amp_scaler_init(_ptr(d_state), init_scale, _stream(stream)))
+
+
+def amp_optimizer_step(master, m, v, grads, gt, w16, wt, n, hp: AdamWHParams, d_state,
+                       flags=0, stream=None):
+    _check("amp_optimizer_step", load().amp_optimizer_step(
+        _ptr(master), _ptr(m), _ptr(v), _ptr(grads), gt, _ptr(w16), wt, n, ctypes.byref(hp),
+        _ptr(d_state), flags, _stream(stream)))
+
+
+def amp_check_overflow(x, xt, n, d_state, stream=None):
+    _check("amp_check_overflow", load().amp_check_overflow(_ptr(x), xt, n, _ptr(d_state),
+                                                           _stream(stream)))
+
+
+def amp_scaler_update(d_state, p: ScalerParams | None = None, stream=None):
+    _check("amp_scaler_update", load().amp_scaler_update(
+        _ptr(d_state), ctypes.byref(p) if p is not None else None, _stream(stream)))
+
+
+def amp_fp8_meta_init(d_metas, d_history, n, history_len, stream=None):
+    _check("amp_fp8_meta_init", load().amp_fp8_meta_init(_ptr(d_metas), _ptr(d_history), n,
+                                                         history_len, _stream(stream)))
+
+
+def amp_delayed_scaling_update(d_metas, d_history, n, r: DelayedRecipe, stream=None):
+    _check("amp_delayed_scaling_update", load().amp_delayed_scaling_update(
+        _ptr(d_metas), _ptr(d_history), n, ctypes.byref(r), _stream(stream)))
+
+
+def amp_nvfp4_quantize(x, xt, rows, cols, ldx, transpose, block2d, rht, rht_seed, rnd, sr_seed,
+                       q, scales, d_tensor, stream=None):
+    _check("amp_nvfp4_quantize", load().amp_nvfp4_quantize(
+        _ptr(x), xt, rows, cols, ldx, int(transpose), int(block2d), int(rht), rht_seed, rnd,
+        sr_seed, _ptr(q), _ptr(scales), _ptr(d_tensor), _stream(stream)))

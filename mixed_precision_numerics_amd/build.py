@@ -1,0 +1,69 @@
+"""Build the HIP library ``libamp.so`` for gfx950 in-tree.
+
+Every ``csrc/*.hip`` and ``csrc/*.cpp`` is compiled by hipcc into ``_build/``
+(in parallel) and linked into ``mixed_precision_numerics_amd/libamp.so``.
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import glob
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libamp.so")
+ARCH = "gfx950"
+
+COMMON = [
+    "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+    "-ffp-contract=off",                         # FP32 op order is part of the contract
+    "-fno-gpu-flush-denormals-to-zero",          # keep FP32 subnormals
+    "-fhip-fp32-correctly-rounded-divide-sqrt",
+    "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
+]
+DEVICE = [
+    "--offload-arch=" + ARCH,
+    # packed FP32 instructions stay off (see the library notes)
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+]
+
+
+def hipcc() -> str:
+    return shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+
+
+def _compile(src: str) -> str:
+    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    cmd = [hipcc(), "-c", src, "-o", obj] + COMMON + DEVICE
+    if src.endswith(".cpp"):
+        cmd = [hipcc(), "-x", "hip", "-c", src, "-o", obj] + COMMON + DEVICE
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")
+    return obj
+
+
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
+    jobs = jobs or min(8, max(1, len(srcs)))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(_compile, srcs))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), "-shared", "-o", tmp] + objs + ["--offload-arch=" + ARCH, "-fPIC"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed:\n" + r.stderr)
+    os.replace(tmp, LIB)
+    if verbose:
+        print("built", LIB, file=sys.stderr)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)

@@ -1,0 +1,213 @@
+// C ABI front of the HIP library: argument validation, device check and
+// dispatch to the kernel launchers.  Nothing is enqueued unless every
+// argument is valid; no call synchronises the host or allocates memory.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+#include <mutex>
+
+#include "amp.h"
+#include "common.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_ok[kMaxDevices];   // 0 unknown, 1 gfx950, -1 other
+std::mutex g_device_mu;
+
+int check_device() {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    g_last_hip_error = static_cast<int>(e);
+    return AMP_ENODEVICE;
+  }
+  int st = g_device_ok[dev].load(std::memory_order_acquire);
+  if (st == 0) {
+    std::lock_guard<std::mutex> lk(g_device_mu);
+    st = g_device_ok[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+      hipDeviceProp_t prop;
+      e = hipGetDeviceProperties(&prop, dev);
+      if (e != hipSuccess) {
+        g_last_hip_error = static_cast<int>(e);
+        return AMP_ENODEVICE;
+      }
+      st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+      g_device_ok[dev].store(st, std::memory_order_release);
+    }
+  }
+  return st == 1 ? AMP_OK : AMP_ENODEVICE;
+}
+
+int hip_status(hipError_t e) {
+  if (e == hipSuccess) return AMP_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return AMP_EHIP;
+}
+
+bool is_cast_in(int t) { return t == AMP_F32 || t == AMP_F16 || t == AMP_BF16; }
+bool is_cast_out(int t) { return t == AMP_F16 || t == AMP_BF16 || t == AMP_E4M3 || t == AMP_E5M2; }
+bool is_grad(int t) { return t == AMP_F32 || t == AMP_F16 || t == AMP_BF16; }
+bool is_fp8(int t) { return t == AMP_E4M3 || t == AMP_E5M2; }
+
+}  // namespace
+
+extern "C" {
+
+int amp_abi_version(void) { return AMP_ABI_VERSION; }
+
+const char* amp_status_string(int status) {
+  switch (status) {
+    case AMP_OK: return "ok";
+    case AMP_EINVAL: return "invalid argument";
+    case AMP_EUNSUPPORTED: return "unsupported dtype or layout";
+    case AMP_EHIP: return "HIP runtime error";
+    case AMP_ENODEVICE: return "no gfx950 device is current";
+    default: return "unknown status";
+  }
+}
+
+int amp_last_hip_error(void) { return g_last_hip_error; }
+
+int amp_cast(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx, void* y, int yt,
+             int64_t ldy, void* y_t, int64_t ldy_t, const float* d_scale, float* d_amax,
+             void* stream) {
+  if (rows < 0 || cols < 0) return AMP_EINVAL;
+  if (!is_cast_in(xt) || !is_cast_out(yt)) return AMP_EUNSUPPORTED;
+  if (rows == 0 || cols == 0) return AMP_OK;
+  if (!x || (!y && !y_t)) return AMP_EINVAL;
+  if (ldx < cols || (y && ldy < cols) || (y_t && ldy_t < rows)) return AMP_EINVAL;
+  if (int st = check_device()) return st;
+  return hip_status(amp::launch_cast(x, xt, rows, cols, ldx, y, yt, ldy, y_t, ldy_t, d_scale,
+                                     d_amax, static_cast<hipStream_t>(stream)));
+}
+
+int amp_gemm(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A, int at,
+             int64_t lda, const float* d_alphaA, const void* B, int bt, int64_t ldb,
+             const float* d_alphaB, void* C, int ct, int64_t ldc, const amp_block_scales* bsA,
+             const amp_block_scales* bsB, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return AMP_EINVAL;
+  if ((opA != AMP_OP_N && opA != AMP_OP_T) || (opB != AMP_OP_N && opB != AMP_OP_T))
+    return AMP_EINVAL;
+  if (ct != AMP_F32 && ct != AMP_F16 && ct != AMP_BF16) return AMP_EUNSUPPORTED;
+  const bool nvfp4 = at == AMP_E2M1X2 || bt == AMP_E2M1X2;
+  if (nvfp4) {
+    if (at != bt || opA != AMP_OP_N || opB != AMP_OP_T) return AMP_EUNSUPPORTED;
+    if (!bsA || !bsB || !bsA->scales || !bsB->scales) return AMP_EINVAL;
+    if (K % 16 != 0) return AMP_EINVAL;
+  } else if (is_fp8(at) || is_fp8(bt)) {
+    if (!is_fp8(at) || !is_fp8(bt) || opA != AMP_OP_N || opB != AMP_OP_T) return AMP_EUNSUPPORTED;
+    if (bsA || bsB) return AMP_EINVAL;
+  } else {
+    if (!((at == AMP_F16 || at == AMP_BF16) && at == bt)) return AMP_EUNSUPPORTED;
+    if (bsA || bsB) return AMP_EINVAL;
+  }
+  if (M == 0 || N == 0) return AMP_OK;
+  if (!C || ldc < N) return AMP_EINVAL;
+  if (K > 0) {
+    if (!A || !B) return AMP_EINVAL;
+    // leading dimensions in elements (NVFP4: bytes = K/2 per row)
+    const int64_t kA = nvfp4 ? K / 2 : K, kB = nvfp4 ? K / 2 : K;
+    if (opA == AMP_OP_N ? lda < kA : lda < M) return AMP_EINVAL;
+    if (opB == AMP_OP_T ? ldb < kB : ldb < N) return AMP_EINVAL;
+    if (nvfp4 && (bsA->ld < (bsA->block2d ? K / 16 : K / 16) || bsB->ld < K / 16)) return AMP_EINVAL;
+    if (nvfp4 && ((bsA->block2d && M % 16) || (bsB->block2d && N % 16))) return AMP_EINVAL;
+  }
+  if (int st = check_device()) return st;
+  return hip_status(amp::launch_gemm(opA, opB, M, N, K, A, at, lda, d_alphaA, B, bt, ldb,
+                                     d_alphaB, C, ct, ldc, bsA, bsB,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+int amp_scaler_init(amp_scaler_state* d_state, float init_scale, void* stream) {
+  if (!d_state || !(init_scale > 0.0f)) return AMP_EINVAL;
+  if (int st = check_device()) return st;
+  return hip_status(amp::launch_scaler_init(d_state, init_scale, static_cast<hipStream_t>(stream)));
+}
+
+int amp_check_overflow(const void* x, int xt, int64_t n, amp_scaler_state* d_state,
+                       void* stream) {
+  if (n < 0 || !d_state) return AMP_EINVAL;
+  if (!is_grad(xt)) return AMP_EUNSUPPORTED;
+  if (n == 0) return AMP_OK;
+  if (!x) return AMP_EINVAL;
+  if (int st = check_device()) return st;
+  return hip_status(amp::launch_check_overflow(x, xt, n, d_state, static_cast<hipStream_t>(stream)));
+}
+
+int amp_optimizer_step(float* master, float* m, float* v, const void* grads, int gt, void* w16,
+                       int wt, int64_t n, const amp_adamw_hparams* hp,
+                       amp_scaler_state* d_state, int flags, void* stream) {
+  if (n < 0 || !hp || !d_state) return AMP_EINVAL;
+  if (!is_grad(gt)) return AMP_EUNSUPPORTED;
+  if (w16 && wt != AMP_F16 && wt != AMP_BF16) return AMP_EUNSUPPORTED;
+  if (flags & ~AMP_OPT_SKIP_CHECK) return AMP_EINVAL;
+  if (n > 0 && (!master || !m || !v || !grads)) return AMP_EINVAL;
+  if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0 && hp->beta2 >= 0.0 && hp->beta2 < 1.0))
+    return AMP_EINVAL;
+  if (int st = check_device()) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (n > 0) {
+    if (!(flags & AMP_OPT_SKIP_CHECK)) {
+      if (int st = hip_status(amp::launch_check_overflow(grads, gt, n, d_state, s))) return st;
+    }
+    if (int st = hip_status(amp::launch_optimizer_apply(master, m, v, grads, gt, w16, wt, n, *hp,
+                                                        d_state, s)))
+      return st;
+  }
+  return hip_status(amp::launch_optimizer_commit(d_state, *hp, s));
+}
+
+int amp_scaler_update(amp_scaler_state* d_state, const amp_scaler_params* p, void* stream) {
+  if (!d_state) return AMP_EINVAL;
+  amp_scaler_params q{2.0f, 0.5f, 2000};
+  if (p) q = *p;
+  if (q.growth_interval <= 0) return AMP_EINVAL;
+  if (int st = check_device()) return st;
+  return hip_status(amp::launch_scaler_update(d_state, q, static_cast<hipStream_t>(stream)));
+}
+
+int amp_fp8_meta_init(amp_fp8_meta* d_metas, float* d_history, int32_t n, int32_t history_len,
+                      void* stream) {
+  if (n < 0 || history_len <= 0) return AMP_EINVAL;
+  if (n == 0) return AMP_OK;
+  if (!d_metas || !d_history) return AMP_EINVAL;
+  if (int st = check_device()) return st;
+  return hip_status(amp::launch_meta_init(d_metas, d_history, n, history_len,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int amp_delayed_scaling_update(amp_fp8_meta* d_metas, float* d_history, int32_t n,
+                               const amp_delayed_recipe* r, void* stream) {
+  if (n < 0 || !r || r->history_len <= 0) return AMP_EINVAL;
+  if (r->algo != AMP_AMAX_MAX && r->algo != AMP_AMAX_MOST_RECENT) return AMP_EINVAL;
+  if (!(r->fp8_max > 0.0f) || !(r->margin > 0.0f)) return AMP_EINVAL;
+  if (n == 0) return AMP_OK;
+  if (!d_metas || !d_history) return AMP_EINVAL;
+  if (int st = check_device()) return st;
+  return hip_status(amp::launch_delayed_update(d_metas, d_history, n, *r,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int amp_nvfp4_quantize(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
+                       int transpose, int block2d, int rht, uint64_t rht_seed, int rnd,
+                       uint64_t sr_seed, uint8_t* q, uint8_t* scales, float* d_tensor,
+                       void* stream) {
+  if (rows < 0 || cols < 0 || ldx < cols) return AMP_EINVAL;
+  if (xt != AMP_BF16 && xt != AMP_F32) return AMP_EUNSUPPORTED;
+  if (rnd != AMP_ROUND_RNE && rnd != AMP_ROUND_SR) return AMP_EINVAL;
+  const int64_t R = transpose ? cols : rows, K = transpose ? rows : cols;
+  if (R % 16 || K % 16) return AMP_EINVAL;
+  if (!d_tensor) return AMP_EINVAL;
+  if (R > 0 && K > 0 && (!x || !q || !scales)) return AMP_EINVAL;
+  if (int st = check_device()) return st;
+  return hip_status(amp::launch_nvfp4_quantize(x, xt, rows, cols, ldx, transpose, block2d, rht,
+                                               rht_seed, rnd, sr_seed, q, scales, d_tensor,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

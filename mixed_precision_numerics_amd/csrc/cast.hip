@@ -1,0 +1,296 @@
+// Scaled down-cast with amax capture (gfx950).
+//
+// What is computed: page "FP8 혼합 정밀도 LLM 학습" (hwlabs), sections
+// "FP8이 어려운 이유" (a per-tensor scale brings the tensor into the FP8 range,
+// values are clipped to [-448, 448]) and "Delayed Scaling 동작 원리" (each
+// step records the tensor's amax; with the scale known in advance the tensor
+// is read once); page "혼합 정밀도 학습" (itwiki), section "FP16 학습 루프"
+// (16-bit copies are made from the FP32 parameters just before use).
+//
+//   y = round(fl32(x * scale)),  amax = max(amax, max|x|)  (bit-pattern max)
+//
+// Two kernels, both HBM-bound:
+//  * cast_flat: contiguous tensors, 8 elements per thread per iteration with
+//    16-byte loads, grid-stride, one atomic max per block.
+//  * cast_tile: strided tensors and the optional transposed copy (the FP8
+//    dgrad / wgrad operands).  A 256-thread block owns a 128x128 tile; each
+//    thread converts an 8x8 sub-block, writes its row-major codes directly and
+//    its transposed codes into LDS, from where the block writes the transposed
+//    tile with coalesced 16-byte stores.
+#include "common.hpp"
+#include "formats.hpp"
+
+namespace amp {
+namespace {
+
+template <int XT>
+__device__ __forceinline__ float load_one(const void* p, int64_t i) {
+  if constexpr (XT == AMP_F32) return static_cast<const float*>(p)[i];
+  else if constexpr (XT == AMP_BF16) return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+  else return f16_to_f32(static_cast<const uint16_t*>(p)[i]);
+}
+
+// Load 8 consecutive elements (16-byte aligned).
+template <int XT>
+__device__ __forceinline__ void load8(const void* p, int64_t i, float (&v)[8]) {
+  if constexpr (XT == AMP_F32) {
+    const float4* q = reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
+    const float4 a = q[0], b = q[1];
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
+    const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + i);
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if constexpr (XT == AMP_BF16) {
+        v[2 * k] = bitsf(ww[k] << 16);
+        v[2 * k + 1] = bitsf(ww[k] & 0xffff0000u);
+      } else {
+        v[2 * k] = f16_to_f32(ww[k] & 0xffffu);
+        v[2 * k + 1] = f16_to_f32(ww[k] >> 16);
+      }
+    }
+  }
+}
+
+template <int YT>
+__device__ __forceinline__ uint32_t to_code(float t) {
+  if constexpr (YT == AMP_F16) return f32_to_f16(t);
+  else if constexpr (YT == AMP_BF16) return f32_to_bf16(t);
+  else if constexpr (YT == AMP_E4M3) return f32_to_e4m3(t);
+  else return f32_to_e5m2(t);
+}
+
+template <int YT>
+struct CodeT { using type = uint16_t; };
+template <> struct CodeT<AMP_E4M3> { using type = uint8_t; };
+template <> struct CodeT<AMP_E5M2> { using type = uint8_t; };
+
+// Store 8 codes at y + i (8- or 16-byte aligned).
+template <int YT>
+__device__ __forceinline__ void store8(void* y, int64_t i, const uint32_t (&c)[8]) {
+  if constexpr (sizeof(typename CodeT<YT>::type) == 1) {
+    uint2 w;
+    w.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+    w.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+    *reinterpret_cast<uint2*>(static_cast<uint8_t*>(y) + i) = w;
+  } else {
+    uint4 w;
+    w.x = c[0] | (c[1] << 16); w.y = c[2] | (c[3] << 16);
+    w.z = c[4] | (c[5] << 16); w.w = c[6] | (c[7] << 16);
+    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + i) = w;
+  }
+}
+
+template <int YT>
+__device__ __forceinline__ void store_one(void* y, int64_t i, uint32_t c) {
+  static_cast<typename CodeT<YT>::type*>(y)[i] = static_cast<typename CodeT<YT>::type>(c);
+}
+
+constexpr int kFlatThreads = 256;
+
+template <int XT, int YT, bool VEC>
+__global__ __launch_bounds__(kFlatThreads) void cast_flat(const void* __restrict__ x,
+                                                          void* __restrict__ y, int64_t n,
+                                                          const float* __restrict__ d_scale,
+                                                          float* __restrict__ d_amax) {
+  __shared__ uint32_t red[kFlatThreads / kWave];
+  const bool SCALE = d_scale != nullptr, AMAX = d_amax != nullptr;
+  const float scale = SCALE ? *d_scale : 1.0f;
+  uint32_t am = 0;
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * kFlatThreads + threadIdx.x;
+  const int64_t nthr = static_cast<int64_t>(gridDim.x) * kFlatThreads;
+  if constexpr (VEC) {
+    const int64_t nv = n / 8;
+    for (int64_t j = tid; j < nv; j += nthr) {
+      float v[8];
+      load8<XT>(x, j * 8, v);
+      uint32_t c[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        if (AMAX) { const uint32_t a = fbits(v[k]) & 0x7fffffffu; am = am > a ? am : a; }
+        c[k] = to_code<YT>(SCALE ? v[k] * scale : v[k]);
+      }
+      store8<YT>(y, j * 8, c);
+    }
+    for (int64_t i = nv * 8 + tid; i < n; i += nthr) {
+      const float v = load_one<XT>(x, i);
+      if (AMAX) { const uint32_t a = fbits(v) & 0x7fffffffu; am = am > a ? am : a; }
+      store_one<YT>(y, i, to_code<YT>(SCALE ? v * scale : v));
+    }
+  } else {
+    for (int64_t i = tid; i < n; i += nthr) {
+      const float v = load_one<XT>(x, i);
+      if (AMAX) { const uint32_t a = fbits(v) & 0x7fffffffu; am = am > a ? am : a; }
+      store_one<YT>(y, i, to_code<YT>(SCALE ? v * scale : v));
+    }
+  }
+  if (AMAX) {
+    am = block_max_u32<kFlatThreads>(am, red);
+    if (threadIdx.x == 0 && am != 0)
+      atomicMax(reinterpret_cast<unsigned int*>(d_amax), canon_amax(am));
+  }
+}
+
+constexpr int kTile = 128;
+constexpr int kTileThreads = 256;
+
+// 128x128 tile per block.  Thread t owns rows r0..r0+7 and columns c0..c0+7
+// with c0 = 8*(t % 16), r0 = 8*(t / 16).  FULL: the tile is inside the tensor
+// and every access is 16-byte aligned (checked on the host).
+template <int XT, int YT, bool WY, bool WYT, bool VEC>
+__global__ __launch_bounds__(kTileThreads) void cast_tile(
+    const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
+    void* __restrict__ y, int64_t ldy, void* __restrict__ y_t, int64_t ldy_t,
+    const float* __restrict__ d_scale, float* __restrict__ d_amax) {
+  using Code = typename CodeT<YT>::type;
+  constexpr int kPitch = kTile + 16 / static_cast<int>(sizeof(Code));  // row pitch in codes
+  __shared__ __align__(16) Code lds[WYT ? kTile * kPitch : 1];
+  __shared__ uint32_t red[kTileThreads / kWave];
+
+  const bool SCALE = d_scale != nullptr, AMAX = d_amax != nullptr;
+  const float scale = SCALE ? *d_scale : 1.0f;
+  const int64_t r_base = static_cast<int64_t>(blockIdx.y) * kTile;
+  const int64_t c_base = static_cast<int64_t>(blockIdx.x) * kTile;
+  const int t = threadIdx.x;
+  const int c0 = 8 * (t % 16), r0 = 8 * (t / 16);
+  const bool full = VEC && (r_base + kTile <= rows) && (c_base + kTile <= cols);
+  uint32_t am = 0;
+  uint32_t code[8][8];
+
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t r = r_base + r0 + i;
+    const int64_t c = c_base + c0;
+    float v[8];
+    if (full) {
+      load8<XT>(x, r * ldx + c, v);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        v[j] = (r < rows && c + j < cols) ? load_one<XT>(x, r * ldx + c + j) : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (AMAX) { const uint32_t a = fbits(v[j]) & 0x7fffffffu; am = am > a ? am : a; }
+      code[i][j] = to_code<YT>(SCALE ? v[j] * scale : v[j]);
+    }
+    if constexpr (WY) {
+      if (full) {
+        store8<YT>(y, r * ldy + c, code[i]);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (r < rows && c + j < cols) store_one<YT>(y, r * ldy + c + j, code[i][j]);
+      }
+    }
+  }
+
+  if constexpr (WYT) {
+    // transposed 8x8 sub-block -> LDS rows c0+j, columns r0..r0+7
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      Code* dst = lds + (c0 + j) * kPitch + r0;
+      if constexpr (sizeof(Code) == 1) {
+        uint2 w;
+        w.x = code[0][j] | (code[1][j] << 8) | (code[2][j] << 16) | (code[3][j] << 24);
+        w.y = code[4][j] | (code[5][j] << 8) | (code[6][j] << 16) | (code[7][j] << 24);
+        *reinterpret_cast<uint2*>(dst) = w;
+      } else {
+        uint4 w;
+        w.x = code[0][j] | (code[1][j] << 16); w.y = code[2][j] | (code[3][j] << 16);
+        w.z = code[4][j] | (code[5][j] << 16); w.w = code[6][j] | (code[7][j] << 16);
+        *reinterpret_cast<uint4*>(dst) = w;
+      }
+    }
+    __syncthreads();
+    // y_t rows c_base + cc hold tile rows r_base .. r_base + 127
+    constexpr int kPer = 16 / static_cast<int>(sizeof(Code));       // codes per 16 B
+    constexpr int kChunksPerRow = kTile / kPer;
+    constexpr int kIters = kTile * kChunksPerRow / kTileThreads;
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+      const int idx = it * kTileThreads + t;
+      const int cc = idx / kChunksPerRow;
+      const int rr = (idx % kChunksPerRow) * kPer;
+      const int64_t orow = c_base + cc;
+      const int64_t ocol = r_base + rr;
+      const Code* src = lds + cc * kPitch + rr;
+      if (full) {
+        *reinterpret_cast<uint4*>(static_cast<Code*>(y_t) + orow * ldy_t + ocol) =
+            *reinterpret_cast<const uint4*>(src);
+      } else if (orow < cols) {
+#pragma unroll
+        for (int k = 0; k < kPer; ++k)
+          if (ocol + k < rows) static_cast<Code*>(y_t)[orow * ldy_t + ocol + k] = src[k];
+      }
+    }
+  }
+
+  if (AMAX) {
+    am = block_max_u32<kTileThreads>(am, red);
+    if (t == 0 && am != 0) atomicMax(reinterpret_cast<unsigned int*>(d_amax), canon_amax(am));
+  }
+}
+
+template <int XT, int YT>
+hipError_t dispatch_layout(const void* x, int64_t rows, int64_t cols, int64_t ldx, void* y,
+                           int64_t ldy, void* y_t, int64_t ldy_t, const float* d_scale,
+                           float* d_amax, hipStream_t s) {
+  const int xb = dtype_bytes(XT), yb = dtype_bytes(YT);
+  if (y_t == nullptr && ldx == cols && ldy == cols) {
+    const int64_t n = rows * cols;
+    const bool vec = aligned(x, 16) && aligned(y, 8 * yb);
+    int64_t blocks = (n / 8 + kFlatThreads - 1) / kFlatThreads;
+    if (blocks > 256 * 16) blocks = 256 * 16;
+    if (blocks < 1) blocks = 1;
+    if (vec)
+      cast_flat<XT, YT, true><<<dim3(static_cast<unsigned>(blocks)), kFlatThreads, 0, s>>>(
+          x, y, n, d_scale, d_amax);
+    else
+      cast_flat<XT, YT, false><<<dim3(static_cast<unsigned>(blocks)), kFlatThreads, 0, s>>>(
+          x, y, n, d_scale, d_amax);
+    return hipGetLastError();
+  }
+  // the vector path needs every row start 16-byte aligned for x and the outputs
+  bool vec = aligned(x, 16) && (ldx * xb) % 16 == 0;
+  if (y) vec = vec && aligned(y, 8 * yb) && (ldy * yb) % (8 * yb) == 0;
+  if (y_t) vec = vec && aligned(y_t, 16) && (ldy_t * yb) % 16 == 0;
+  const dim3 grid(static_cast<unsigned>((cols + kTile - 1) / kTile),
+                  static_cast<unsigned>((rows + kTile - 1) / kTile));
+#define AMP_TILE(WY, WYT, V) \
+  cast_tile<XT, YT, WY, WYT, V><<<grid, kTileThreads, 0, s>>>( \
+      x, rows, cols, ldx, y, ldy, y_t, ldy_t, d_scale, d_amax)
+  if (y && y_t) { if (vec) AMP_TILE(true, true, true); else AMP_TILE(true, true, false); }
+  else if (y)   { if (vec) AMP_TILE(true, false, true); else AMP_TILE(true, false, false); }
+  else          { if (vec) AMP_TILE(false, true, true); else AMP_TILE(false, true, false); }
+#undef AMP_TILE
+  return hipGetLastError();
+}
+
+template <int XT>
+hipError_t dispatch_out(int yt, const void* x, int64_t rows, int64_t cols, int64_t ldx, void* y,
+                        int64_t ldy, void* y_t, int64_t ldy_t, const float* d_scale,
+                        float* d_amax, hipStream_t s) {
+  switch (yt) {
+    case AMP_F16: return dispatch_layout<XT, AMP_F16>(x, rows, cols, ldx, y, ldy, y_t, ldy_t, d_scale, d_amax, s);
+    case AMP_BF16: return dispatch_layout<XT, AMP_BF16>(x, rows, cols, ldx, y, ldy, y_t, ldy_t, d_scale, d_amax, s);
+    case AMP_E4M3: return dispatch_layout<XT, AMP_E4M3>(x, rows, cols, ldx, y, ldy, y_t, ldy_t, d_scale, d_amax, s);
+    default: return dispatch_layout<XT, AMP_E5M2>(x, rows, cols, ldx, y, ldy, y_t, ldy_t, d_scale, d_amax, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_cast(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx, void* y,
+                       int yt, int64_t ldy, void* y_t, int64_t ldy_t, const float* d_scale,
+                       float* d_amax, hipStream_t s) {
+  switch (xt) {
+    case AMP_F32: return dispatch_out<AMP_F32>(yt, x, rows, cols, ldx, y, ldy, y_t, ldy_t, d_scale, d_amax, s);
+    case AMP_BF16: return dispatch_out<AMP_BF16>(yt, x, rows, cols, ldx, y, ldy, y_t, ldy_t, d_scale, d_amax, s);
+    default: return dispatch_out<AMP_F16>(yt, x, rows, cols, ldx, y, ldy, y_t, ldy_t, d_scale, d_amax, s);
+  }
+}
+
+}  // namespace amp

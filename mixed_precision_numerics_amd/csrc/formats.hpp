@@ -1,0 +1,155 @@
+// Device-side number-format conversions for gfx950.
+//
+// Every conversion rounds to nearest with ties to the even code, keeps
+// gradual underflow and the sign of zero, and is written with integer and
+// exact FP32 operations so that it is bit-identical on every input:
+//   * FP16 / BF16 (IEEE): overflow gives +-inf, NaN gives the canonical quiet
+//     NaN (0x7E00 / 0x7FC0).
+//   * FP8 E4M3 (OCP, max 448) and E5M2 (max 57344): values are clipped to
+//     [-max, max] first (inf included), the page's clip(x, -448, 448) of
+//     "FP8 혼합 정밀도 LLM 학습" (hwlabs), section "FP8이 어려운 이유"; NaN -> 0x7F.
+//   * FP4 E2M1 (NVFP4 element, page "Pretraining Large Language Models with
+//     NVFP4", section 2.1): clipped to [-6, 6]; nearest-even or stochastic.
+// Subnormal targets use one exact FP32 addition of a power of two whose ulp
+// equals the target's subnormal spacing, so the FPU does the tie-to-even.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace amp {
+
+__device__ __forceinline__ uint32_t fbits(float x) { return __float_as_uint(x); }
+__device__ __forceinline__ float bitsf(uint32_t u) { return __uint_as_float(u); }
+
+// ---- FP32 -> FP16 ---------------------------------------------------------
+__device__ __forceinline__ uint32_t f32_to_f16(float x) {
+  const uint32_t u = fbits(x);
+  const uint32_t s = (u >> 16) & 0x8000u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7e00u;               // NaN
+  if (a >= 0x477ff000u) return s | 0x7c00u;          // >= 65520 rounds to inf
+  if (a >= 0x38800000u) {                            // normal: >= 2^-14
+    const uint32_t r = a + 0xfffu + ((a >> 13) & 1u);
+    return s | ((r - 0x38000000u) >> 13);
+  }
+  // |x| < 2^-14: spacing 2^-24 = ulp of [0.5, 1)
+  return s | (fbits(bitsf(a) + 0.5f) - 0x3f000000u);
+}
+
+// ---- FP32 -> BF16 ---------------------------------------------------------
+__device__ __forceinline__ uint32_t f32_to_bf16(float x) {
+  const uint32_t u = fbits(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---- FP32 -> E4M3 (saturating) -------------------------------------------
+__device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
+  const uint32_t u = fbits(x);
+  const uint32_t s = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7fu;
+  if (a >= 0x43e00000u) return s | 0x7eu;            // >= 448 (and inf)
+  if (a >= 0x3c800000u) {                            // normal: >= 2^-6
+    const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);
+    return s | ((r - 0x3c000000u) >> 20);
+  }
+  return s | (fbits(bitsf(a) + 16384.0f) - 0x46800000u);   // spacing 2^-9
+}
+
+// ---- FP32 -> E5M2 (saturating) -------------------------------------------
+__device__ __forceinline__ uint32_t f32_to_e5m2(float x) {
+  const uint32_t u = fbits(x);
+  const uint32_t s = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7fu;
+  if (a >= 0x47600000u) return s | 0x7bu;            // >= 57344 (and inf)
+  if (a >= 0x38800000u) {                            // normal: >= 2^-14
+    const uint32_t r = a + 0xfffffu + ((a >> 21) & 1u);
+    return s | ((r - 0x38000000u) >> 21);
+  }
+  return s | (fbits(bitsf(a) + 128.0f) - 0x43000000u);     // spacing 2^-16
+}
+
+// ---- widening (exact) -----------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint32_t c) { return bitsf(c << 16); }
+
+__device__ __forceinline__ float f16_to_f32(uint32_t c) {
+  const uint32_t s = (c & 0x8000u) << 16;
+  const uint32_t e = (c >> 10) & 0x1fu;
+  const uint32_t m = c & 0x3ffu;
+  if (e == 0x1fu) return bitsf(s | 0x7f800000u | (m << 13));
+  if (e == 0) {  // subnormal or zero: m * 2^-24, exact in FP32
+    return bitsf(s | fbits(static_cast<float>(m) * 5.9604644775390625e-8f));
+  }
+  return bitsf(s | ((e + 112u) << 23) | (m << 13));
+}
+
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  const uint32_t s = (c & 0x80u) << 24;
+  const uint32_t e = (c >> 3) & 0xfu;
+  const uint32_t m = c & 0x7u;
+  if (e == 0xfu && m == 0x7u) return bitsf(0x7fc00000u);
+  if (e == 0) return bitsf(s | fbits(static_cast<float>(m) * 0.001953125f));
+  return bitsf(s | ((e + 120u) << 23) | (m << 20));
+}
+
+__device__ __forceinline__ float e5m2_to_f32(uint32_t c) {
+  const uint32_t s = (c & 0x80u) << 24;
+  const uint32_t e = (c >> 2) & 0x1fu;
+  const uint32_t m = c & 0x3u;
+  if (e == 0x1fu) return bitsf(s | 0x7f800000u | (m << 21));
+  if (e == 0) return bitsf(s | fbits(static_cast<float>(m) * 1.52587890625e-5f));
+  return bitsf(s | ((e + 112u) << 23) | (m << 21));
+}
+
+// ---- E2M1 (FP4) -----------------------------------------------------------
+// Magnitude codes 0..7 = {0, 0.5, 1, 1.5, 2, 3, 4, 6}; bit 3 is the sign.
+__device__ __forceinline__ uint32_t e2m1_rne(float y) {
+  const float a = fabsf(y);
+  // each threshold is a midpoint; '>' where the lower neighbour has the even
+  // code, '>=' where the upper one has it
+  uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) +
+               (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
+  return c | ((fbits(y) >> 28) & 0x8u);
+}
+
+// Stochastic rounding with u in [0, 1): round the magnitude up iff u < frac.
+__device__ __forceinline__ uint32_t e2m1_sr(float y, float u) {
+  const float a = fminf(fabsf(y), 6.0f);
+  const uint32_t lo = (a >= 0.5f) + (a >= 1.0f) + (a >= 1.5f) + (a >= 2.0f) +
+                      (a >= 3.0f) + (a >= 4.0f) + (a >= 6.0f);
+  // lower neighbour value and gap to the upper one
+  const float lov = lo < 4 ? 0.5f * static_cast<float>(lo)
+                           : (lo == 4 ? 2.0f : (lo == 5 ? 3.0f : (lo == 6 ? 4.0f : 6.0f)));
+  const float inv_gap = lo < 4 ? 2.0f : (lo < 6 ? 1.0f : 0.5f);
+  const float frac = (a - lov) * inv_gap;   // exact (Sterbenz, power-of-two gap)
+  const uint32_t up = (lo < 7) && (u < frac);
+  return (lo + up) | ((fbits(y) >> 28) & 0x8u);
+}
+
+__device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
+  const uint32_t m = c & 7u;
+  const float v = m < 4 ? 0.5f * static_cast<float>(m)
+                        : (m == 4 ? 2.0f : (m == 5 ? 3.0f : (m == 6 ? 4.0f : 6.0f)));
+  return (c & 8u) ? -v : v;
+}
+
+// ---- Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) ---------------------
+struct ctr4 { uint32_t x, y, z, w; };
+
+__device__ __forceinline__ ctr4 philox4x32_10(ctr4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = static_cast<uint64_t>(0xD2511F53u) * c.x;
+    const uint64_t p1 = static_cast<uint64_t>(0xCD9E8D57u) * c.z;
+    const uint32_t hi0 = static_cast<uint32_t>(p0 >> 32), lo0 = static_cast<uint32_t>(p0);
+    const uint32_t hi1 = static_cast<uint32_t>(p1 >> 32), lo1 = static_cast<uint32_t>(p1);
+    c = ctr4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  return c;
+}
+
+}  // namespace amp

@@ -1,0 +1,378 @@
+// Fused FP32-master AdamW step with dynamic loss scaling, the loss-scaler
+// update and the delayed-scaling (amax history) update (gfx950).
+//
+// Sources: page "혼합 정밀도 학습" (itwiki), sections "FP32 마스터 가중치" (the
+// update goes to the FP32 copy, the 16-bit copy is re-rounded from it) and
+// "손실 스케일링" (unscale by 1/S in FP32; check every step for inf/NaN, skip
+// the update and halve S on overflow, double S after 2000 clean steps); page
+// "Mixed Precision Training/es" (marovi), sections "Escalado dinámico de
+// pérdida" and "Operaciones que permanecen en FP32" (Adam moments stay FP32);
+// page "FP8 혼합 정밀도 LLM 학습" (hwlabs), section "Delayed Scaling 동작 원리"
+// (amax history, scale = fp8_max / (margin * amax_max)).  AdamW itself is
+// only named on the pages; the update is the decoupled-weight-decay form.
+//
+// Skip semantics: an overflowing step must leave master, m, v, the 16-bit
+// copy and the step count untouched, so an in-place update cannot begin
+// before every gradient is checked.  The step is therefore two sweeps:
+//   check  -- reads the 16-bit gradients (2 B/param) and sets found_inf;
+//   apply  -- gated on found_inf, one fused pass over the state
+//             (read g, master, m, v; write master, m, v, w16: 28 B/param).
+// A producer that already knows the overflow flag skips the check sweep.
+// The per-element arithmetic is FP32 without contraction (-ffp-contract=off):
+//   g = f32(g16)*invS; m = b1*m + c1*g; v = b2*v + c2*(g*g);
+//   d = sqrt(v)*rbc2 + eps; theta = theta*decay - step*(m/d); w16 = rne(theta).
+#include "common.hpp"
+#include "formats.hpp"
+
+namespace amp {
+namespace {
+
+constexpr int kThreads = 256;
+
+// ---------------------------------------------------------------- check ---
+template <int GT>
+__device__ __forceinline__ bool nonfinite_word(uint32_t w) {
+  if constexpr (GT == AMP_F32) {
+    return (w & 0x7f800000u) == 0x7f800000u;
+  } else {
+    constexpr uint32_t kMask = GT == AMP_F16 ? 0x7c007c00u : 0x7f807f80u;
+    const uint32_t t = (w & kMask) ^ kMask;     // a half is non-finite iff its part is 0
+    return (t & 0xffffu) == 0 || (t >> 16) == 0;
+  }
+}
+
+template <int GT, bool VEC>
+__global__ __launch_bounds__(kThreads) void check_kernel(const void* __restrict__ g, int64_t n,
+                                                         amp_scaler_state* __restrict__ st) {
+  // a block that starts after the flag is already set has nothing to add
+  if (__hip_atomic_load(&st->found_inf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return;
+  const int eb = GT == AMP_F32 ? 4 : 2;
+  const int64_t nvec = VEC ? n * eb / 16 : 0;
+  const u32x4* gv = static_cast<const u32x4*>(g);
+  bool bad = false;
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t nthr = static_cast<int64_t>(gridDim.x) * kThreads;
+  for (int64_t i = tid; i < nvec; i += nthr) {
+    const u32x4 w = __builtin_nontemporal_load(gv + i);
+    bad = bad || nonfinite_word<GT>(w.x) || nonfinite_word<GT>(w.y) ||
+          nonfinite_word<GT>(w.z) || nonfinite_word<GT>(w.w);
+  }
+  // tail elements (n not a multiple of 16 bytes)
+  for (int64_t e = nvec * 16 / eb + tid; e < n; e += nthr) {
+    if constexpr (GT == AMP_F32) {
+      bad = bad || nonfinite_word<GT>(static_cast<const uint32_t*>(g)[e]);
+    } else {
+      const uint32_t h = static_cast<const uint16_t*>(g)[e];
+      bad = bad || nonfinite_word<GT>(h | (h << 16));
+    }
+  }
+  if (__syncthreads_or(bad) && threadIdx.x == 0) atomicOr(&st->found_inf, 1);
+}
+
+// ---------------------------------------------------------------- apply ---
+struct StepScalars {
+  float inv_s, b1, b2, c1, c2, eps, rbc2, decay, step;
+};
+
+__device__ __forceinline__ StepScalars make_scalars(const amp_scaler_state& st,
+                                                    const amp_adamw_hparams& hp) {
+  StepScalars k;
+  const double b1p = st.beta1_pow * hp.beta1;
+  const double b2p = st.beta2_pow * hp.beta2;
+  k.step = static_cast<float>(hp.lr / (1.0 - b1p));
+  k.rbc2 = static_cast<float>(1.0 / sqrt(1.0 - b2p));
+  k.decay = static_cast<float>(1.0 - hp.lr * hp.weight_decay);
+  k.c1 = static_cast<float>(1.0 - hp.beta1);
+  k.c2 = static_cast<float>(1.0 - hp.beta2);
+  k.b1 = static_cast<float>(hp.beta1);
+  k.b2 = static_cast<float>(hp.beta2);
+  k.eps = static_cast<float>(hp.eps);
+  k.inv_s = 1.0f / st.scale;
+  return k;
+}
+
+template <int GT>
+__device__ __forceinline__ float grad_at(const void* g, int64_t i) {
+  if constexpr (GT == AMP_F32) return static_cast<const float*>(g)[i];
+  else if constexpr (GT == AMP_BF16) return bf16_to_f32(static_cast<const uint16_t*>(g)[i]);
+  else return f16_to_f32(static_cast<const uint16_t*>(g)[i]);
+}
+
+template <int WT>
+__device__ __forceinline__ uint32_t w16_code(float t) {
+  if constexpr (WT == AMP_BF16) return f32_to_bf16(t);
+  else return f32_to_f16(t);
+}
+
+__device__ __forceinline__ void adam_elem(const StepScalars& k, float g16, float& th, float& m,
+                                          float& v) {
+  const float g = g16 * k.inv_s;
+  m = k.b1 * m + k.c1 * g;
+  v = k.b2 * v + k.c2 * (g * g);
+  const float d = sqrtf(v) * k.rbc2 + k.eps;
+  th = th * k.decay - k.step * (m / d);
+}
+
+// Vector path: 8 elements per thread per iteration, 16-byte accesses,
+// non-temporal (streaming) loads and stores.
+template <int GT, int WT, bool HAS_W>
+__global__ __launch_bounds__(kThreads) void apply_kernel(float* __restrict__ th_p,
+                                                         float* __restrict__ m_p,
+                                                         float* __restrict__ v_p,
+                                                         const void* __restrict__ g_p,
+                                                         void* __restrict__ w_p, int64_t n,
+                                                         amp_adamw_hparams hp,
+                                                         const amp_scaler_state* __restrict__ st_p) {
+  const amp_scaler_state st = *st_p;
+  if (st.found_inf) return;
+  const StepScalars k = make_scalars(st, hp);
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t nthr = static_cast<int64_t>(gridDim.x) * kThreads;
+  const int64_t nv = n / 8;
+  f32x4* th4 = reinterpret_cast<f32x4*>(th_p);
+  f32x4* m4 = reinterpret_cast<f32x4*>(m_p);
+  f32x4* v4 = reinterpret_cast<f32x4*>(v_p);
+  for (int64_t j = tid; j < nv; j += nthr) {
+    float gg[8];
+    if constexpr (GT == AMP_F32) {
+      const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g_p) + 2 * j);
+      const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g_p) + 2 * j + 1);
+      gg[0] = a.x; gg[1] = a.y; gg[2] = a.z; gg[3] = a.w;
+      gg[4] = b.x; gg[5] = b.y; gg[6] = b.z; gg[7] = b.w;
+    } else {
+      const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(g_p) + j);
+      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if constexpr (GT == AMP_BF16) {
+          gg[2 * q] = bitsf(ww[q] << 16);
+          gg[2 * q + 1] = bitsf(ww[q] & 0xffff0000u);
+        } else {
+          gg[2 * q] = f16_to_f32(ww[q] & 0xffffu);
+          gg[2 * q + 1] = f16_to_f32(ww[q] >> 16);
+        }
+      }
+    }
+    const f32x4 t0 = __builtin_nontemporal_load(th4 + 2 * j), t1 = __builtin_nontemporal_load(th4 + 2 * j + 1);
+    const f32x4 m0 = __builtin_nontemporal_load(m4 + 2 * j), m1 = __builtin_nontemporal_load(m4 + 2 * j + 1);
+    const f32x4 v0 = __builtin_nontemporal_load(v4 + 2 * j), v1 = __builtin_nontemporal_load(v4 + 2 * j + 1);
+    float th[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
+    float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
+    float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) adam_elem(k, gg[q], th[q], mm[q], vv[q]);
+    __builtin_nontemporal_store(f32x4{th[0], th[1], th[2], th[3]}, th4 + 2 * j);
+    __builtin_nontemporal_store(f32x4{th[4], th[5], th[6], th[7]}, th4 + 2 * j + 1);
+    __builtin_nontemporal_store(f32x4{mm[0], mm[1], mm[2], mm[3]}, m4 + 2 * j);
+    __builtin_nontemporal_store(f32x4{mm[4], mm[5], mm[6], mm[7]}, m4 + 2 * j + 1);
+    __builtin_nontemporal_store(f32x4{vv[0], vv[1], vv[2], vv[3]}, v4 + 2 * j);
+    __builtin_nontemporal_store(f32x4{vv[4], vv[5], vv[6], vv[7]}, v4 + 2 * j + 1);
+    if constexpr (HAS_W) {
+      u32x4 w;
+      w.x = w16_code<WT>(th[0]) | (w16_code<WT>(th[1]) << 16);
+      w.y = w16_code<WT>(th[2]) | (w16_code<WT>(th[3]) << 16);
+      w.z = w16_code<WT>(th[4]) | (w16_code<WT>(th[5]) << 16);
+      w.w = w16_code<WT>(th[6]) | (w16_code<WT>(th[7]) << 16);
+      __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(w_p) + j);
+    }
+  }
+  for (int64_t i = nv * 8 + tid; i < n; i += nthr) {
+    float th = th_p[i], m = m_p[i], v = v_p[i];
+    adam_elem(k, grad_at<GT>(g_p, i), th, m, v);
+    th_p[i] = th; m_p[i] = m; v_p[i] = v;
+    if constexpr (HAS_W) static_cast<uint16_t*>(w_p)[i] = static_cast<uint16_t>(w16_code<WT>(th));
+  }
+}
+
+// Scalar path for buffers that are not 16-byte aligned.
+template <int GT, int WT, bool HAS_W>
+__global__ __launch_bounds__(kThreads) void apply_kernel_scalar(float* __restrict__ th_p,
+                                                                float* __restrict__ m_p,
+                                                                float* __restrict__ v_p,
+                                                                const void* __restrict__ g_p,
+                                                                void* __restrict__ w_p, int64_t n,
+                                                                amp_adamw_hparams hp,
+                                                                const amp_scaler_state* __restrict__ st_p) {
+  const amp_scaler_state st = *st_p;
+  if (st.found_inf) return;
+  const StepScalars k = make_scalars(st, hp);
+  const int64_t nthr = static_cast<int64_t>(gridDim.x) * kThreads;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n; i += nthr) {
+    float th = th_p[i], m = m_p[i], v = v_p[i];
+    adam_elem(k, grad_at<GT>(g_p, i), th, m, v);
+    th_p[i] = th; m_p[i] = m; v_p[i] = v;
+    if constexpr (HAS_W) static_cast<uint16_t*>(w_p)[i] = static_cast<uint16_t>(w16_code<WT>(th));
+  }
+}
+
+__global__ void commit_kernel(amp_scaler_state* st, amp_adamw_hparams hp) {
+  if (threadIdx.x == 0 && !st->found_inf) {
+    st->adam_step += 1;
+    st->beta1_pow *= hp.beta1;
+    st->beta2_pow *= hp.beta2;
+  }
+}
+
+// --------------------------------------------------------------- scaler ---
+__global__ void scaler_init_kernel(amp_scaler_state* st, float init_scale) {
+  if (threadIdx.x == 0) {
+    st->scale = init_scale;
+    st->growth_tracker = 0;
+    st->found_inf = 0;
+    st->pad_ = 0;
+    st->adam_step = 0;
+    st->beta1_pow = 1.0;
+    st->beta2_pow = 1.0;
+  }
+}
+
+__global__ void scaler_update_kernel(amp_scaler_state* st, amp_scaler_params p) {
+  if (threadIdx.x != 0) return;
+  if (st->found_inf) {
+    st->scale = st->scale * p.backoff_factor;
+    st->growth_tracker = 0;
+  } else {
+    const int32_t t = st->growth_tracker + 1;
+    if (t == p.growth_interval) {
+      st->scale = st->scale * p.growth_factor;
+      st->growth_tracker = 0;
+    } else {
+      st->growth_tracker = t;
+    }
+  }
+  st->found_inf = 0;
+}
+
+// --------------------------------------------------------- FP8 recipe ---
+__global__ __launch_bounds__(kThreads) void meta_init_kernel(amp_fp8_meta* metas, float* hist,
+                                                             int32_t len) {
+  const int i = blockIdx.x;
+  for (int j = threadIdx.x; j < len; j += kThreads) hist[static_cast<int64_t>(i) * len + j] = 0.0f;
+  if (threadIdx.x == 0) {
+    metas[i].amax_cur = 0.0f;
+    metas[i].scale = 1.0f;
+    metas[i].scale_inv = 1.0f;
+    metas[i].pos = 0;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void delayed_update_kernel(amp_fp8_meta* metas, float* hist,
+                                                                  amp_delayed_recipe r) {
+  __shared__ uint32_t red[kThreads / kWave];
+  const int i = blockIdx.x;
+  amp_fp8_meta* mt = metas + i;
+  float* h = hist + static_cast<int64_t>(i) * r.history_len;
+  const int32_t pos = mt->pos;
+  const uint32_t cur = fbits(mt->amax_cur);
+  uint32_t mx = 0;
+  if (r.algo == AMP_AMAX_MOST_RECENT) {
+    mx = cur;
+  } else {
+    for (int j = threadIdx.x; j < r.history_len; j += kThreads) {
+      const uint32_t b = j == pos ? cur : fbits(h[j]);
+      mx = mx > b ? mx : b;
+    }
+    mx = block_max_u32<kThreads>(mx, red);
+  }
+  __syncthreads();   // every thread has read h[] before thread 0 rewrites it
+  if (threadIdx.x == 0) {
+    h[pos] = bitsf(cur);
+    const float amax = bitsf(mx);
+    if (mx < 0x7f800000u && mx != 0u) {
+      const float denom = r.margin * amax;
+      const float scale = r.fp8_max / denom;
+      mt->scale = scale;
+      mt->scale_inv = 1.0f / scale;
+    }
+    mt->pos = pos + 1 == r.history_len ? 0 : pos + 1;
+    mt->amax_cur = 0.0f;
+  }
+}
+
+int64_t grid_for(int64_t work_items) {
+  int64_t b = (work_items + kThreads - 1) / kThreads;
+  if (b > 256 * 8) b = 256 * 8;
+  return b < 1 ? 1 : b;
+}
+
+template <int GT, int WT, bool HAS_W>
+hipError_t launch_apply_t(float* th, float* m, float* v, const void* g, void* w, int64_t n,
+                          const amp_adamw_hparams& hp, amp_scaler_state* st, hipStream_t s) {
+  const bool vec = aligned(th, 16) && aligned(m, 16) && aligned(v, 16) && aligned(g, 16) &&
+                   (!HAS_W || aligned(w, 16));
+  if (vec)
+    apply_kernel<GT, WT, HAS_W><<<dim3(static_cast<unsigned>(grid_for(n / 8))), kThreads, 0, s>>>(
+        th, m, v, g, w, n, hp, st);
+  else
+    apply_kernel_scalar<GT, WT, HAS_W><<<dim3(static_cast<unsigned>(grid_for(n))), kThreads, 0, s>>>(
+        th, m, v, g, w, n, hp, st);
+  return hipGetLastError();
+}
+
+template <int GT>
+hipError_t launch_apply_g(float* th, float* m, float* v, const void* g, void* w, int wt, int64_t n,
+                          const amp_adamw_hparams& hp, amp_scaler_state* st, hipStream_t s) {
+  if (w == nullptr) return launch_apply_t<GT, AMP_F16, false>(th, m, v, g, w, n, hp, st, s);
+  if (wt == AMP_BF16) return launch_apply_t<GT, AMP_BF16, true>(th, m, v, g, w, n, hp, st, s);
+  return launch_apply_t<GT, AMP_F16, true>(th, m, v, g, w, n, hp, st, s);
+}
+
+}  // namespace
+
+hipError_t launch_check_overflow(const void* g, int gt, int64_t n, amp_scaler_state* st,
+                                 hipStream_t s) {
+  // the vector loop reads 16-byte words; an unaligned buffer uses the element loop
+  const bool vec = aligned(g, 16);
+  const int64_t blocks = grid_for(vec ? (n * dtype_bytes(gt) + 15) / 16 : n);
+  const dim3 grid(static_cast<unsigned>(blocks));
+#define AMP_CHECK(T)                                                       \
+  if (vec) check_kernel<T, true><<<grid, kThreads, 0, s>>>(g, n, st);      \
+  else check_kernel<T, false><<<grid, kThreads, 0, s>>>(g, n, st);
+  switch (gt) {
+    case AMP_F32: AMP_CHECK(AMP_F32) break;
+    case AMP_BF16: AMP_CHECK(AMP_BF16) break;
+    default: AMP_CHECK(AMP_F16) break;
+  }
+#undef AMP_CHECK
+  return hipGetLastError();
+}
+
+hipError_t launch_optimizer_apply(float* th, float* m, float* v, const void* g, int gt, void* w,
+                                  int wt, int64_t n, const amp_adamw_hparams& hp,
+                                  amp_scaler_state* st, hipStream_t s) {
+  switch (gt) {
+    case AMP_F32: return launch_apply_g<AMP_F32>(th, m, v, g, w, wt, n, hp, st, s);
+    case AMP_BF16: return launch_apply_g<AMP_BF16>(th, m, v, g, w, wt, n, hp, st, s);
+    default: return launch_apply_g<AMP_F16>(th, m, v, g, w, wt, n, hp, st, s);
+  }
+}
+
+hipError_t launch_optimizer_commit(amp_scaler_state* st, const amp_adamw_hparams& hp,
+                                   hipStream_t s) {
+  commit_kernel<<<1, 64, 0, s>>>(st, hp);
+  return hipGetLastError();
+}
+
+hipError_t launch_scaler_init(amp_scaler_state* st, float init_scale, hipStream_t s) {
+  scaler_init_kernel<<<1, 64, 0, s>>>(st, init_scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_scaler_update(amp_scaler_state* st, const amp_scaler_params& p, hipStream_t s) {
+  scaler_update_kernel<<<1, 64, 0, s>>>(st, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_meta_init(amp_fp8_meta* metas, float* hist, int32_t n, int32_t len,
+                            hipStream_t s) {
+  meta_init_kernel<<<dim3(static_cast<unsigned>(n)), kThreads, 0, s>>>(metas, hist, len);
+  return hipGetLastError();
+}
+
+hipError_t launch_delayed_update(amp_fp8_meta* metas, float* hist, int32_t n,
+                                 const amp_delayed_recipe& r, hipStream_t s) {
+  delayed_update_kernel<<<dim3(static_cast<unsigned>(n)), kThreads, 0, s>>>(metas, hist, r);
+  return hipGetLastError();
+}
+
+}  // namespace amp

@@ -1,0 +1,56 @@
+"""The C-ABI library loads and exports every function declared in include/amp.h
+(no GPU needed: nothing is called except the version and status strings)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mixed_precision_numerics_amd as amp
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "amp.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|const char\*)\s+(amp_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("amp_cast", "amp_gemm", "amp_optimizer_step", "amp_scaler_update",
+                     "amp_scaler_init", "amp_delayed_scaling_update", "amp_nvfp4_quantize",
+                     "amp_check_overflow", "amp_fp8_meta_init"):
+        assert required in names
+
+
+@pytest.mark.skipif(not os.path.exists(amp.lib_path()), reason="libamp.so not built")
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(amp.lib_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(amp._SIGS) == set(declared_functions())
+
+
+@pytest.mark.skipif(not os.path.exists(amp.lib_path()), reason="libamp.so not built")
+def test_version_and_status_strings():
+    assert amp.amp_abi_version() == 1
+    assert amp.amp_status_string(0) == "ok"
+    assert amp.amp_status_string(-4).startswith("no gfx950")
+
+
+@pytest.mark.skipif(not os.path.exists(amp.lib_path()), reason="libamp.so not built")
+def test_invalid_arguments_rejected_before_any_device_work():
+    lib = amp.load()
+    # negative sizes, bad dtypes and bad enums fail validation without a device
+    assert lib.amp_cast(None, 0, -1, 4, 4, None, 1, 4, None, 0, None, None, None) == -1
+    assert lib.amp_cast(None, 7, 1, 4, 4, None, 1, 4, None, 0, None, None, None) == -2
+    assert lib.amp_gemm(5, 0, 1, 1, 1, None, 2, 1, None, None, 2, 1, None, None, 2, 1,
+                        None, None, None) == -1
+    assert lib.amp_gemm(0, 1, 1, 1, 1, None, 2, 1, None, None, 1, 1, None, None, 2, 1,
+                        None, None, None) == -2
+    assert lib.amp_optimizer_step(None, None, None, None, 1, None, 1, -5, None, None, 0, None) == -1
+    assert lib.amp_nvfp4_quantize(None, 2, 17, 32, 32, 0, 0, 0, 0, 0, 0, None, None, None, None) == -1
+    # empty work is a successful no-op
+    assert lib.amp_cast(None, 0, 0, 4, 4, None, 1, 4, None, 0, None, None, None) == 0

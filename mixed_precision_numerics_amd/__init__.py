@@ -17,10 +17,10 @@ import numpy as np
 
 __all__ = [
     "F32", "F16", "BF16", "E4M3", "E5M2", "E2M1X2", "OP_N", "OP_T", "ROUND_RNE", "ROUND_SR",
-    "AMAX_MAX", "AMAX_MOST_RECENT", "OPT_SKIP_CHECK", "AmpError", "AdamWHParams",
+    "AMAX_MAX", "AMAX_MOST_RECENT", "OPT_SKIP_CHECK", "GEMM_FP8_NATIVE", "AmpError", "AdamWHParams",
     "ScalerParams", "DelayedRecipe", "BlockScales", "SCALER_STATE_DTYPE", "FP8_META_DTYPE",
     "lib_path", "load", "amp_abi_version", "amp_status_string", "amp_last_hip_error",
-    "amp_cast", "amp_gemm", "amp_scaler_init", "amp_optimizer_step", "amp_check_overflow",
+    "amp_cast", "amp_gemm", "amp_gemm_ex", "amp_scaler_init", "amp_optimizer_step", "amp_check_overflow",
     "amp_scaler_update", "amp_fp8_meta_init", "amp_delayed_scaling_update",
     "amp_nvfp4_quantize",
 ]
@@ -30,6 +30,7 @@ OP_N, OP_T = 0, 1
 ROUND_RNE, ROUND_SR = 0, 1
 AMAX_MAX, AMAX_MOST_RECENT = 0, 1
 OPT_SKIP_CHECK = 1
+GEMM_FP8_NATIVE = 1
 
 # Device-resident state layouts (mirror the C structs; for reading back).
 SCALER_STATE_DTYPE = np.dtype([("scale", "<f4"), ("growth_tracker", "<i4"),
@@ -78,6 +79,8 @@ _SIGS = {
     "amp_cast": ([_P, _I, _I64, _I64, _I64, _P, _I, _I64, _P, _I64, _P, _P, _P], _I),
     "amp_gemm": ([_I, _I, _I64, _I64, _I64, _P, _I, _I64, _P, _P, _I, _I64, _P, _P, _I, _I64,
                   _P, _P, _P], _I),
+    "amp_gemm_ex": ([_I, _I, _I64, _I64, _I64, _P, _I, _I64, _P, _P, _I, _I64, _P, _P, _I, _I64,
+                     _P, _P, _I, _P], _I),
     "amp_scaler_init": ([_P, ctypes.c_float, _P], _I),
     "amp_optimizer_step": ([_P, _P, _P, _P, _I, _P, _I, _I64, _P, _P, _I, _P], _I),
     "amp_check_overflow": ([_P, _I, _I64, _P, _P], _I),
@@ -163,6 +166,14 @@ def amp_gemm(opA, opB, M, N, K, A, at, lda, d_alphaA, B, bt, ldb, d_alphaB, C, c
         opA, opB, M, N, K, _ptr(A), at, lda, _ptr(d_alphaA), _ptr(B), bt, ldb, _ptr(d_alphaB),
         _ptr(C), ct, ldc, ctypes.byref(bsA) if bsA is not None else None,
         ctypes.byref(bsB) if bsB is not None else None, _stream(stream)))
+
+
+def amp_gemm_ex(opA, opB, M, N, K, A, at, lda, d_alphaA, B, bt, ldb, d_alphaB, C, ct, ldc,
+                bsA=None, bsB=None, flags=0, stream=None):
+    _check("amp_gemm_ex", load().amp_gemm_ex(
+        opA, opB, M, N, K, _ptr(A), at, lda, _ptr(d_alphaA), _ptr(B), bt, ldb, _ptr(d_alphaB),
+        _ptr(C), ct, ldc, ctypes.byref(bsA) if bsA is not None else None,
+        ctypes.byref(bsB) if bsB is not None else None, flags, _stream(stream)))
 
 
 def amp_scaler_init(d_state, init_scale=65536.0, stream=None):

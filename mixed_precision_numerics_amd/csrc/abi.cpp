@@ -90,6 +90,16 @@ int amp_gemm(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A, i
              int64_t lda, const float* d_alphaA, const void* B, int bt, int64_t ldb,
              const float* d_alphaB, void* C, int ct, int64_t ldc, const amp_block_scales* bsA,
              const amp_block_scales* bsB, void* stream) {
+  return amp_gemm_ex(opA, opB, M, N, K, A, at, lda, d_alphaA, B, bt, ldb, d_alphaB, C, ct, ldc,
+                     bsA, bsB, 0, stream);
+}
+
+int amp_gemm_ex(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A, int at,
+                int64_t lda, const float* d_alphaA, const void* B, int bt, int64_t ldb,
+                const float* d_alphaB, void* C, int ct, int64_t ldc,
+                const amp_block_scales* bsA, const amp_block_scales* bsB, int flags,
+                void* stream) {
+  if (flags & ~AMP_GEMM_FP8_NATIVE) return AMP_EINVAL;
   if (M < 0 || N < 0 || K < 0) return AMP_EINVAL;
   if ((opA != AMP_OP_N && opA != AMP_OP_T) || (opB != AMP_OP_N && opB != AMP_OP_T))
     return AMP_EINVAL;
@@ -120,6 +130,7 @@ int amp_gemm(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A, i
   if (int st = check_device()) return st;
   return hip_status(amp::launch_gemm(opA, opB, M, N, K, A, at, lda, d_alphaA, B, bt, ldb,
                                      d_alphaB, C, ct, ldc, bsA, bsB,
+                                     (flags & AMP_GEMM_FP8_NATIVE) != 0,
                                      static_cast<hipStream_t>(stream)));
 }
 

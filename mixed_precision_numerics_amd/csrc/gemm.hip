@@ -1,0 +1,510 @@
+// Low-precision GEMM with FP32 accumulation on CDNA4 MFMA (gfx950).
+//
+// What is computed: page "혼합 정밀도 학습" (itwiki), section "FP32 누산과
+// 연산별 정밀도" (16-bit products are accumulated in FP32 and the result is
+// written in 16 bits); page "FP8 혼합 정밀도 LLM 학습" (hwlabs), section
+// "GEMM 누적 정밀도 문제" (FP8 products, FP32 accumulation across partial
+// sums, output cast); page "Mixed Precision Training/es" (marovi), section
+// "La receta de precisión mixta".  For NVFP4 operands (page "Pretraining
+// Large Language Models with NVFP4", section 2.1) each E2M1 element times its
+// E4M3 block scale is an exact BF16 value (at most 6 significant bits, range
+// 2^-10 .. 2688), so the operand is decoded exactly to BF16 and the tensor
+// scales are applied in the epilogue.
+//
+//   C = out_cast( fl32(alphaA * alphaB) * sum_k op(A)[m,k] op(B)[k,n] )
+//
+// Kernel shape: one 256-thread block (4 waves, 2x2) per 256x256 output tile,
+// each wave a 128x128 sub-tile of 4x4 MFMA 32x32 blocks with FP32
+// accumulators.  K advances in steps whose LDS image is 128 bytes per row
+// (64 16-bit or 128 8-bit elements); two LDS stages alternate so the global
+// loads of step k+1 are in flight while step k runs on the matrix cores.
+// Operand rows are stored K-contiguous in LDS with a 16-byte-chunk XOR
+// swizzle (chunk ^ ((row ^ row >> 3) & 7)) so that both the MFMA fragment
+// reads (32 consecutive rows, one chunk) and the transposed stores (rows 8
+// apart) spread over the banks.  Operands whose contiguous dimension is M or N
+// (dgrad's weight, both wgrad operands) are loaded as 8x8 blocks and
+// transposed in registers with byte permutes before the LDS store.
+// Tiles are ordered so that each XCD (own L2) works on a contiguous range of
+// tiles, grouped 8 tile-rows at a time for L2 reuse of the B operand.
+#include "common.hpp"
+#include "formats.hpp"
+
+namespace amp {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kBM = 256, kBN = 256, kThreads = 256;
+constexpr int kRowBytes = 128;                       // LDS bytes per tile row per K-step
+constexpr int kOperandBytes = 256 * kRowBytes;       // one operand, one stage
+
+// How operands travel from HBM to the matrix cores.
+enum Path : int {
+  kP16 = 0,       // F16/BF16 operands, BF16/F16 MFMA 32x32x16, BK = 64
+  kPF8Exact = 1,  // FP8 operands decoded to BF16 on the way to LDS, BF16 MFMA, BK = 64
+  kPF8Native = 2, // FP8 operands in LDS, FP8 MFMA 32x32x64, BK = 128
+  kPFP4 = 3,      // NVFP4 operands decoded (x block scale) to BF16, BF16 MFMA, BK = 64
+};
+
+struct GemmArgs {
+  const void* A;
+  const void* B;
+  void* C;
+  int64_t M, N, K, lda, ldb, ldc;
+  const float* alphaA;
+  const float* alphaB;
+  const uint8_t* sA;
+  const uint8_t* sB;
+  int64_t ldsA, ldsB;
+  int s2dA, s2dB;
+};
+
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * kRowBytes + ((chunk ^ ((row ^ (row >> 3)) & 7)) << 4);
+}
+
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *static_cast<const u32x4*>(p); }
+
+// 8x8 transpose of 16-bit elements held as 8 rows of 4 words.
+__device__ __forceinline__ void transpose8x8_16(const u32x4 (&v)[8], u32x4 (&o)[8]) {
+#pragma unroll
+  for (int mm = 0; mm < 8; ++mm) {
+    const uint32_t sel = (mm & 1) ? 0x07060302u : 0x05040100u;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      o[mm][q] = __builtin_amdgcn_perm(v[2 * q + 1][mm >> 1], v[2 * q][mm >> 1], sel);
+    }
+  }
+}
+
+// FP8 (E4M3 or E5M2) -> BF16, exact: 2 values per conversion instruction.
+template <int FMT, bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  if constexpr (FMT == AMP_E4M3)
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+  else
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, HI));
+}
+
+// Two E2M1 codes (byte SEL of w) times the scale S -> two BF16 (exact).
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w, float S) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, S, SEL));
+}
+
+// ---------------------------------------------------------------- loaders
+// Each loader fetches one K-step of one operand (256 rows) into registers
+// (`fetch`) and writes it to an LDS stage (`store`).  R: rows of the operand
+// (M for A, N for B); ld: leading dimension in elements (bytes for FP4).
+
+template <int ET, bool KC, int PATH>
+struct Loader;
+
+// 16-bit, K-contiguous: thread t owns chunk t%8 of rows t/8 + 32i.
+template <int ET>
+struct Loader<ET, true, kP16> {
+  u32x4 v[8];
+  __device__ __forceinline__ void fetch(const void* X, int64_t ld, int64_t R, int64_t K,
+                                        int64_t r0, int64_t k0, const uint8_t*, int64_t, int) {
+    const int t = threadIdx.x;
+    const int c = t & 7;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t gr = r0 + (t >> 3) + 32 * i;
+      const int64_t gk = k0 + 8 * c;
+      v[i] = (gr < R && gk < K) ? ld16(static_cast<const uint16_t*>(X) + gr * ld + gk)
+                                : u32x4{0, 0, 0, 0};
+    }
+  }
+  __device__ __forceinline__ void store(uint8_t* lds) const {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<u32x4*>(lds + swz((t >> 3) + 32 * i, t & 7)) = v[i];
+  }
+};
+
+// 16-bit, M/N-contiguous: thread t loads k rows 8g..8g+7 (g = t/32) of the
+// 8-wide column chunk c = t%32, i.e. an 8x8 block, and transposes it.
+template <int ET>
+struct Loader<ET, false, kP16> {
+  u32x4 v[8];
+  __device__ __forceinline__ void fetch(const void* X, int64_t ld, int64_t R, int64_t K,
+                                        int64_t r0, int64_t k0, const uint8_t*, int64_t, int) {
+    const int t = threadIdx.x;
+    const int g = t >> 5, c = t & 31;
+    const int64_t gr = r0 + 8 * c;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t gk = k0 + 8 * g + i;
+      v[i] = (gr < R && gk < K) ? ld16(static_cast<const uint16_t*>(X) + gk * ld + gr)
+                                : u32x4{0, 0, 0, 0};
+    }
+  }
+  __device__ __forceinline__ void store(uint8_t* lds) const {
+    const int t = threadIdx.x;
+    const int g = t >> 5, c = t & 31;
+    u32x4 o[8];
+    transpose8x8_16(v, o);
+#pragma unroll
+    for (int mm = 0; mm < 8; ++mm) *reinterpret_cast<u32x4*>(lds + swz(8 * c + mm, g)) = o[mm];
+  }
+};
+
+// FP8 -> BF16 (exact path), K-contiguous, BK = 64: thread t loads 16 FP8 of
+// row t/4 + 64i at k offset 16*(t%4) and writes two 16-byte BF16 chunks.
+template <int ET>
+struct Loader<ET, true, kPF8Exact> {
+  u32x4 v[4];
+  __device__ __forceinline__ void fetch(const void* X, int64_t ld, int64_t R, int64_t K,
+                                        int64_t r0, int64_t k0, const uint8_t*, int64_t, int) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t gr = r0 + (t >> 2) + 64 * i;
+      const int64_t gk = k0 + 16 * (t & 3);
+      v[i] = (gr < R && gk < K) ? ld16(static_cast<const uint8_t*>(X) + gr * ld + gk)
+                                : u32x4{0, 0, 0, 0};
+    }
+  }
+  __device__ __forceinline__ void store(uint8_t* lds) const {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = (t >> 2) + 64 * i;
+      u32x4 lo, hi;
+      lo[0] = fp8x2_to_bf16x2<ET, false>(v[i][0]); lo[1] = fp8x2_to_bf16x2<ET, true>(v[i][0]);
+      lo[2] = fp8x2_to_bf16x2<ET, false>(v[i][1]); lo[3] = fp8x2_to_bf16x2<ET, true>(v[i][1]);
+      hi[0] = fp8x2_to_bf16x2<ET, false>(v[i][2]); hi[1] = fp8x2_to_bf16x2<ET, true>(v[i][2]);
+      hi[2] = fp8x2_to_bf16x2<ET, false>(v[i][3]); hi[3] = fp8x2_to_bf16x2<ET, true>(v[i][3]);
+      *reinterpret_cast<u32x4*>(lds + swz(row, 2 * (t & 3))) = lo;
+      *reinterpret_cast<u32x4*>(lds + swz(row, 2 * (t & 3) + 1)) = hi;
+    }
+  }
+};
+
+// FP8 native, K-contiguous, BK = 128: same chunk map as the 16-bit loader.
+template <int ET>
+struct Loader<ET, true, kPF8Native> {
+  u32x4 v[8];
+  __device__ __forceinline__ void fetch(const void* X, int64_t ld, int64_t R, int64_t K,
+                                        int64_t r0, int64_t k0, const uint8_t*, int64_t, int) {
+    const int t = threadIdx.x;
+    const int c = t & 7;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t gr = r0 + (t >> 3) + 32 * i;
+      const int64_t gk = k0 + 16 * c;
+      v[i] = (gr < R && gk < K) ? ld16(static_cast<const uint8_t*>(X) + gr * ld + gk)
+                                : u32x4{0, 0, 0, 0};
+    }
+  }
+  __device__ __forceinline__ void store(uint8_t* lds) const {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<u32x4*>(lds + swz((t >> 3) + 32 * i, t & 7)) = v[i];
+  }
+};
+
+// NVFP4 -> BF16, K-contiguous, BK = 64: thread t loads 32 E2M1 codes (16 B) of
+// row t/2 + 128i at k offset 32*(t%2) plus their two E4M3 block scales, and
+// writes four 16-byte BF16 chunks of e2m1 * S.
+template <int ET>
+struct Loader<ET, true, kPFP4> {
+  u32x4 v[2];
+  uint32_t s[2];
+  __device__ __forceinline__ void fetch(const void* X, int64_t ld, int64_t R, int64_t K,
+                                        int64_t r0, int64_t k0, const uint8_t* sc, int64_t lds_,
+                                        int s2d) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int64_t gr = r0 + (t >> 1) + 128 * i;
+      const int64_t gk = k0 + 32 * (t & 1);
+      const bool ok = gr < R && gk < K;
+      v[i] = ok ? ld16(static_cast<const uint8_t*>(X) + gr * ld + gk / 2) : u32x4{0, 0, 0, 0};
+      const int64_t srow = s2d ? gr / 16 : gr;
+      s[i] = ok ? *reinterpret_cast<const uint16_t*>(sc + srow * lds_ + gk / 16) : 0u;
+    }
+  }
+  __device__ __forceinline__ void store(uint8_t* lds) const {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int row = (t >> 1) + 128 * i;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const float S = e4m3_to_f32((s[i] >> (8 * half)) & 0xffu);
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          const uint32_t w = v[i][2 * half + cc];
+          u32x4 o;
+          o[0] = fp4x2_to_bf16x2<0>(w, S);
+          o[1] = fp4x2_to_bf16x2<1>(w, S);
+          o[2] = fp4x2_to_bf16x2<2>(w, S);
+          o[3] = fp4x2_to_bf16x2<3>(w, S);
+          *reinterpret_cast<u32x4*>(lds + swz(row, 4 * (t & 1) + 2 * half + cc)) = o;
+        }
+      }
+    }
+  }
+};
+
+// ----------------------------------------------------------------- kernel
+
+template <int CT>
+__device__ __forceinline__ void store_c(void* C, int64_t idx, float x) {
+  if constexpr (CT == AMP_F32) static_cast<float*>(C)[idx] = x;
+  else if constexpr (CT == AMP_BF16) static_cast<uint16_t*>(C)[idx] = static_cast<uint16_t>(f32_to_bf16(x));
+  else static_cast<uint16_t*>(C)[idx] = static_cast<uint16_t>(f32_to_f16(x));
+}
+
+template <int AT, int BT, bool A_KC, bool B_KC, int PATH, int CT>
+__global__ __launch_bounds__(kThreads, 1) void gemm_mfma(GemmArgs g) {
+  __shared__ __align__(16) uint8_t smem[2][2][kOperandBytes];
+  constexpr int BK = PATH == kPF8Native ? 128 : 64;
+
+  // XCD-aware, L2-grouped tile order
+  const int64_t nbm = (g.M + kBM - 1) / kBM, nbn = (g.N + kBN - 1) / kBN;
+  const int64_t total = nbm * nbn;
+  int64_t tile = blockIdx.x;
+  if (total % 8 == 0) tile = (tile % 8) * (total / 8) + tile / 8;
+  constexpr int64_t kGroup = 8;
+  const int64_t group = tile / (kGroup * nbn);
+  const int64_t first_m = group * kGroup;
+  const int64_t gsz = nbm - first_m < kGroup ? nbm - first_m : kGroup;
+  const int64_t in_group = tile % (kGroup * nbn);
+  const int64_t tm = first_m + in_group % gsz;
+  const int64_t tn = in_group / gsz;
+  const int64_t m0 = tm * kBM, n0 = tn * kBN;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  Loader<AT, A_KC, PATH> la;
+  Loader<BT, B_KC, PATH> lb;
+  const int64_t nk = (g.K + BK - 1) / BK;
+
+  if (nk > 0) {
+    la.fetch(g.A, g.lda, g.M, g.K, m0, 0, g.sA, g.ldsA, g.s2dA);
+    lb.fetch(g.B, g.ldb, g.N, g.K, n0, 0, g.sB, g.ldsB, g.s2dB);
+    la.store(smem[0][0]);
+    lb.store(smem[0][1]);
+    __syncthreads();
+  }
+
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const int cur = static_cast<int>(kt & 1);
+    if (kt + 1 < nk) {
+      la.fetch(g.A, g.lda, g.M, g.K, m0, (kt + 1) * BK, g.sA, g.ldsA, g.s2dA);
+      lb.fetch(g.B, g.ldb, g.N, g.K, n0, (kt + 1) * BK, g.sB, g.ldsB, g.s2dB);
+    }
+    const uint8_t* sa = smem[cur][0];
+    const uint8_t* sb = smem[cur][1];
+    if constexpr (PATH == kPF8Native) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        i32x8 af[4], bfr[4];
+        const int ch = 4 * ks + 2 * (lane >> 5);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          const int row = wm * 128 + mb * 32 + (lane & 31);
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(sa + swz(row, ch));
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(sa + swz(row, ch + 1));
+          af[mb] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                         (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        }
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const int row = wn * 128 + nb * 32 + (lane & 31);
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(sb + swz(row, ch));
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(sb + swz(row, ch + 1));
+          bfr[nb] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                          (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        }
+        constexpr int fa = AT == AMP_E4M3 ? 0 : 1;
+        constexpr int fb = BT == AMP_E4M3 ? 0 : 1;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                af[mb], bfr[nb], acc[mb][nb], fa, fb, 0, 127, 0, 127);
+      }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        u32x4 af[4], bfr[4];
+        const int ch = 2 * ks + (lane >> 5);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+          af[mb] = *reinterpret_cast<const u32x4*>(sa + swz(wm * 128 + mb * 32 + (lane & 31), ch));
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          bfr[nb] = *reinterpret_cast<const u32x4*>(sb + swz(wn * 128 + nb * 32 + (lane & 31), ch));
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) {
+            if constexpr (PATH == kP16 && AT == AMP_F16)
+              acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                  __builtin_bit_cast(f16x8_t, af[mb]), __builtin_bit_cast(f16x8_t, bfr[nb]),
+                  acc[mb][nb], 0, 0, 0);
+            else
+              acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  __builtin_bit_cast(bf16x8_t, af[mb]), __builtin_bit_cast(bf16x8_t, bfr[nb]),
+                  acc[mb][nb], 0, 0, 0);
+          }
+      }
+    }
+    if (kt + 1 < nk) {
+      la.store(smem[cur ^ 1][0]);
+      lb.store(smem[cur ^ 1][1]);
+    }
+    __syncthreads();
+  }
+
+  const float alpha = (g.alphaA ? *g.alphaA : 1.0f) * (g.alphaB ? *g.alphaB : 1.0f);
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int64_t col = n0 + wn * 128 + nb * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + wm * 128 + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (row < g.M && col < g.N) store_c<CT>(g.C, row * g.ldc + col, acc[mb][nb][r] * alpha);
+      }
+    }
+}
+
+// ---------------------------------------------------------------- generic
+// Any shape, stride and layout (small or odd GEMMs): one output per thread,
+// operands widened exactly to FP32, products exact, FP32 fused accumulation.
+template <int ET>
+__device__ __forceinline__ float load_elem(const void* X, int64_t idx) {
+  if constexpr (ET == AMP_BF16) return bf16_to_f32(static_cast<const uint16_t*>(X)[idx]);
+  else if constexpr (ET == AMP_F16) return f16_to_f32(static_cast<const uint16_t*>(X)[idx]);
+  else if constexpr (ET == AMP_E4M3) return e4m3_to_f32(static_cast<const uint8_t*>(X)[idx]);
+  else return e5m2_to_f32(static_cast<const uint8_t*>(X)[idx]);
+}
+
+template <int ET>
+__device__ __forceinline__ float operand(const void* X, int64_t ld, bool kc, int64_t r, int64_t k,
+                                         const uint8_t* sc, int64_t lds_, int s2d) {
+  if constexpr (ET == AMP_E2M1X2) {
+    const uint8_t byte = static_cast<const uint8_t*>(X)[r * ld + k / 2];
+    const float e = e2m1_to_f32((k & 1) ? (byte >> 4) : (byte & 0xf));
+    const float S = e4m3_to_f32(sc[(s2d ? r / 16 : r) * lds_ + k / 16]);
+    return e * S;
+  } else {
+    return load_elem<ET>(X, kc ? r * ld + k : k * ld + r);
+  }
+}
+
+template <int AT, int BT, int CT>
+__global__ __launch_bounds__(256) void gemm_generic(GemmArgs g, int a_kc, int b_kc) {
+  const int64_t col = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x & 15);
+  const int64_t row = static_cast<int64_t>(blockIdx.y) * 16 + (threadIdx.x >> 4);
+  if (row >= g.M || col >= g.N) return;
+  float acc = 0.0f;
+  for (int64_t k = 0; k < g.K; ++k) {
+    const float a = operand<AT>(g.A, g.lda, a_kc, row, k, g.sA, g.ldsA, g.s2dA);
+    const float b = operand<BT>(g.B, g.ldb, b_kc, col, k, g.sB, g.ldsB, g.s2dB);
+    acc = __builtin_fmaf(a, b, acc);
+  }
+  const float alpha = (g.alphaA ? *g.alphaA : 1.0f) * (g.alphaB ? *g.alphaB : 1.0f);
+  store_c<CT>(g.C, row * g.ldc + col, acc * alpha);
+}
+
+// ---------------------------------------------------------------- dispatch
+template <int AT, int BT, bool A_KC, bool B_KC, int PATH>
+hipError_t launch_mfma(const GemmArgs& g, int ct, hipStream_t s) {
+  const int64_t tiles = ((g.M + kBM - 1) / kBM) * ((g.N + kBN - 1) / kBN);
+  const dim3 grid(static_cast<unsigned>(tiles));
+  switch (ct) {
+    case AMP_F32: gemm_mfma<AT, BT, A_KC, B_KC, PATH, AMP_F32><<<grid, kThreads, 0, s>>>(g); break;
+    case AMP_BF16: gemm_mfma<AT, BT, A_KC, B_KC, PATH, AMP_BF16><<<grid, kThreads, 0, s>>>(g); break;
+    default: gemm_mfma<AT, BT, A_KC, B_KC, PATH, AMP_F16><<<grid, kThreads, 0, s>>>(g); break;
+  }
+  return hipGetLastError();
+}
+
+template <int AT, int BT>
+hipError_t launch_generic(const GemmArgs& g, bool a_kc, bool b_kc, int ct, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((g.N + 15) / 16), static_cast<unsigned>((g.M + 15) / 16));
+  switch (ct) {
+    case AMP_F32: gemm_generic<AT, BT, AMP_F32><<<grid, 256, 0, s>>>(g, a_kc, b_kc); break;
+    case AMP_BF16: gemm_generic<AT, BT, AMP_BF16><<<grid, 256, 0, s>>>(g, a_kc, b_kc); break;
+    default: gemm_generic<AT, BT, AMP_F16><<<grid, 256, 0, s>>>(g, a_kc, b_kc); break;
+  }
+  return hipGetLastError();
+}
+
+template <int ET>
+hipError_t launch_16(const GemmArgs& g, bool a_kc, bool b_kc, bool fast, int ct, hipStream_t s) {
+  if (!fast) return launch_generic<ET, ET>(g, a_kc, b_kc, ct, s);
+  if (a_kc && b_kc) return launch_mfma<ET, ET, true, true, kP16>(g, ct, s);
+  if (a_kc) return launch_mfma<ET, ET, true, false, kP16>(g, ct, s);
+  if (b_kc) return launch_mfma<ET, ET, false, true, kP16>(g, ct, s);
+  return launch_mfma<ET, ET, false, false, kP16>(g, ct, s);
+}
+
+template <int AT, int BT>
+hipError_t launch_f8(const GemmArgs& g, bool fast, bool native, int ct, hipStream_t s) {
+  if (!fast) return launch_generic<AT, BT>(g, true, true, ct, s);
+  if (native) return launch_mfma<AT, BT, true, true, kPF8Native>(g, ct, s);
+  return launch_mfma<AT, BT, true, true, kPF8Exact>(g, ct, s);
+}
+
+}  // namespace
+
+// fp8_native: use the FP8 matrix-core dot product (reduced internal precision
+// of the 64-term partial sums) instead of the exact BF16 route.
+hipError_t launch_gemm(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A,
+                       int at, int64_t lda, const float* alphaA, const void* B, int bt,
+                       int64_t ldb, const float* alphaB, void* C, int ct, int64_t ldc,
+                       const amp_block_scales* bsA, const amp_block_scales* bsB,
+                       bool fp8_native, hipStream_t s) {
+  GemmArgs g{A, B, C, M, N, K, lda, ldb, ldc, alphaA, alphaB,
+             bsA ? bsA->scales : nullptr, bsB ? bsB->scales : nullptr,
+             bsA ? bsA->ld : 0, bsB ? bsB->ld : 0, bsA ? bsA->block2d : 0,
+             bsB ? bsB->block2d : 0};
+  const bool a_kc = opA == AMP_OP_N, b_kc = opB == AMP_OP_T;
+  if (at == AMP_E2M1X2) {
+    const bool fast = aligned(A, 16) && aligned(B, 16) && lda % 16 == 0 && ldb % 16 == 0 &&
+                      K % 64 == 0 && aligned(g.sA, 2) && aligned(g.sB, 2) && g.ldsA % 2 == 0 &&
+                      g.ldsB % 2 == 0;
+    if (!fast) return launch_generic<AMP_E2M1X2, AMP_E2M1X2>(g, true, true, ct, s);
+    return launch_mfma<AMP_E2M1X2, AMP_E2M1X2, true, true, kPFP4>(g, ct, s);
+  }
+  if (at == AMP_E4M3 || at == AMP_E5M2) {
+    const bool fast = aligned(A, 16) && aligned(B, 16) && lda % 16 == 0 && ldb % 16 == 0 &&
+                      K % 16 == 0;
+    if (at == AMP_E4M3 && bt == AMP_E4M3) return launch_f8<AMP_E4M3, AMP_E4M3>(g, fast, fp8_native, ct, s);
+    if (at == AMP_E4M3) return launch_f8<AMP_E4M3, AMP_E5M2>(g, fast, fp8_native, ct, s);
+    if (bt == AMP_E4M3) return launch_f8<AMP_E5M2, AMP_E4M3>(g, fast, fp8_native, ct, s);
+    return launch_f8<AMP_E5M2, AMP_E5M2>(g, fast, fp8_native, ct, s);
+  }
+  // 16-bit: the vector path needs 16-byte aligned rows and the contiguous
+  // extent of every operand a multiple of 8 elements
+  bool fast = aligned(A, 16) && aligned(B, 16) && lda % 8 == 0 && ldb % 8 == 0;
+  fast = fast && (a_kc ? K % 8 == 0 : M % 8 == 0) && (b_kc ? K % 8 == 0 : N % 8 == 0);
+  if (at == AMP_BF16) return launch_16<AMP_BF16>(g, a_kc, b_kc, fast, ct, s);
+  return launch_16<AMP_F16>(g, a_kc, b_kc, fast, ct, s);
+}
+
+}  // namespace amp

@@ -243,7 +243,7 @@ hipError_t dispatch_layout(const void* x, int64_t rows, int64_t cols, int64_t ld
     const int64_t n = rows * cols;
     const bool vec = aligned(x, 16) && aligned(y, 8 * yb);
     int64_t blocks = (n / 8 + kFlatThreads - 1) / kFlatThreads;
-    if (blocks > 256 * 16) blocks = 256 * 16;
+    if (blocks > 256 * 64) blocks = 256 * 64;
     if (blocks < 1) blocks = 1;
     if (vec)
       cast_flat<XT, YT, true><<<dim3(static_cast<unsigned>(blocks)), kFlatThreads, 0, s>>>(

@@ -21,26 +21,29 @@ namespace amp {
 __device__ __forceinline__ uint32_t fbits(float x) { return __float_as_uint(x); }
 __device__ __forceinline__ float bitsf(uint32_t u) { return __uint_as_float(u); }
 
+// All conversions below are branch-free: both the normal-range and the
+// subnormal-range result are formed and selected, so a wave never diverges.
+
 // ---- FP32 -> FP16 ---------------------------------------------------------
 __device__ __forceinline__ uint32_t f32_to_f16(float x) {
   const uint32_t u = fbits(x);
   const uint32_t s = (u >> 16) & 0x8000u;
   const uint32_t a = u & 0x7fffffffu;
-  if (a > 0x7f800000u) return 0x7e00u;               // NaN
-  if (a >= 0x477ff000u) return s | 0x7c00u;          // >= 65520 rounds to inf
-  if (a >= 0x38800000u) {                            // normal: >= 2^-14
-    const uint32_t r = a + 0xfffu + ((a >> 13) & 1u);
-    return s | ((r - 0x38000000u) >> 13);
-  }
+  // normal result (|x| >= 2^-14): round the mantissa at bit 13, rebias by 112
+  const uint32_t rn = (a + 0xfffu + ((a >> 13) & 1u) - 0x38000000u) >> 13;
   // |x| < 2^-14: spacing 2^-24 = ulp of [0.5, 1)
-  return s | (fbits(bitsf(a) + 0.5f) - 0x3f000000u);
+  const uint32_t rs = fbits(bitsf(a) + 0.5f) - 0x3f000000u;
+  uint32_t r = a >= 0x38800000u ? rn : rs;
+  r = a >= 0x477ff000u ? 0x7c00u : r;                 // >= 65520 rounds to inf
+  r |= s;
+  return a > 0x7f800000u ? 0x7e00u : r;               // NaN
 }
 
 // ---- FP32 -> BF16 ---------------------------------------------------------
 __device__ __forceinline__ uint32_t f32_to_bf16(float x) {
   const uint32_t u = fbits(x);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  return (u & 0x7fffffffu) > 0x7f800000u ? 0x7fc0u : r;
 }
 
 // ---- FP32 -> E4M3 (saturating) -------------------------------------------
@@ -48,13 +51,12 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
   const uint32_t u = fbits(x);
   const uint32_t s = (u >> 24) & 0x80u;
   const uint32_t a = u & 0x7fffffffu;
-  if (a > 0x7f800000u) return 0x7fu;
-  if (a >= 0x43e00000u) return s | 0x7eu;            // >= 448 (and inf)
-  if (a >= 0x3c800000u) {                            // normal: >= 2^-6
-    const uint32_t r = a + 0x7ffffu + ((a >> 20) & 1u);
-    return s | ((r - 0x3c000000u) >> 20);
-  }
-  return s | (fbits(bitsf(a) + 16384.0f) - 0x46800000u);   // spacing 2^-9
+  const uint32_t rn = (a + 0x7ffffu + ((a >> 20) & 1u) - 0x3c000000u) >> 20;  // >= 2^-6
+  const uint32_t rs = fbits(bitsf(a) + 16384.0f) - 0x46800000u;              // spacing 2^-9
+  uint32_t r = a >= 0x3c800000u ? rn : rs;
+  r = a >= 0x43e00000u ? 0x7eu : r;                   // >= 448 (and inf) saturate
+  r |= s;
+  return a > 0x7f800000u ? 0x7fu : r;
 }
 
 // ---- FP32 -> E5M2 (saturating) -------------------------------------------
@@ -62,45 +64,41 @@ __device__ __forceinline__ uint32_t f32_to_e5m2(float x) {
   const uint32_t u = fbits(x);
   const uint32_t s = (u >> 24) & 0x80u;
   const uint32_t a = u & 0x7fffffffu;
-  if (a > 0x7f800000u) return 0x7fu;
-  if (a >= 0x47600000u) return s | 0x7bu;            // >= 57344 (and inf)
-  if (a >= 0x38800000u) {                            // normal: >= 2^-14
-    const uint32_t r = a + 0xfffffu + ((a >> 21) & 1u);
-    return s | ((r - 0x38000000u) >> 21);
-  }
-  return s | (fbits(bitsf(a) + 128.0f) - 0x43000000u);     // spacing 2^-16
+  const uint32_t rn = (a + 0xfffffu + ((a >> 21) & 1u) - 0x38000000u) >> 21;  // >= 2^-14
+  const uint32_t rs = fbits(bitsf(a) + 128.0f) - 0x43000000u;                // spacing 2^-16
+  uint32_t r = a >= 0x38800000u ? rn : rs;
+  r = a >= 0x47600000u ? 0x7bu : r;                   // >= 57344 (and inf) saturate
+  r |= s;
+  return a > 0x7f800000u ? 0x7fu : r;
 }
 
 // ---- widening (exact) -----------------------------------------------------
 __device__ __forceinline__ float bf16_to_f32(uint32_t c) { return bitsf(c << 16); }
 
+// FP16 -> FP32 with the hardware conversion: exact for every code (FP16
+// subnormals are kept), NaN stays NaN.
 __device__ __forceinline__ float f16_to_f32(uint32_t c) {
-  const uint32_t s = (c & 0x8000u) << 16;
-  const uint32_t e = (c >> 10) & 0x1fu;
-  const uint32_t m = c & 0x3ffu;
-  if (e == 0x1fu) return bitsf(s | 0x7f800000u | (m << 13));
-  if (e == 0) {  // subnormal or zero: m * 2^-24, exact in FP32
-    return bitsf(s | fbits(static_cast<float>(m) * 5.9604644775390625e-8f));
-  }
-  return bitsf(s | ((e + 112u) << 23) | (m << 13));
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(c)));
 }
 
 __device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
   const uint32_t s = (c & 0x80u) << 24;
   const uint32_t e = (c >> 3) & 0xfu;
   const uint32_t m = c & 0x7u;
-  if (e == 0xfu && m == 0x7u) return bitsf(0x7fc00000u);
-  if (e == 0) return bitsf(s | fbits(static_cast<float>(m) * 0.001953125f));
-  return bitsf(s | ((e + 120u) << 23) | (m << 20));
+  const uint32_t sub = fbits(static_cast<float>(m) * 0.001953125f);
+  const uint32_t nrm = ((e + 120u) << 23) | (m << 20);
+  const uint32_t r = s | (e == 0 ? sub : nrm);
+  return bitsf((e == 0xfu && m == 0x7u) ? 0x7fc00000u : r);
 }
 
 __device__ __forceinline__ float e5m2_to_f32(uint32_t c) {
   const uint32_t s = (c & 0x80u) << 24;
   const uint32_t e = (c >> 2) & 0x1fu;
   const uint32_t m = c & 0x3u;
-  if (e == 0x1fu) return bitsf(s | 0x7f800000u | (m << 21));
-  if (e == 0) return bitsf(s | fbits(static_cast<float>(m) * 1.52587890625e-5f));
-  return bitsf(s | ((e + 112u) << 23) | (m << 21));
+  const uint32_t sub = fbits(static_cast<float>(m) * 1.52587890625e-5f);
+  const uint32_t nrm = ((e + 112u) << 23) | (m << 21);
+  const uint32_t spec = 0x7f800000u | (m << 21);
+  return bitsf(s | (e == 0 ? sub : (e == 0x1fu ? spec : nrm)));
 }
 
 // ---- E2M1 (FP4) -----------------------------------------------------------

@@ -112,3 +112,32 @@ def test_amax_is_order_free_and_deterministic():
         res.append(int(host(amax, np.uint32)[0]))
     want = int(OC.amax_bits(OC.widen_to_f32_bits(codes, F.BF16)))
     assert res == [want] * 3
+
+
+def _structured_f32_bits(low_bits, patterns, seed=0):
+    """Every sign/exponent/top-mantissa combination with chosen low bits."""
+    top = np.arange(1 << (32 - low_bits), dtype=np.uint64) << np.uint64(low_bits)
+    rnd = np.random.default_rng(seed).integers(0, 1 << low_bits, size=top.size, dtype=np.uint64)
+    parts = [top | np.uint64(p) for p in patterns] + [top | rnd]
+    return np.concatenate(parts).astype(np.uint32)
+
+
+@pytest.mark.parametrize("yt,low,pats", [
+    (amp.F16, 13, [0, 1, 0xFFF, 0x1000, 0x1001, 0x1FFF]),
+    (amp.BF16, 16, [0, 1, 0x7FFF, 0x8000, 0x8001, 0xFFFF]),
+    (amp.E4M3, 20, [0, 1, 0x7FFFF, 0x80000, 0x80001, 0xFFFFF]),
+    (amp.E5M2, 21, [0, 1, 0xFFFFF, 0x100000, 0x100001, 0x1FFFFF])])
+def test_cast_structured_sweep_of_all_binades(yt, low, pats):
+    """All FP32 exponents and leading mantissa bits, each with the rounding-
+    critical low bit patterns (exact ties, one above, one below, random)."""
+    bits = _structured_f32_bits(low, pats, seed=yt)
+    fout, odt = OUT[yt]
+    want, want_amax = OC.cast(bits, F.F32, fout, None)
+    n = bits.size
+    y = empty(n * np.dtype(odt).itemsize)
+    amax = f32_dev([0.0])
+    amp.amp_cast(dev(bits), amp.F32, 1, n, n, y, yt, n, d_amax=amax)
+    got = host(y, odt)[:n]
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, (bad[:8], bits[bad[:8]], got[bad[:8]], want[bad[:8]])
+    assert host(amax, np.uint32)[0] == want_amax

@@ -16,16 +16,21 @@
 // Kernel shape: one 256-thread block (4 waves, 2x2) per 256x256 output tile,
 // each wave a 128x128 sub-tile of 4x4 MFMA 32x32 blocks with FP32
 // accumulators.  K advances in steps whose LDS image is 128 bytes per row
-// (64 16-bit or 128 8-bit elements); two LDS stages alternate so the global
-// loads of step k+1 are in flight while step k runs on the matrix cores.
+// (64 16-bit or 128 8-bit elements) and two LDS stages alternate.
 // Operand rows are stored K-contiguous in LDS with a 16-byte-chunk XOR
 // swizzle (chunk ^ ((row ^ row >> 3) & 7)) so that both the MFMA fragment
 // reads (32 consecutive rows, one chunk) and the transposed stores (rows 8
-// apart) spread over the banks.  Operands whose contiguous dimension is M or N
-// (dgrad's weight, both wgrad operands) are loaded as 8x8 blocks and
-// transposed in registers with byte permutes before the LDS store.
+// apart) spread over the banks (measured: no bank conflicts).
+//  * gemm_mfma_d2l: both operands K-contiguous, full tiles.  The next K-step
+//    is fetched with direct-to-LDS loads (global_load_lds, 16 B per lane, no
+//    VGPR staging): lane l of each 1 KB load fetches the logical chunk that
+//    the swizzle places at LDS byte 16*l.
+//  * gemm_mfma: any layout and ragged edges.  The next K-step is staged in
+//    registers; operands whose contiguous dimension is M or N (dgrad's
+//    weight, both wgrad operands) are loaded as 8x8 blocks and transposed in
+//    registers with byte permutes before the LDS store.
 // Tiles are ordered so that each XCD (own L2) works on a contiguous range of
-// tiles, grouped 8 tile-rows at a time for L2 reuse of the B operand.
+// tiles, grouped 8 tile-rows at a time for L2 reuse.
 #include "common.hpp"
 #include "formats.hpp"
 
@@ -107,6 +112,7 @@ struct Loader;
 template <int ET>
 struct Loader<ET, true, kP16> {
   u32x4 v[8];
+  template <bool CHECK>
   __device__ __forceinline__ void fetch(const void* X, int64_t ld, int64_t R, int64_t K,
                                         int64_t r0, int64_t k0, const uint8_t*, int64_t, int) {
     const int t = threadIdx.x;
@@ -115,7 +121,7 @@ struct Loader<ET, true, kP16> {
     for (int i = 0; i < 8; ++i) {
       const int64_t gr = r0 + (t >> 3) + 32 * i;
       const int64_t gk = k0 + 8 * c;
-      v[i] = (gr < R && gk < K) ? ld16(static_cast<const uint16_t*>(X) + gr * ld + gk)
+      v[i] = (!CHECK || (gr < R && gk < K)) ? ld16(static_cast<const uint16_t*>(X) + gr * ld + gk)
                                 : u32x4{0, 0, 0, 0};
     }
   }
@@ -132,6 +138,7 @@ struct Loader<ET, true, kP16> {
 template <int ET>
 struct Loader<ET, false, kP16> {
   u32x4 v[8];
+  template <bool CHECK>
   __device__ __forceinline__ void fetch(const void* X, int64_t ld, int64_t R, int64_t K,
                                         int64_t r0, int64_t k0, const uint8_t*, int64_t, int) {
     const int t = threadIdx.x;
@@ -140,7 +147,7 @@ struct Loader<ET, false, kP16> {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int64_t gk = k0 + 8 * g + i;
-      v[i] = (gr < R && gk < K) ? ld16(static_cast<const uint16_t*>(X) + gk * ld + gr)
+      v[i] = (!CHECK || (gr < R && gk < K)) ? ld16(static_cast<const uint16_t*>(X) + gk * ld + gr)
                                 : u32x4{0, 0, 0, 0};
     }
   }
@@ -159,6 +166,7 @@ struct Loader<ET, false, kP16> {
 template <int ET>
 struct Loader<ET, true, kPF8Exact> {
   u32x4 v[4];
+  template <bool CHECK>
   __device__ __forceinline__ void fetch(const void* X, int64_t ld, int64_t R, int64_t K,
                                         int64_t r0, int64_t k0, const uint8_t*, int64_t, int) {
     const int t = threadIdx.x;
@@ -166,7 +174,7 @@ struct Loader<ET, true, kPF8Exact> {
     for (int i = 0; i < 4; ++i) {
       const int64_t gr = r0 + (t >> 2) + 64 * i;
       const int64_t gk = k0 + 16 * (t & 3);
-      v[i] = (gr < R && gk < K) ? ld16(static_cast<const uint8_t*>(X) + gr * ld + gk)
+      v[i] = (!CHECK || (gr < R && gk < K)) ? ld16(static_cast<const uint8_t*>(X) + gr * ld + gk)
                                 : u32x4{0, 0, 0, 0};
     }
   }
@@ -190,6 +198,7 @@ struct Loader<ET, true, kPF8Exact> {
 template <int ET>
 struct Loader<ET, true, kPF8Native> {
   u32x4 v[8];
+  template <bool CHECK>
   __device__ __forceinline__ void fetch(const void* X, int64_t ld, int64_t R, int64_t K,
                                         int64_t r0, int64_t k0, const uint8_t*, int64_t, int) {
     const int t = threadIdx.x;
@@ -198,7 +207,7 @@ struct Loader<ET, true, kPF8Native> {
     for (int i = 0; i < 8; ++i) {
       const int64_t gr = r0 + (t >> 3) + 32 * i;
       const int64_t gk = k0 + 16 * c;
-      v[i] = (gr < R && gk < K) ? ld16(static_cast<const uint8_t*>(X) + gr * ld + gk)
+      v[i] = (!CHECK || (gr < R && gk < K)) ? ld16(static_cast<const uint8_t*>(X) + gr * ld + gk)
                                 : u32x4{0, 0, 0, 0};
     }
   }
@@ -217,6 +226,7 @@ template <int ET>
 struct Loader<ET, true, kPFP4> {
   u32x4 v[2];
   uint32_t s[2];
+  template <bool CHECK>
   __device__ __forceinline__ void fetch(const void* X, int64_t ld, int64_t R, int64_t K,
                                         int64_t r0, int64_t k0, const uint8_t* sc, int64_t lds_,
                                         int s2d) {
@@ -225,7 +235,7 @@ struct Loader<ET, true, kPFP4> {
     for (int i = 0; i < 2; ++i) {
       const int64_t gr = r0 + (t >> 1) + 128 * i;
       const int64_t gk = k0 + 32 * (t & 1);
-      const bool ok = gr < R && gk < K;
+      const bool ok = !CHECK || (gr < R && gk < K);
       v[i] = ok ? ld16(static_cast<const uint8_t*>(X) + gr * ld + gk / 2) : u32x4{0, 0, 0, 0};
       const int64_t srow = s2d ? gr / 16 : gr;
       s[i] = ok ? *reinterpret_cast<const uint16_t*>(sc + srow * lds_ + gk / 16) : 0u;
@@ -263,7 +273,7 @@ __device__ __forceinline__ void store_c(void* C, int64_t idx, float x) {
   else static_cast<uint16_t*>(C)[idx] = static_cast<uint16_t>(f32_to_f16(x));
 }
 
-template <int AT, int BT, bool A_KC, bool B_KC, int PATH, int CT>
+template <int AT, int BT, bool A_KC, bool B_KC, int PATH, int CT, bool CHECK>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mfma(GemmArgs g) {
   __shared__ __align__(16) uint8_t smem[2][2][kOperandBytes];
   constexpr int BK = PATH == kPF8Native ? 128 : 64;
@@ -299,8 +309,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma(GemmArgs g) {
   const int64_t nk = (g.K + BK - 1) / BK;
 
   if (nk > 0) {
-    la.fetch(g.A, g.lda, g.M, g.K, m0, 0, g.sA, g.ldsA, g.s2dA);
-    lb.fetch(g.B, g.ldb, g.N, g.K, n0, 0, g.sB, g.ldsB, g.s2dB);
+    la.template fetch<CHECK>(g.A, g.lda, g.M, g.K, m0, 0, g.sA, g.ldsA, g.s2dA);
+    lb.template fetch<CHECK>(g.B, g.ldb, g.N, g.K, n0, 0, g.sB, g.ldsB, g.s2dB);
     la.store(smem[0][0]);
     lb.store(smem[0][1]);
     __syncthreads();
@@ -309,8 +319,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma(GemmArgs g) {
   for (int64_t kt = 0; kt < nk; ++kt) {
     const int cur = static_cast<int>(kt & 1);
     if (kt + 1 < nk) {
-      la.fetch(g.A, g.lda, g.M, g.K, m0, (kt + 1) * BK, g.sA, g.ldsA, g.s2dA);
-      lb.fetch(g.B, g.ldb, g.N, g.K, n0, (kt + 1) * BK, g.sB, g.ldsB, g.s2dB);
+      la.template fetch<CHECK>(g.A, g.lda, g.M, g.K, m0, (kt + 1) * BK, g.sA, g.ldsA, g.s2dA);
+      lb.template fetch<CHECK>(g.B, g.ldb, g.N, g.K, n0, (kt + 1) * BK, g.sB, g.ldsB, g.s2dB);
     }
     const uint8_t* sa = smem[cur][0];
     const uint8_t* sb = smem[cur][1];
@@ -345,30 +355,47 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma(GemmArgs g) {
                 af[mb], bfr[nb], acc[mb][nb], fa, fb, 0, 127, 0, 127);
       }
     } else {
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        u32x4 af[4], bfr[4];
+      u32x4 af[2][4], bfr[2][4];
+      auto frag = [&](int ks, u32x4 (&a)[4], u32x4 (&b)[4]) {
         const int ch = 2 * ks + (lane >> 5);
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
-          af[mb] = *reinterpret_cast<const u32x4*>(sa + swz(wm * 128 + mb * 32 + (lane & 31), ch));
+          a[mb] = *reinterpret_cast<const u32x4*>(sa + swz(wm * 128 + mb * 32 + (lane & 31), ch));
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
-          bfr[nb] = *reinterpret_cast<const u32x4*>(sb + swz(wn * 128 + nb * 32 + (lane & 31), ch));
+          b[nb] = *reinterpret_cast<const u32x4*>(sb + swz(wn * 128 + nb * 32 + (lane & 31), ch));
+      };
+      frag(0, af[0], bfr[0]);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        if (ks < 3) frag(ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
           for (int nb = 0; nb < 4; ++nb) {
             if constexpr (PATH == kP16 && AT == AMP_F16)
               acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                  __builtin_bit_cast(f16x8_t, af[mb]), __builtin_bit_cast(f16x8_t, bfr[nb]),
+                  __builtin_bit_cast(f16x8_t, af[ks & 1][mb]), __builtin_bit_cast(f16x8_t, bfr[ks & 1][nb]),
                   acc[mb][nb], 0, 0, 0);
             else
               acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                  __builtin_bit_cast(bf16x8_t, af[mb]), __builtin_bit_cast(bf16x8_t, bfr[nb]),
+                  __builtin_bit_cast(bf16x8_t, af[ks & 1][mb]), __builtin_bit_cast(bf16x8_t, bfr[ks & 1][nb]),
                   acc[mb][nb], 0, 0, 0);
           }
       }
+      // 64 MFMA, 32 DS reads (8 already issued), 16 VMEM loads
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
     }
     if (kt + 1 < nk) {
       la.store(smem[cur ^ 1][0]);
@@ -387,6 +414,157 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma(GemmArgs g) {
       for (int r = 0; r < 16; ++r) {
         const int64_t row = m0 + wm * 128 + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (row < g.M && col < g.N) store_c<CT>(g.C, row * g.ldc + col, acc[mb][nb][r] * alpha);
+      }
+    }
+}
+
+
+// ------------------------------------------------------- direct-to-LDS NT
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Wave w fills rows w*64 .. w*64+63 of a 256-row operand stage, 8 rows
+// (1 KB) per instruction; lane l writes LDS bytes 16*l of those 8 rows, i.e.
+// physical chunk l%8 of row l/8, so it fetches the logical chunk that the
+// swizzle maps there.
+template <int EB>   // element bytes (2: 16-bit, 1: FP8)
+__device__ __forceinline__ void d2l_stage(const void* X, int64_t ld, int64_t r0, int64_t k0,
+                                          uint8_t* stage) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = w * 64 + i * 8 + (lane >> 3);
+    const int p = lane & 7;
+    const int c = p ^ ((r ^ (r >> 3)) & 7);
+    const uint8_t* src = static_cast<const uint8_t*>(X) + ((r0 + r) * ld + k0) * EB + c * 16;
+    __builtin_amdgcn_global_load_lds(src, (lds_void*)(stage + (w * 64 + i * 8) * kRowBytes), 16, 0, 0);
+  }
+}
+
+template <int AT, int BT, int PATH, int CT>
+__global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
+  __shared__ __align__(16) uint8_t smem[2][2][kOperandBytes];
+  constexpr int BK = PATH == kPF8Native ? 128 : 64;
+  constexpr int EB = PATH == kPF8Native ? 1 : 2;
+  const int64_t nbm = g.M / kBM, nbn = g.N / kBN;
+  const int64_t total = nbm * nbn;
+  int64_t tile = blockIdx.x;
+  if (total % 8 == 0) tile = (tile % 8) * (total / 8) + tile / 8;
+  constexpr int64_t kGroup = 8;
+  const int64_t group = tile / (kGroup * nbn);
+  const int64_t first_m = group * kGroup;
+  const int64_t gsz = nbm - first_m < kGroup ? nbm - first_m : kGroup;
+  const int64_t in_group = tile % (kGroup * nbn);
+  const int64_t m0 = (first_m + in_group % gsz) * kBM, n0 = (in_group / gsz) * kBN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  const int64_t nk = g.K / BK;
+  d2l_stage<EB>(g.A, g.lda, m0, 0, smem[0][0]);
+  d2l_stage<EB>(g.B, g.ldb, n0, 0, smem[0][1]);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const int cur = static_cast<int>(kt & 1);
+    {
+      // past the end: reload the last step into the idle stage (never read)
+      const int64_t kn = kt + 1 < nk ? kt + 1 : nk - 1;
+      d2l_stage<EB>(g.A, g.lda, m0, kn * BK, smem[cur ^ 1][0]);
+      d2l_stage<EB>(g.B, g.ldb, n0, kn * BK, smem[cur ^ 1][1]);
+    }
+    const uint8_t* sa = smem[cur][0];
+    const uint8_t* sb = smem[cur][1];
+    if constexpr (PATH == kPF8Native) {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        i32x8 af[4], bfr[4];
+        const int ch = 4 * ks + 2 * (lane >> 5);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+          const int row = wm * 128 + mb * 32 + (lane & 31);
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(sa + swz(row, ch));
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(sa + swz(row, ch + 1));
+          af[mb] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        }
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+          const int row = wn * 128 + nb * 32 + (lane & 31);
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(sb + swz(row, ch));
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(sb + swz(row, ch + 1));
+          bfr[nb] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        }
+        constexpr int fa = AT == AMP_E4M3 ? 0 : 1;
+        constexpr int fb = BT == AMP_E4M3 ? 0 : 1;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb)
+            acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[mb], bfr[nb], acc[mb][nb], fa, fb, 0, 127, 0, 127);
+      }
+      // per K-step: 32 MFMA, 32 LDS reads, 16 direct-to-LDS loads
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+    } else {
+      u32x4 af[2][4], bfr[2][4];
+      auto frag = [&](int ks, u32x4 (&a)[4], u32x4 (&b)[4]) {
+        const int ch = 2 * ks + (lane >> 5);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+          a[mb] = *reinterpret_cast<const u32x4*>(sa + swz(wm * 128 + mb * 32 + (lane & 31), ch));
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          b[nb] = *reinterpret_cast<const u32x4*>(sb + swz(wn * 128 + nb * 32 + (lane & 31), ch));
+      };
+      frag(0, af[0], bfr[0]);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        if (ks < 3) frag(ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 4; ++nb) {
+            if constexpr (AT == AMP_F16)
+              acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, af[ks & 1][mb]), __builtin_bit_cast(f16x8_t, bfr[ks & 1][nb]), acc[mb][nb], 0, 0, 0);
+            else
+              acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[ks & 1][mb]), __builtin_bit_cast(bf16x8_t, bfr[ks & 1][nb]), acc[mb][nb], 0, 0, 0);
+          }
+      }
+      // per K-step: 64 MFMA, 32 LDS reads, 16 direct-to-LDS loads, spread out
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+  const float alpha = (g.alphaA ? *g.alphaA : 1.0f) * (g.alphaB ? *g.alphaB : 1.0f);
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) {
+      const int64_t col = n0 + wn * 128 + nb * 32 + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + wm * 128 + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        store_c<CT>(g.C, row * g.ldc + col, acc[mb][nb][r] * alpha);
       }
     }
 }
@@ -431,16 +609,38 @@ __global__ __launch_bounds__(256) void gemm_generic(GemmArgs g, int a_kc, int b_
 }
 
 // ---------------------------------------------------------------- dispatch
-template <int AT, int BT, bool A_KC, bool B_KC, int PATH>
-hipError_t launch_mfma(const GemmArgs& g, int ct, hipStream_t s) {
+template <int AT, int BT, bool A_KC, bool B_KC, int PATH, bool CHECK>
+hipError_t launch_mfma_c(const GemmArgs& g, int ct, hipStream_t s) {
   const int64_t tiles = ((g.M + kBM - 1) / kBM) * ((g.N + kBN - 1) / kBN);
   const dim3 grid(static_cast<unsigned>(tiles));
   switch (ct) {
-    case AMP_F32: gemm_mfma<AT, BT, A_KC, B_KC, PATH, AMP_F32><<<grid, kThreads, 0, s>>>(g); break;
-    case AMP_BF16: gemm_mfma<AT, BT, A_KC, B_KC, PATH, AMP_BF16><<<grid, kThreads, 0, s>>>(g); break;
-    default: gemm_mfma<AT, BT, A_KC, B_KC, PATH, AMP_F16><<<grid, kThreads, 0, s>>>(g); break;
+    case AMP_F32: gemm_mfma<AT, BT, A_KC, B_KC, PATH, AMP_F32, CHECK><<<grid, kThreads, 0, s>>>(g); break;
+    case AMP_BF16: gemm_mfma<AT, BT, A_KC, B_KC, PATH, AMP_BF16, CHECK><<<grid, kThreads, 0, s>>>(g); break;
+    default: gemm_mfma<AT, BT, A_KC, B_KC, PATH, AMP_F16, CHECK><<<grid, kThreads, 0, s>>>(g); break;
   }
   return hipGetLastError();
+}
+
+// Interior launches (every tile full, K a multiple of the K-step) use the
+// loaders without bounds checks.
+template <int AT, int BT, bool A_KC, bool B_KC, int PATH>
+hipError_t launch_mfma(const GemmArgs& g, int ct, hipStream_t s) {
+  constexpr int64_t BK = PATH == kPF8Native ? 128 : 64;
+  if constexpr (A_KC && B_KC && (PATH == kP16 || PATH == kPF8Native)) {
+    const int eb = PATH == kPF8Native ? 1 : 2;
+    if (g.M % kBM == 0 && g.N % kBN == 0 && g.K % BK == 0 && (g.lda * eb) % 16 == 0 && (g.ldb * eb) % 16 == 0) {
+      const dim3 grid(static_cast<unsigned>((g.M / kBM) * (g.N / kBN)));
+      switch (ct) {
+        case AMP_F32: gemm_mfma_d2l<AT, BT, PATH, AMP_F32><<<grid, kThreads, 0, s>>>(g); break;
+        case AMP_BF16: gemm_mfma_d2l<AT, BT, PATH, AMP_BF16><<<grid, kThreads, 0, s>>>(g); break;
+        default: gemm_mfma_d2l<AT, BT, PATH, AMP_F16><<<grid, kThreads, 0, s>>>(g); break;
+      }
+      return hipGetLastError();
+    }
+  }
+  if (g.M % kBM == 0 && g.N % kBN == 0 && g.K % BK == 0)
+    return launch_mfma_c<AT, BT, A_KC, B_KC, PATH, false>(g, ct, s);
+  return launch_mfma_c<AT, BT, A_KC, B_KC, PATH, true>(g, ct, s);
 }
 
 template <int AT, int BT>

@@ -170,3 +170,27 @@ def test_gemm_bf16_full_size_sampled(name, M, N, K, opA, opB):
     bound = np.sum(np.abs(rows) * np.abs(cols), axis=1)
     ok = OG.check_rounded(out[ii, jj], F.BF16, cref, bound)
     assert ok.all(), np.nonzero(~ok)[0][:5]
+
+
+@pytest.mark.parametrize("et,ct", [(amp.F16, amp.F32), (amp.BF16, amp.F16), (amp.BF16, amp.BF16)])
+def test_gemm_interior_direct_to_lds_path(et, ct):
+    """Full 256x256 tiles, K a multiple of the K-step, K-contiguous operands:
+    the direct-to-LDS kernel."""
+    M, N, K = 512, 768, 320
+    a = codes_16(et, (M, K), 21)
+    b = codes_16(et, (N, K), 22, 0.05)
+    out = run_gemm(amp.OP_N, amp.OP_T, M, N, K, a, et, K, b, et, K, ct, alphaA=2.0)
+    A, B = ref_values(amp.OP_N, amp.OP_T, M, N, K, a, et, b, et)
+    cref, bound = OG.reference(A, B, alpha=2.0)
+    check(out, ct, cref, bound, "d2l")
+
+
+@pytest.mark.parametrize("fa,fb", [(amp.E4M3, amp.E4M3), (amp.E5M2, amp.E4M3)])
+def test_gemm_fp8_exact_interior(fa, fb):
+    M, N, K = 256, 512, 512
+    a, b, ia, ib = fp8_operands(31, M, N, K, fa, fb)
+    out = run_gemm(amp.OP_N, amp.OP_T, M, N, K, a, fa, K, b, fb, K, amp.F32, alphaA=ia, alphaB=ib)
+    A, B = ref_values(amp.OP_N, amp.OP_T, M, N, K, a, fa, b, fb)
+    alpha = float(np.float32(np.float32(ia) * np.float32(ib)))
+    cref, bound = OG.reference(A, B, alpha=alpha)
+    check(out, amp.F32, cref, bound, "fp8 exact interior")

@@ -94,10 +94,17 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, HI));
 }
 
-// Two E2M1 codes (byte SEL of w) times the scale S -> two BF16 (exact).
+// Two E2M1 codes (byte SEL of w) times the block scale S -> two BF16.  The
+// hardware conversion runs at scale 1 (exact); the product with the E4M3
+// scale is formed in FP32, where it is exact (at most 6 significant bits,
+// range 2^-10 .. 2688), and truncation to BF16 is therefore exact too.  (The
+// conversion's own scale operand is not used: it only carries a power of two.)
 template <int SEL>
 __device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w, float S) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, S, SEL));
+  const uint32_t p = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, SEL));
+  const float lo = bitsf(p << 16) * S;
+  const float hi = bitsf(p & 0xffff0000u) * S;
+  return (fbits(lo) >> 16) | (fbits(hi) & 0xffff0000u);
 }
 
 // ---------------------------------------------------------------- loaders

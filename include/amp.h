@@ -263,6 +263,36 @@ int amp_nvfp4_quantize(const void* x, int xt, int64_t rows, int64_t cols, int64_
                        int rnd, uint64_t sr_seed, uint8_t* q, uint8_t* scales,
                        float* d_tensor, void* stream);
 
+/* ---- FP16 AMP training step of a two-layer MLP: the element-wise glue ----
+ * Page "혼합 정밀도 학습" (itwiki), section "FP16 학습 루프": Linear(512, 2048)
+ * -> GELU -> Linear(2048, 10) under FP16 autocast with cross-entropy in FP32
+ * and the backward pass started from S * loss; marovi "Operaciones que
+ * permanecen en FP32" (softmax / cross-entropy in FP32).  FP16 tensors are
+ * passed as raw 16-bit codes (void*).  The GEMMs of the step are amp_gemm
+ * calls; these kernels cover what sits between them. */
+
+/* z = round16(fl32(acc + b)) and, if a16 != NULL, a = round16(gelu(z)) with
+ * the exact-erf GELU evaluated in FP32.  acc: [rows, cols] FP32 (contiguous);
+ * b16: [cols] FP16 or NULL; z16, a16: [rows, cols] FP16. */
+int amp_bias_gelu_f16(const float* acc, int64_t rows, int64_t cols, const void* b16,
+                      void* z16, void* a16, void* stream);
+
+/* Cross-entropy of FP16 logits [rows, cols] (contiguous) against int32
+ * labels in [0, cols): *d_loss = mean over rows, in FP32 (NULL: not written);
+ * dlogits16 = round16(S * (softmax - onehot) / rows) with S read from
+ * d_state->scale (d_state NULL: S = 1; dlogits16 NULL: not written).
+ * Runs as one work-group (meant for classifier heads, rows <= 65536). */
+int amp_softmax_xent_f16(const void* logits16, const int32_t* labels, int64_t rows,
+                         int64_t cols, const amp_scaler_state* d_state, float* d_loss,
+                         void* dlogits16, void* stream);
+
+/* dz = round16(fl32(dA * fl32(gelu'(z)))), element-wise over n FP16 values. */
+int amp_gelu_backward_f16(const void* dA16, const void* z16, int64_t n, void* dz16,
+                          void* stream);
+
+/* out[c] = round16(fl32(sum_r x[r][c])) (sequential FP32 sum; bias grads). */
+int amp_colsum_f16(const void* x16, int64_t rows, int64_t cols, void* out16, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -22,7 +22,8 @@ __all__ = [
     "lib_path", "load", "amp_abi_version", "amp_status_string", "amp_last_hip_error",
     "amp_cast", "amp_gemm", "amp_gemm_ex", "amp_scaler_init", "amp_optimizer_step", "amp_check_overflow",
     "amp_scaler_update", "amp_fp8_meta_init", "amp_delayed_scaling_update",
-    "amp_nvfp4_quantize",
+    "amp_nvfp4_quantize", "amp_bias_gelu_f16", "amp_softmax_xent_f16", "amp_gelu_backward_f16",
+    "amp_colsum_f16",
 ]
 
 F32, F16, BF16, E4M3, E5M2, E2M1X2 = 0, 1, 2, 3, 4, 5
@@ -89,6 +90,10 @@ _SIGS = {
     "amp_delayed_scaling_update": ([_P, _P, ctypes.c_int32, _P, _P], _I),
     "amp_nvfp4_quantize": ([_P, _I, _I64, _I64, _I64, _I, _I, _I, _U64, _I, _U64, _P, _P, _P,
                             _P], _I),
+    "amp_bias_gelu_f16": ([_P, _I64, _I64, _P, _P, _P, _P], _I),
+    "amp_softmax_xent_f16": ([_P, _P, _I64, _I64, _P, _P, _P, _P], _I),
+    "amp_gelu_backward_f16": ([_P, _P, _I64, _P, _P], _I),
+    "amp_colsum_f16": ([_P, _I64, _I64, _P, _P], _I),
 }
 
 _lib = None
@@ -212,3 +217,24 @@ def amp_nvfp4_quantize(x, xt, rows, cols, ldx, transpose, block2d, rht, rht_seed
     _check("amp_nvfp4_quantize", load().amp_nvfp4_quantize(
         _ptr(x), xt, rows, cols, ldx, int(transpose), int(block2d), int(rht), rht_seed, rnd,
         sr_seed, _ptr(q), _ptr(scales), _ptr(d_tensor), _stream(stream)))
+
+
+def amp_bias_gelu_f16(acc, rows, cols, b16, z16, a16=None, stream=None):
+    _check("amp_bias_gelu_f16", load().amp_bias_gelu_f16(_ptr(acc), rows, cols, _ptr(b16), _ptr(z16),
+                                                         _ptr(a16), _stream(stream)))
+
+
+def amp_softmax_xent_f16(logits16, labels, rows, cols, d_state, d_loss, dlogits16, stream=None):
+    _check("amp_softmax_xent_f16", load().amp_softmax_xent_f16(
+        _ptr(logits16), _ptr(labels), rows, cols, _ptr(d_state), _ptr(d_loss), _ptr(dlogits16),
+        _stream(stream)))
+
+
+def amp_gelu_backward_f16(dA16, z16, n, dz16, stream=None):
+    _check("amp_gelu_backward_f16", load().amp_gelu_backward_f16(_ptr(dA16), _ptr(z16), n,
+                                                                 _ptr(dz16), _stream(stream)))
+
+
+def amp_colsum_f16(x16, rows, cols, out16, stream=None):
+    _check("amp_colsum_f16", load().amp_colsum_f16(_ptr(x16), rows, cols, _ptr(out16),
+                                                   _stream(stream)))

@@ -221,4 +221,41 @@ int amp_nvfp4_quantize(const void* x, int xt, int64_t rows, int64_t cols, int64_
                                                static_cast<hipStream_t>(stream)));
 }
 
+int amp_bias_gelu_f16(const float* acc, int64_t rows, int64_t cols, const void* b16, void* z16,
+                      void* a16, void* stream) {
+  if (rows < 0 || cols < 0) return AMP_EINVAL;
+  if (rows == 0 || cols == 0) return AMP_OK;
+  if (!acc || !z16) return AMP_EINVAL;
+  if (int st = check_device()) return st;
+  return hip_status(amp::launch_bias_gelu(acc, rows, cols, b16, z16, a16,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int amp_softmax_xent_f16(const void* logits16, const int32_t* labels, int64_t rows, int64_t cols,
+                         const amp_scaler_state* d_state, float* d_loss, void* dlogits16,
+                         void* stream) {
+  if (rows < 0 || cols <= 0 || rows > 65536) return AMP_EINVAL;
+  if (rows == 0) return AMP_OK;
+  if (!logits16 || !labels) return AMP_EINVAL;
+  if (int st = check_device()) return st;
+  return hip_status(amp::launch_softmax_xent(logits16, labels, rows, cols, d_state, d_loss,
+                                             dlogits16, static_cast<hipStream_t>(stream)));
+}
+
+int amp_gelu_backward_f16(const void* dA16, const void* z16, int64_t n, void* dz16, void* stream) {
+  if (n < 0) return AMP_EINVAL;
+  if (n == 0) return AMP_OK;
+  if (!dA16 || !z16 || !dz16) return AMP_EINVAL;
+  if (int st = check_device()) return st;
+  return hip_status(amp::launch_gelu_backward(dA16, z16, n, dz16, static_cast<hipStream_t>(stream)));
+}
+
+int amp_colsum_f16(const void* x16, int64_t rows, int64_t cols, void* out16, void* stream) {
+  if (rows < 0 || cols < 0) return AMP_EINVAL;
+  if (cols == 0) return AMP_OK;
+  if (!out16 || (rows > 0 && !x16)) return AMP_EINVAL;
+  if (int st = check_device()) return st;
+  return hip_status(amp::launch_colsum(x16, rows, cols, out16, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -84,4 +84,13 @@ hipError_t launch_nvfp4_quantize(const void* x, int xt, int64_t rows, int64_t co
                                  uint64_t rht_seed, int rnd, uint64_t sr_seed, uint8_t* q,
                                  uint8_t* scales, float* d_tensor, hipStream_t s);
 
+hipError_t launch_bias_gelu(const float* acc, int64_t rows, int64_t cols, const void* b16,
+                            void* z16, void* a16, hipStream_t s);
+hipError_t launch_softmax_xent(const void* logits16, const int32_t* labels, int64_t rows,
+                               int64_t cols, const amp_scaler_state* st, float* loss,
+                               void* dlog16, hipStream_t s);
+hipError_t launch_gelu_backward(const void* dA16, const void* z16, int64_t n, void* dz16,
+                                hipStream_t s);
+hipError_t launch_colsum(const void* x16, int64_t rows, int64_t cols, void* out16, hipStream_t s);
+
 }  // namespace amp

@@ -21,7 +21,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = [
+__all__ = ["mlp_init", "mlp_batch",
     "rng", "normal_f32", "student_t_f32", "to_bf16_codes", "to_f16_codes",
     "f32_bits", "bf16_codes_normal", "outlier_bf16_codes", "edge_f32_values",
     "injection_schedule",
@@ -95,3 +95,25 @@ def injection_schedule(seed: int, n_steps: int = 200, n_inject: int = 4,
     vals = [np.inf, np.nan, -np.inf, np.nan]
     return [(int(s), int(g.integers(0, n_params)), vals[k % 4])
             for k, s in enumerate(steps)]
+
+
+MLP_SHAPES = (("W1", (2048, 512), 512), ("b1", (2048,), 512), ("W2", (10, 2048), 2048),
+              ("b2", (10,), 2048))
+
+
+def mlp_init(seed: int = 0) -> np.ndarray:
+    """Flat FP32 parameters [W1, b1, W2, b2] of Linear(512,2048) + Linear(2048,10),
+    each drawn U(-1/sqrt(fan_in), 1/sqrt(fan_in)) (the nn.Linear default)."""
+    g = rng(seed)
+    parts = []
+    for _, shp, fan_in in MLP_SHAPES:
+        bnd = 1.0 / np.sqrt(fan_in)
+        parts.append(g.uniform(-bnd, bnd, size=shp).astype(np.float32).ravel())
+    return np.concatenate(parts)
+
+
+def mlp_batch(t: int, batch: int = 64, d_in: int = 512, classes: int = 10):
+    """Batch t: x ~ N(0,1) FP32 [batch, d_in], labels uniform in 0..classes-1."""
+    x = normal_f32(1000 + t, (batch, d_in))
+    y = rng(2000 + t).integers(0, classes, size=batch).astype(np.int32)
+    return x, y

@@ -8,19 +8,12 @@ import synth
 
 
 def _init(seed=0):
-    g = synth.rng(seed)
-    parts = []
-    for name, shp in M.SHAPES:
-        fan_in = M.D_IN if name in ("W1", "b1") else M.D_H
-        bnd = 1.0 / np.sqrt(fan_in)
-        parts.append(g.uniform(-bnd, bnd, size=shp).astype(np.float32).ravel())
-    return np.concatenate(parts).astype(np.float64)
+    return synth.mlp_init(seed).astype(np.float64)
 
 
 def _batch(t):
-    x = synth.normal_f32(1000 + t, (M.BATCH, M.D_IN)).astype(np.float64)
-    y = synth.rng(2000 + t).integers(0, M.D_OUT, size=M.BATCH)
-    return x, y
+    x, y = synth.mlp_batch(t)
+    return x.astype(np.float64), y
 
 
 def test_param_count():

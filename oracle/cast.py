@@ -35,6 +35,9 @@ def widen_to_f32_bits(codes, in_fmt: F.Fmt) -> np.ndarray:
     codes = np.asarray(codes)
     if in_fmt is F.F32:
         return codes.astype(np.uint32)
+    if in_fmt is F.BF16:
+        # BF16 is the upper half of the FP32 bit layout (1/8/7 vs 1/8/23)
+        return codes.astype(np.uint32) << np.uint32(16)
     v = F.decode(codes, in_fmt)
     return F.encode_exact(v, F.F32)
 

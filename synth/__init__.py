@@ -117,3 +117,38 @@ def mlp_batch(t: int, batch: int = 64, d_in: int = 512, classes: int = 10):
     x = normal_f32(1000 + t, (batch, d_in))
     y = rng(2000 + t).integers(0, classes, size=batch).astype(np.int32)
     return x, y
+
+
+# ---- device-side generators (PyTorch RNG on the GPU; input making only) ----
+
+def torch_student_t(gen, shape, device="cuda"):
+    """Student-t with 3 degrees of freedom: N0 / sqrt((N1^2 + N2^2 + N3^2) / 3)."""
+    import torch
+    z = torch.randn((4,) + tuple(shape), generator=gen, device=device)
+    return z[0] / torch.sqrt((z[1] ** 2 + z[2] ** 2 + z[3] ** 2) / 3.0)
+
+
+def adam_grads_f16(gen, n, loss_scale, device="cuda"):
+    """FP16 gradients round16(S * 1e-4 * N(0,1) * exp(2 Z)) (PyTorch's RNE
+    conversion; values beyond the FP16 range become inf, as a real overflow)."""
+    import torch
+    out = torch.empty(n, device=device, dtype=torch.float16)
+    chunk = 1 << 26
+    for o in range(0, n, chunk):
+        k = min(chunk, n - o)
+        z = torch.randn(k, generator=gen, device=device)
+        g = torch.randn(k, generator=gen, device=device) * 1e-4 * torch.exp(2.0 * z)
+        out[o:o + k] = (g * loss_scale).half()
+    return out
+
+
+def nvfp4_operand(seed, rows, k):
+    """Synthetic NVFP4 operand: random E2M1 codes, E4M3 block scales in
+    [2^-6, 2^6] and a tensor scale (for GEMM tests independent of a quantizer)."""
+    g = rng(seed)
+    q = g.integers(0, 256, size=(rows, k // 2), dtype=np.uint8)
+    e = g.integers(1, 13, size=(rows, k // 16))            # exponent field 1..12
+    m = g.integers(0, 8, size=(rows, k // 16))
+    sc = ((e << 3) | m).astype(np.uint8)
+    enc = float(np.float32(g.uniform(1.0, 100.0)))
+    return q, sc, enc

@@ -13,8 +13,10 @@ Also measured in the same run (reported under "components"):
   * the BF16 and FP8 (delayed-scaling, E4M3 fwd / E5M2 bwd) GEMMs of one
     transformer block's linear layers at hidden 4096, FFN 14336, 8192 tokens
     (fwd, dgrad, wgrad of QKV, O, up/gate, down: 10.72 TFLOP per block step);
-  * the NVFP4 weight-gradient GEMM 20480 x 5120 x 16384 and its quantizer;
-  * the scaled casts (BF16 -> E4M3 flat, BF16 -> E5M2 with transposed copy).
+  * the NVFP4 weight-gradient GEMM 20480 x 5120 x 16384 and its two
+    quantizer calls (RHT on both operands, stochastic rounding on dY);
+  * the scaled casts (BF16 -> E4M3 flat 2^31, BF16 -> E5M2 [8192 x 28672]
+    with its transposed copy).
 The CPU oracle is timed on a bounded sample of the optimizer workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-components]
@@ -35,6 +37,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 FP8_PEAK_TFLOPS = 5000.0
+FP4_PEAK_TFLOPS = 10100.0
 N_PARAMS = 1 << 31
 BYTES_PER_PARAM = 28
 
@@ -235,6 +238,112 @@ def cast_workload(torch, amp):
             "frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def _timed(torch, f, reps):
+    f()
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(reps):
+        f()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / reps
+
+
+def cast_t_workload(torch, amp):
+    """BF16 -> E5M2 of an FFN output gradient [8192 x 28672] with its
+    transposed copy (the dgrad and wgrad operands) and amax: 4 B/elem."""
+    R, C = 8192, 28672
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    x = torch.randn(R, C, device="cuda", generator=gen).to(torch.bfloat16)
+    y = torch.empty(R * C, device="cuda", dtype=torch.uint8)
+    yt = torch.empty(R * C, device="cuda", dtype=torch.uint8)
+    sc = torch.ones(1, device="cuda")
+    am = torch.zeros(1, device="cuda")
+    ms = _timed(torch, lambda: amp.amp_cast(x, amp.BF16, R, C, C, y, amp.E5M2, C, yt, R, sc, am),
+                5)
+    del x, y, yt
+    torch.cuda.empty_cache()
+    gbs = 4 * R * C / ms / 1e6
+    return {"what": "BF16->E5M2 [8192 x 28672] + transposed copy + amax", "ms": round(ms, 4),
+            "gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def nvfp4_workload(torch, amp):
+    """NVFP4 weight-gradient step of a 12B-style FFN up projection (hidden
+    5120, FFN 20480, 16384 tokens): quantize dY^T (RHT + stochastic rounding)
+    and X^T (RHT, round to nearest) along the token axis, then
+    dW[20480 x 5120] = dY^T X in BF16."""
+    T, I, O = 16384, 5120, 20480
+    dev = "cuda"
+    gen = torch.Generator(device=dev).manual_seed(7)
+
+    def outliers(rows, cols):
+        x = torch.randn(rows, cols, device=dev, generator=gen)
+        hit = torch.rand(rows, cols, device=dev, generator=gen) < 1e-3
+        sgn = torch.where(torch.rand(rows, cols, device=dev, generator=gen) < 0.5, -50.0, 50.0)
+        return torch.where(hit, sgn, x).to(torch.bfloat16)
+
+    dY = outliers(T, O)
+    X = outliers(T, I)
+    qa = torch.empty(O * T // 2, device=dev, dtype=torch.uint8)
+    sa = torch.empty(O * T // 16, device=dev, dtype=torch.uint8)
+    qb = torch.empty(I * T // 2, device=dev, dtype=torch.uint8)
+    sb = torch.empty(I * T // 16, device=dev, dtype=torch.uint8)
+    ta = torch.empty(3, device=dev)
+    tb = torch.empty(3, device=dev)
+    dW = torch.empty(O, I, device=dev, dtype=torch.bfloat16)
+
+    def quant():
+        amp.amp_nvfp4_quantize(dY, amp.BF16, T, O, O, 1, 0, 1, 11, amp.ROUND_SR, 12, qa, sa, ta)
+        amp.amp_nvfp4_quantize(X, amp.BF16, T, I, I, 1, 0, 1, 11, amp.ROUND_RNE, 0, qb, sb, tb)
+
+    def gemm():
+        amp.amp_gemm(amp.OP_N, amp.OP_T, O, I, T, qa, amp.E2M1X2, T // 2, ta.data_ptr() + 8,
+                     qb, amp.E2M1X2, T // 2, tb.data_ptr() + 8, dW, amp.BF16, I,
+                     amp.BlockScales(sa.data_ptr(), T // 16, 0, 0),
+                     amp.BlockScales(sb.data_ptr(), T // 16, 0, 0))
+
+    q_ms = _timed(torch, quant, 5)
+    g_ms = _timed(torch, gemm, 5)
+    del dY, X, qa, sa, qb, sb, dW
+    torch.cuda.empty_cache()
+    flops = 2 * O * I * T
+    tf = flops / g_ms / 1e9
+    # quantizer traffic: amax pass reads BF16, encode pass reads BF16 and
+    # writes 0.5 B of codes + 1/16 B of scales per element
+    qbytes = (T * O + T * I) * (2 + 2 + 0.5 + 1.0 / 16)
+    return {"gemm_ms": round(g_ms, 4), "gemm_tflops": round(tf, 1),
+            "peak_tflops_fp4": FP4_PEAK_TFLOPS, "frac_fp4": round(tf / FP4_PEAK_TFLOPS, 4),
+            "frac_bf16_mfma": round(tf / BF16_PEAK_TFLOPS, 4),
+            "mfma": "bf16 (E2M1 x E4M3 decoded exactly to BF16)",
+            "quantize_ms": round(q_ms, 4), "quantize_gbs": round(qbytes / q_ms / 1e6, 1),
+            "tflop_per_step": round(flops / 1e12, 3)}
+
+
+def measured_traffic():
+    """HBM bytes per launch of the apply kernel, from the committed rocprofv3
+    counter summary, or None when the kernel sources changed since then."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", "apply_kernel_adamw_2pow31_hbm_bytes.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_bytes = re.search(r"traffic_bytes_per_launch: (\d+)", text)
+    m_sha = re.search(r"source_sha256_16: (\w+)", text)
+    m_src = re.search(r"sources: (.*)", text)
+    if not (m_bytes and m_sha and m_src):
+        return None
+    h = hashlib.sha256()
+    for rel in m_src.group(1).split(", "):
+        h.update(open(os.path.join(ROOT, rel.strip()), "rb").read())
+    if h.hexdigest()[:16] != m_sha.group(1):
+        return None
+    return int(m_bytes.group(1))
+
+
 def cpu_baseline(sample: int = 1 << 20, steps: int = 12):
     """The oracle's optimizer step (as it stands) on a bounded sample."""
     import numpy as np
@@ -290,6 +399,11 @@ def main():
         comps["gemm_fp8_block"] = gemm_block_workload(torch, amp, fp8=True)
         log("components: cast")
         comps["cast"] = cast_workload(torch, amp)
+        log("components: cast with transposed copy")
+        comps["cast_t"] = cast_t_workload(torch, amp)
+        log("components: NVFP4 weight-gradient quantize + GEMM")
+        comps["nvfp4_wgrad"] = nvfp4_workload(torch, amp)
+    traffic = measured_traffic()
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
@@ -313,7 +427,11 @@ def main():
                    "n_params": N_PARAMS, "grad_dtype": "f16", "bytes_per_param": BYTES_PER_PARAM},
         "roofline": {"bound": "hbm", "kernel": "apply_kernel (fused AdamW pass)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic is None else round(traffic / 1e9, 3),
+                     "traffic_unit": "GB per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                     "copy-calibrated)",
+                     "algorithmic": round(BYTES_PER_PARAM * N_PARAMS / 1e9, 3)},
         "components": comps,
         "cpu_baseline": cpu,
     }

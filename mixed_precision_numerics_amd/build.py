@@ -32,6 +32,13 @@ DEVICE = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
 ]
 
+# Per-file additions.  The quantizer's register-resident cells are indexed by
+# fully unrolled loops; the default unroll budget stops short on the
+# stochastic-rounding variants and leaves the cell in scratch memory.
+PER_FILE = {
+    "nvfp4.hip": ["-mllvm", "-pragma-unroll-threshold=1000000"],
+}
+
 
 def hipcc() -> str:
     return shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -39,9 +46,10 @@ def hipcc() -> str:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), "-c", src, "-o", obj] + COMMON + DEVICE
+    extra = PER_FILE.get(os.path.basename(src), [])
+    cmd = [hipcc(), "-c", src, "-o", obj] + COMMON + DEVICE + extra
     if src.endswith(".cpp"):
-        cmd = [hipcc(), "-x", "hip", "-c", src, "-o", obj] + COMMON + DEVICE
+        cmd = [hipcc(), "-x", "hip", "-c", src, "-o", obj] + COMMON + DEVICE + extra
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

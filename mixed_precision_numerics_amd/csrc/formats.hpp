@@ -103,27 +103,38 @@ __device__ __forceinline__ float e5m2_to_f32(uint32_t c) {
 
 // ---- E2M1 (FP4) -----------------------------------------------------------
 // Magnitude codes 0..7 = {0, 0.5, 1, 1.5, 2, 3, 4, 6}; bit 3 is the sign.
+// From [1, 8) up the E2M1 grid is the FP32 grid cut to one fraction bit, so
+// code = (FP32 bits >> 22) - 252 there; below 1 the spacing is 0.5.
 __device__ __forceinline__ uint32_t e2m1_rne(float y) {
   const float a = fabsf(y);
-  // each threshold is a midpoint; '>' where the lower neighbour has the even
-  // code, '>=' where the upper one has it
-  uint32_t c = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) +
-               (a > 2.5f) + (a >= 3.5f) + (a > 5.0f);
+  const uint32_t b = fbits(a);
+  // a >= 1: round the significand to one fraction bit, ties to even; 7 and up
+  // (the tie 7 goes to 8) saturate to 6
+  uint32_t cn = ((b + 0x1fffffu + ((b >> 22) & 1u)) >> 22) - 252u;
+  cn = cn > 7u ? 7u : cn;
+  // a < 1: midpoints 0.25 (tie to 0) and 0.75 (tie to 1)
+  const uint32_t cs = static_cast<uint32_t>(a > 0.25f) + static_cast<uint32_t>(a >= 0.75f);
+  uint32_t c = b >= 0x3f800000u ? cn : cs;
+  c = b > 0x7f800000u ? 0u : c;             // NaN -> 0 (E2M1 has no NaN)
   return c | ((fbits(y) >> 28) & 0x8u);
 }
 
-// Stochastic rounding with u in [0, 1): round the magnitude up iff u < frac.
+// Stochastic rounding with u in [0, 1): round the magnitude up iff u < frac,
+// frac = (|y| - lower neighbour) / gap, exact.  Above 1 the lower neighbour is
+// the FP32 value cut to one fraction bit and frac is the remaining 22 bits.
 __device__ __forceinline__ uint32_t e2m1_sr(float y, float u) {
   const float a = fminf(fabsf(y), 6.0f);
-  const uint32_t lo = (a >= 0.5f) + (a >= 1.0f) + (a >= 1.5f) + (a >= 2.0f) +
-                      (a >= 3.0f) + (a >= 4.0f) + (a >= 6.0f);
-  // lower neighbour value and gap to the upper one
-  const float lov = lo < 4 ? 0.5f * static_cast<float>(lo)
-                           : (lo == 4 ? 2.0f : (lo == 5 ? 3.0f : (lo == 6 ? 4.0f : 6.0f)));
-  const float inv_gap = lo < 4 ? 2.0f : (lo < 6 ? 1.0f : 0.5f);
-  const float frac = (a - lov) * inv_gap;   // exact (Sterbenz, power-of-two gap)
-  const uint32_t up = (lo < 7) && (u < frac);
-  return (lo + up) | ((fbits(y) >> 28) & 0x8u);
+  const uint32_t b = fbits(a);
+  const uint32_t lo_n = (b >> 22) - 252u;
+  const float frac_n = static_cast<float>(b & 0x3fffffu) * 2.384185791015625e-7f;   // 2^-22
+  const uint32_t lo_s = a >= 0.5f;
+  const float frac_s = (a - (lo_s ? 0.5f : 0.0f)) * 2.0f;
+  const bool nrm = b >= 0x3f800000u;
+  const uint32_t lo = nrm ? lo_n : lo_s;
+  const float frac = nrm ? frac_n : frac_s;
+  const uint32_t up = static_cast<uint32_t>(lo < 7u) & static_cast<uint32_t>(u < frac);
+  const uint32_t c = (fbits(y) & 0x7fffffffu) > 0x7f800000u ? 0u : lo + up;   // NaN -> 0
+  return c | ((fbits(y) >> 28) & 0x8u);
 }
 
 __device__ __forceinline__ float e2m1_to_f32(uint32_t c) {

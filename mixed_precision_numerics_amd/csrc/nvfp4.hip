@@ -236,9 +236,272 @@ __global__ __launch_bounds__(kT) void nvfp4_kernel(const void* __restrict__ x, i
   }
 }
 
+// ---------------------------------------------------------------------------
+// Vector path (16-byte aligned rows).  No LDS staging: a lane owns a "cell"
+// of CW op rows x one 16-chunk along K, fetched with sixteen 16-byte loads
+// (CW = 8 for BF16, 4 for FP32), and runs the RHT, the block amax and the
+// encoding in registers, one op row at a time.
+//   transposed operand (x rows are K): lane = cg + 8*kc -> op rows CW*cg..,
+//     chunk kc; one load instruction reads 8 x rows x 128 contiguous bytes.
+//   plain operand (x rows are op rows): lane = rg + G*kc (G = 16/CW) -> op
+//     rows CW*rg.., chunk kc; consecutive lanes walk along K.
+// In both, the CW-row groups of one 16-row block are G adjacent lanes, so a
+// 16x16 block amax is a G-lane xor-shuffle reduction.  A wave tile is
+// TILE_R op rows x TILE_K; a row of a tile writes 128 (transposed) or 256
+// (plain) contiguous code bytes.
+template <int XT, bool TRANS>
+struct VecGeom {
+  static constexpr int kESize = XT == AMP_BF16 ? 2 : 4;
+  static constexpr int kCW = 16 / kESize;          // op rows per lane
+  static constexpr int kG = 16 / kCW;              // lanes per 16-row block
+  static constexpr int kLR = TRANS ? 8 : kG;       // lanes across op rows
+  static constexpr int kLK = kWave / kLR;          // lanes across K
+  static constexpr int kTileR = kLR * kCW;
+  static constexpr int kSubK = 16 * kLK;
+  static constexpr int kNSub = TRANS ? 2 : 1;
+  static constexpr int kTileK = kSubK * kNSub;
+};
+
+template <int XT, bool TRANS>
+__device__ __forceinline__ void load_cell(const uint8_t* __restrict__ xb, int64_t ldb, int64_t gr,
+                                          int64_t gk, bool valid, u32x4 (&raw)[16]) {
+  using Gm = VecGeom<XT, TRANS>;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) raw[j] = u32x4{0u, 0u, 0u, 0u};
+  if (!valid) return;
+  if constexpr (TRANS) {
+    const uint8_t* p = xb + gk * ldb + gr * Gm::kESize;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) raw[j] = *reinterpret_cast<const u32x4*>(p + j * ldb);
+  } else {
+    const uint8_t* p = xb + gr * ldb + gk * Gm::kESize;
+    constexpr int kPerRow = Gm::kESize;            // 16 elements = kESize x 16 bytes
+#pragma unroll
+    for (int i = 0; i < Gm::kCW; ++i)
+#pragma unroll
+      for (int h = 0; h < kPerRow; ++h)
+        raw[i * kPerRow + h] = *reinterpret_cast<const u32x4*>(p + i * ldb + 16 * h);
+  }
+}
+
+// Element (op row i of the cell, K offset j of the chunk).
+template <int XT, bool TRANS>
+__device__ __forceinline__ float cell_elem(const u32x4 (&raw)[16], int i, int j) {
+  if constexpr (TRANS) {
+    if constexpr (XT == AMP_BF16) {
+      const uint32_t w = raw[j][i >> 1];
+      return bitsf((i & 1) ? (w & 0xffff0000u) : (w << 16));
+    } else {
+      return bitsf(raw[j][i]);
+    }
+  } else {
+    if constexpr (XT == AMP_BF16) {
+      const uint32_t w = raw[2 * i + (j >> 3)][(j & 7) >> 1];
+      return bitsf((j & 1) ? (w & 0xffff0000u) : (w << 16));
+    } else {
+      return bitsf(raw[4 * i + (j >> 2)][j & 3]);
+    }
+  }
+}
+
+template <int XT, bool TRANS, bool RHT>
+__device__ __forceinline__ uint32_t row_chunk(const u32x4 (&raw)[16], int i, uint32_t sign_bits,
+                                              float (&z)[16]) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) z[j] = cell_elem<XT, TRANS>(raw, i, j);
+  if constexpr (RHT) rht16(z, sign_bits);
+  uint32_t bmax = 0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    const uint32_t a = fbits(z[j]) & 0x7fffffffu;
+    bmax = bmax > a ? bmax : a;
+  }
+  return bmax;
+}
+
+// Philox4x32-10 on the four counters blk0 .. blk0+3 (high words from blk),
+// side by side: the rounds stay rolled so only the current round key is live,
+// and the four independent chains fill the multiplier's latency.
+__device__ __forceinline__ void philox_x4(uint64_t blk0, uint64_t seed, uint32_t (&w)[16]) {
+  uint32_t x[4], y[4], z[4], v[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const uint64_t blk = blk0 + q;
+    x[q] = static_cast<uint32_t>(blk);
+    y[q] = static_cast<uint32_t>(blk >> 32);
+    z[q] = 0u;
+    v[q] = 0u;
+  }
+  uint32_t k0 = static_cast<uint32_t>(seed), k1 = static_cast<uint32_t>(seed >> 32);
+#pragma unroll 1
+  for (int r = 0; r < 10; ++r) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint64_t p0 = static_cast<uint64_t>(0xD2511F53u) * x[q];
+      const uint64_t p1 = static_cast<uint64_t>(0xCD9E8D57u) * z[q];
+      x[q] = static_cast<uint32_t>(p1 >> 32) ^ y[q] ^ k0;
+      y[q] = static_cast<uint32_t>(p1);
+      z[q] = static_cast<uint32_t>(p0 >> 32) ^ v[q] ^ k1;
+      v[q] = static_cast<uint32_t>(p0);
+    }
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    w[4 * q] = x[q];
+    w[4 * q + 1] = y[q];
+    w[4 * q + 2] = z[q];
+    w[4 * q + 3] = v[q];
+  }
+}
+
+template <bool SR>
+__device__ __forceinline__ u32x2 encode_chunk(const float (&z)[16], float mult, bool live,
+                                              uint64_t idx0, uint64_t sr_seed) {
+  uint32_t codes[16];
+  if constexpr (SR) {
+    // word (idx & 3) of the Philox block idx >> 2, idx = idx0 + j
+    uint32_t w[16];
+    philox_x4(idx0 >> 2, sr_seed, w);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float u = static_cast<float>(w[j] >> 8) * 5.9604644775390625e-8f;
+      codes[j] = e2m1_sr(z[j] * mult, u);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 16; ++j) codes[j] = e2m1_rne(z[j] * mult);
+  }
+  uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    w0 |= codes[j] << (4 * j);
+    w1 |= codes[8 + j] << (4 * j);
+  }
+  return live ? u32x2{w0, w1} : u32x2{0u, 0u};
+}
+
+// PASS2 = false: tensor amax only.
+template <int XT, bool TRANS, bool PASS2, bool BLOCK2D, bool RHT, bool SR>
+__global__ __launch_bounds__(kT) void nvfp4_vec_kernel(
+    const uint8_t* __restrict__ xb, int64_t ldb, int64_t R, int64_t K, int64_t tiles_r,
+    int64_t tiles_k, uint64_t rht_seed, uint64_t sr_seed, uint8_t* __restrict__ q,
+    uint8_t* __restrict__ scales, float* __restrict__ d_tensor) {
+  using Gm = VecGeom<XT, TRANS>;
+  __shared__ uint32_t red[kT / kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int lr = lane % Gm::kLR;
+  const int lk = lane / Gm::kLR;
+  const uint32_t sign_bits = RHT ? rht_signs(rht_seed) : 0u;
+  const float enc = PASS2 ? d_tensor[1] : 1.0f;
+  const int64_t ntiles = tiles_r * tiles_k;
+  const int64_t wstride = static_cast<int64_t>(gridDim.x) * (kT / kWave);
+  uint32_t am = 0;
+  for (int64_t w = static_cast<int64_t>(blockIdx.x) * (kT / kWave) + threadIdx.x / kWave;
+       w < ntiles; w += wstride) {
+    // neighbouring waves read neighbouring bytes of the same x rows
+    const int64_t tr = TRANS ? w % tiles_r : w / tiles_k;
+    const int64_t tk = TRANS ? w / tiles_r : w % tiles_k;
+    const int64_t gr = tr * Gm::kTileR + Gm::kCW * lr;
+#pragma unroll
+    for (int sub = 0; sub < Gm::kNSub; ++sub) {
+      const int64_t gk = tk * Gm::kTileK + sub * Gm::kSubK + 16 * lk;
+      const bool valid = gr < R && gk < K;
+      u32x4 raw[16];
+      load_cell<XT, TRANS>(xb, ldb, gr, gk, valid, raw);
+      if constexpr (!PASS2) {
+#pragma unroll
+        for (int i = 0; i < Gm::kCW; ++i) {
+          float z[16];
+          const uint32_t b = row_chunk<XT, TRANS, RHT>(raw, i, sign_bits, z);
+          am = am > b ? am : b;
+        }
+      } else if constexpr (BLOCK2D) {
+        // block amax over the CW rows here and the G-1 neighbouring lanes,
+        // then a second RHT per row for the encoding
+        uint32_t bmax = 0;
+#pragma unroll
+        for (int i = 0; i < Gm::kCW; ++i) {
+          float z[16];
+          const uint32_t b = row_chunk<XT, TRANS, RHT>(raw, i, sign_bits, z);
+          bmax = bmax > b ? bmax : b;
+        }
+#pragma unroll
+        for (int off = 1; off < Gm::kG; off <<= 1) {
+          const uint32_t o = static_cast<uint32_t>(__shfl_xor(static_cast<int>(bmax), off, kWave));
+          bmax = bmax > o ? bmax : o;
+        }
+        const uint32_t scode = f32_to_e4m3((bitsf(bmax) / 6.0f) * enc);
+        const float S = e4m3_to_f32(scode);
+        const bool live = S > 0.0f;
+        const float mult = live ? enc / S : 0.0f;
+#pragma unroll
+        for (int i = 0; i < Gm::kCW; ++i) {
+          float z[16];
+          (void)row_chunk<XT, TRANS, RHT>(raw, i, sign_bits, z);
+          const uint64_t idx0 = static_cast<uint64_t>(gr + i) * static_cast<uint64_t>(K) +
+                                static_cast<uint64_t>(gk);
+          const u32x2 cw = encode_chunk<SR>(z, mult, live, idx0, sr_seed);
+          if (valid) *reinterpret_cast<u32x2*>(q + (gr + i) * (K / 2) + gk / 2) = cw;
+        }
+        if (valid && (lr % Gm::kG) == 0)
+          scales[(gr / 16) * (K / 16) + gk / 16] = static_cast<uint8_t>(scode);
+      } else {
+#pragma unroll
+        for (int i = 0; i < Gm::kCW; ++i) {
+          float z[16];
+          const uint32_t bmax = row_chunk<XT, TRANS, RHT>(raw, i, sign_bits, z);
+          const uint32_t scode = f32_to_e4m3((bitsf(bmax) / 6.0f) * enc);
+          const float S = e4m3_to_f32(scode);
+          const bool live = S > 0.0f;
+          const float mult = live ? enc / S : 0.0f;
+          const uint64_t idx0 = static_cast<uint64_t>(gr + i) * static_cast<uint64_t>(K) +
+                                static_cast<uint64_t>(gk);
+          const u32x2 cw = encode_chunk<SR>(z, mult, live, idx0, sr_seed);
+          if (valid) {
+            *reinterpret_cast<u32x2*>(q + (gr + i) * (K / 2) + gk / 2) = cw;
+            scales[(gr + i) * (K / 16) + gk / 16] = static_cast<uint8_t>(scode);
+          }
+        }
+      }
+    }
+  }
+  if constexpr (!PASS2) {
+    am = block_max_u32<kT>(am, red);
+    if (threadIdx.x == 0 && am != 0)
+      atomicMax(reinterpret_cast<unsigned int*>(d_tensor), canon_amax(am));
+  }
+}
+
+template <int XT, bool TRANS, bool BLOCK2D, bool RHT, bool SR>
+hipError_t run_vec(const void* x, int64_t ldx, int64_t R, int64_t K, uint64_t rs, uint64_t ss,
+                   uint8_t* q, uint8_t* sc, float* dt, hipStream_t s) {
+  using Gm = VecGeom<XT, TRANS>;
+  const int64_t tiles_r = (R + Gm::kTileR - 1) / Gm::kTileR;
+  const int64_t tiles_k = (K + Gm::kTileK - 1) / Gm::kTileK;
+  const int64_t waves = tiles_r * tiles_k;
+  int64_t blocks = (waves + kT / kWave - 1) / (kT / kWave);
+  if (blocks > 2048) blocks = 2048;
+  const uint8_t* xb = static_cast<const uint8_t*>(x);
+  const int64_t ldb = ldx * Gm::kESize;
+  zero_amax<<<1, 64, 0, s>>>(dt);
+  nvfp4_vec_kernel<XT, TRANS, false, BLOCK2D, RHT, SR><<<static_cast<unsigned>(blocks), kT, 0, s>>>(
+      xb, ldb, R, K, tiles_r, tiles_k, rs, ss, q, sc, dt);
+  finalize_enc<<<1, 64, 0, s>>>(dt);
+  nvfp4_vec_kernel<XT, TRANS, true, BLOCK2D, RHT, SR><<<static_cast<unsigned>(blocks), kT, 0, s>>>(
+      xb, ldb, R, K, tiles_r, tiles_k, rs, ss, q, sc, dt);
+  return hipGetLastError();
+}
+
 template <int XT, bool TRANS, bool BLOCK2D, bool RHT, bool SR>
 hipError_t run(const void* x, int64_t ldx, int64_t R, int64_t K, uint64_t rs, uint64_t ss,
                uint8_t* q, uint8_t* sc, float* dt, hipStream_t s) {
+  // 16-byte vector loads need 16-byte aligned rows; codes are stored 8 bytes
+  // at a time
+  const int64_t esize = XT == AMP_BF16 ? 2 : 4;
+  if (aligned(x, 16) && (ldx * esize) % 16 == 0 && aligned(q, 8))
+    return run_vec<XT, TRANS, BLOCK2D, RHT, SR>(x, ldx, R, K, rs, ss, q, sc, dt, s);
   const dim3 grid(static_cast<unsigned>((K + kK - 1) / kK), static_cast<unsigned>((R + kRows - 1) / kRows));
   zero_amax<<<1, 64, 0, s>>>(dt);
   nvfp4_kernel<XT, TRANS, false, BLOCK2D, RHT, SR><<<grid, kT, 0, s>>>(x, ldx, R, K, rs, ss, q, sc, dt);

@@ -109,3 +109,48 @@ def test_nvfp4_decode_every_code_and_scale_via_identity():
                  amp.BlockScales(sb_d.data_ptr(), K // 16, 0, 0))
     want = F.decode(a_codes, F.E2M1) * np.repeat(F.decode(sa, F.E4M3), 16, axis=1)
     assert np.array_equal(host(c, np.float32).reshape(M, K).astype(np.float64), want)
+
+
+@pytest.mark.parametrize("xt", ["bf16", "f32"])
+@pytest.mark.parametrize("transpose", [False, True])
+@pytest.mark.parametrize("unaligned", [False, True])
+@pytest.mark.parametrize("opts", [(False, True, True), (True, True, False), (False, False, False)])
+def test_nvfp4_layouts_and_strides(xt, transpose, unaligned, opts):
+    """Both load paths: 16-byte aligned rows (vector cells) and rows that
+    start off a 16-byte boundary (the LDS-staged path), in BF16 and FP32, with
+    a padded leading dimension; ragged against every tile shape."""
+    block2d, rht, sr = opts
+    rows, cols = 112, 304
+    ldx = cols + (1 if unaligned else 8)
+    seed = 300 + 16 * transpose + 8 * unaligned + 2 * (xt == "f32") + block2d + 4 * rht
+    xc = synth.outlier_bf16_codes(seed, (rows, cols))
+    x = F.decode(xc, F.BF16)
+    if xt == "f32":
+        x = x * 1.001                      # values off the BF16 grid
+        x32 = x.astype(np.float32)
+        x = x32.astype(np.float64)
+        buf = np.zeros((rows, ldx), dtype=np.uint32)
+        buf[:, :cols] = synth.f32_bits(x32)
+        esize, code = 4, amp.F32
+    else:
+        buf = np.zeros((rows, ldx), dtype=np.uint16)
+        buf[:, :cols] = xc
+        esize, code = 2, amp.BF16
+    flat = np.concatenate([np.zeros(1, dtype=buf.dtype), buf.reshape(-1)])
+    xd = dev(flat)
+    ptr = xd.data_ptr() + esize            # one element in: 16-byte aligned only via ldx
+    if not unaligned:
+        xd = dev(buf.reshape(-1))
+        ptr = xd.data_ptr()
+    R, K = (cols, rows) if transpose else (rows, cols)
+    q = empty(R * K // 2, fill=0xEE)
+    nsc = (R // 16 if block2d else R) * (K // 16)
+    s = empty(nsc, fill=0xEE)
+    ts = empty(12)
+    amp.amp_nvfp4_quantize(ptr, code, rows, cols, ldx, transpose, block2d, rht, 91,
+                           amp.ROUND_SR if sr else amp.ROUND_RNE, 0xC0FFEE, q, s, ts)
+    wq, ws, enc = ON.quantize(x, transpose=transpose, block2d=block2d, rht=rht, rht_seed=91,
+                              sr=sr, sr_seed=0xC0FFEE)
+    assert host(ts, np.float32)[1] == np.float32(enc)
+    assert np.array_equal(host(s, np.uint8)[:nsc], ws.reshape(-1))
+    assert np.array_equal(host(q, np.uint8).reshape(R, K // 2), wq)

@@ -31,6 +31,8 @@
 //    registers with byte permutes before the LDS store.
 // Tiles are ordered so that each XCD (own L2) works on a contiguous range of
 // tiles, grouped 8 tile-rows at a time for L2 reuse.
+#include <type_traits>
+
 #include "common.hpp"
 #include "formats.hpp"
 
@@ -429,29 +431,100 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma(GemmArgs g) {
 // ------------------------------------------------------- direct-to-LDS NT
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Wave w fills rows w*64 .. w*64+63 of a 256-row operand stage, 8 rows
-// (1 KB) per instruction; lane l writes LDS bytes 16*l of those 8 rows, i.e.
+// Wave w fills rows w*64 .. w*64+63 of a 256-row operand stage, 8 rows (1 KB)
+// per buffer load; lane l writes LDS bytes 16*l of those 8 rows, i.e.
 // physical chunk l%8 of row l/8, so it fetches the logical chunk that the
-// swizzle maps there.
-template <int EB>   // element bytes (2: 16-bit, 1: FP8)
-__device__ __forceinline__ void d2l_stage(const void* X, int64_t ld, int64_t r0, int64_t k0,
+// swizzle maps there: p ^ (l/8) ^ i for the i-th load.  The buffer resource
+// starts at the tile's first row; koff is the K-step's byte offset.
+__device__ __forceinline__ void d2l_stage(__amdgpu_buffer_rsrc_t rsrc, uint32_t ldb, uint32_t koff,
                                           uint8_t* stage) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint32_t vrow = static_cast<uint32_t>(w * 64 + lane / 8) * ldb;
+  const uint32_t x = static_cast<uint32_t>(((lane & 7) ^ (lane >> 3)) & 7) << 4;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = w * 64 + i * 8 + (lane >> 3);
-    const int p = lane & 7;
-    const int c = p ^ ((r ^ (r >> 3)) & 7);
-    const uint8_t* src = static_cast<const uint8_t*>(X) + ((r0 + r) * ld + k0) * EB + c * 16;
-    __builtin_amdgcn_global_load_lds(src, (lds_void*)(stage + (w * 64 + i * 8) * kRowBytes), 16, 0, 0);
+  for (int i = 0; i < 8; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(stage + (w * 64 + i * 8) * kRowBytes),
+                                             16, vrow + (x ^ static_cast<uint32_t>(i << 4)),
+                                             koff + static_cast<uint32_t>(8 * i) * ldb, 0, 0);
+}
+
+// M/N-contiguous 16-bit operand (rows of the global matrix are K): an LDS
+// stage holds the step's 64 K-rows of the tile's 256 columns, 512 bytes per
+// row, with 16-byte chunk c of K-row k stored at chunk c ^ 4*(k%4).  Wave w
+// loads K-rows 16w .. 16w+15, two rows (1 KB) per buffer load: lane l writes
+// physical chunk l%32 of row l/32.  rsrc starts at the step's first K-row.
+__device__ __forceinline__ void d2l_stage_mn(__amdgpu_buffer_rsrc_t rsrc, uint32_t ldb,
+                                             uint8_t* stage) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int hr = lane >> 5;
+  const uint32_t v0 = static_cast<uint32_t>(hr) * ldb;
+  // row%4 = 2*(i&1) + hr
+  const uint32_t ve = v0 + (static_cast<uint32_t>((lane & 31) ^ (4 * hr)) << 4);
+  const uint32_t vo = v0 + (static_cast<uint32_t>((lane & 31) ^ (4 * (2 + hr))) << 4);
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(stage + (w * 16 + 2 * i) * 512), 16,
+                                             (i & 1) ? vo : ve,
+                                             static_cast<uint32_t>(w * 16 + 2 * i) * ldb, 0, 0);
+}
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// MFMA 32x32x16 operand fragment (lane l: row l%32 of the 32-block, K
+// 8*(l/32) .. +7) from an M/N-contiguous stage with two transposing 64-bit
+// reads.  ds_read_b64_tr_b16 hands lane i of a 16-lane group element i%4 of
+// the 64 bits read by lane 4j + i/4, j = 0..3; so source lane s of group q
+// reads the 4 columns 16*(q%2) + 4*(s%4) .. +3 of K-row 8*(q/2) + s/4 (+4 for
+// the second read) and every lane receives its own column's 4 K values.
+// addr: this lane's byte address for (32-block, K-slice 0, first read);
+// slice ks adds 16*ks rows, the second read 4 rows.
+__device__ __forceinline__ u32x4 frag_tr(const uint8_t* stage, uint32_t addr, int ks) {
+  const uint8_t* p = stage + addr + ks * 16 * 512;
+  const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4i16*)((__attribute__((address_space(3))) uint8_t*)(__attribute__((address_space(3))) void*)p));
+  const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_v4i16*)((__attribute__((address_space(3))) uint8_t*)(__attribute__((address_space(3))) void*)(p + 4 * 512)));
+  const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+  return u32x4{l2[0], l2[1], h2[0], h2[1]};
+}
+
+// Per-lane byte address of the first transposing read of 32-block b (0..3) of
+// a wave's 128 columns starting at column c0 (a multiple of 128): K-row
+// k = 8*(q/2) + s/4 and column m = c0 + 32b + 16*(q%2) + 4*(s%4), chunk
+// m/8 swizzled by 4*(k%4) = 4*(s/4).
+__device__ __forceinline__ uint32_t tr_addr(int lane, int c0, int b) {
+  const int q = lane >> 4, s = lane & 15;
+  const int k = 8 * (q >> 1) + (s >> 2);
+  const int chunk = (c0 >> 3) + 4 * (b ^ (s >> 2)) + 2 * (q & 1) + ((s & 3) >> 1);
+  return static_cast<uint32_t>(k * 512 + chunk * 16 + 8 * (s & 1));
+}
+
+// Scheduling hint for one K-slice: 16 MFMA, each followed by its share of
+// the R fragment reads of the next slice.
+template <int I, int R>
+__device__ __forceinline__ void sched_slice() {
+  if constexpr (I < 16) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    constexpr int n = (I + 1) * R / 16 - I * R / 16;
+    if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x100, n, 0);
+    sched_slice<I + 1, R>();
   }
 }
 
-template <int AT, int BT, int PATH, int CT>
+// Every tile full; 16-bit operands may be K- or M/N-contiguous (FP8 ones are
+// K-contiguous).  Per K-step: the loads of the
+// next step go straight to the idle LDS stage; the fragments of slice s+1 are
+// read while slice s runs on the matrix cores; the block-wide barrier sits in
+// the last slice, after its fragments are in registers, so the last slice's
+// MFMAs overlap the first fragment reads of the next step.
+template <int AT, int BT, bool A_KC, bool B_KC, int PATH, int CT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
+  static_assert((A_KC && B_KC) || PATH == kP16, "M/N-contiguous operands are 16-bit");
   __shared__ __align__(16) uint8_t smem[2][2][kOperandBytes];
   constexpr int BK = PATH == kPF8Native ? 128 : 64;
   constexpr int EB = PATH == kPF8Native ? 1 : 2;
+  constexpr int NS = PATH == kPF8Native ? 2 : 4;          // MFMA K-slices per step
   const int64_t nbm = g.M / kBM, nbn = g.N / kBN;
   const int64_t total = nbm * nbn;
   int64_t tile = blockIdx.x;
@@ -472,95 +545,124 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   const int64_t nk = g.K / BK;
-  d2l_stage<EB>(g.A, g.lda, m0, 0, smem[0][0]);
-  d2l_stage<EB>(g.B, g.ldb, n0, 0, smem[0][1]);
+  const uint32_t lda_b = static_cast<uint32_t>(g.lda * EB), ldb_b = static_cast<uint32_t>(g.ldb * EB);
+  const uint8_t* gA = static_cast<const uint8_t*>(g.A);
+  const uint8_t* gB = static_cast<const uint8_t*>(g.B);
+  // K-contiguous: the resource covers the tile's 256 rows for every step
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(gA + m0 * g.lda * EB), 0, static_cast<int>(kBM * lda_b), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(gB + n0 * g.ldb * EB), 0, static_cast<int>(kBN * ldb_b), 0x00020000);
+  // past the end a step reloads the last one into the idle stage (never read)
+  auto load_step = [&](int64_t kt) {
+    const int64_t kc = kt < nk ? kt : nk - 1;
+    const uint32_t koff = static_cast<uint32_t>(kc * kRowBytes);
+    if constexpr (A_KC) {
+      d2l_stage(ra, lda_b, koff, smem[kt & 1][0]);
+    } else {
+      // M-contiguous: the step's 64 K-rows, columns m0 .. m0+255
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(gA + (kc * BK * g.lda + m0) * EB), 0, static_cast<int>(BK * lda_b), 0x00020000);
+      d2l_stage_mn(r, lda_b, smem[kt & 1][0]);
+    }
+    if constexpr (B_KC) {
+      d2l_stage(rb, ldb_b, koff, smem[kt & 1][1]);
+    } else {
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(gB + (kc * BK * g.ldb + n0) * EB), 0, static_cast<int>(BK * ldb_b), 0x00020000);
+      d2l_stage_mn(r, ldb_b, smem[kt & 1][1]);
+    }
+  };
+  // Fragment rows wm*128 + mb*32 + l%32 (A) and wn*128 + nb*32 + l%32 (B).
+  // Their swizzle term is g ^ 4*(mb & 1) with g = (l%8) ^ (l%32 / 8), so the
+  // LDS address is base + 32*mb rows + ((y ^ c) << 4) with a per-lane y and
+  // a compile-time c.
+  const int l32 = lane & 31, h = lane >> 5;
+  const uint32_t gsw = static_cast<uint32_t>((l32 & 7) ^ (l32 >> 3));
+  const uint32_t abase = static_cast<uint32_t>(wm * 128 + l32) * kRowBytes;
+  const uint32_t bbase = static_cast<uint32_t>(wn * 128 + l32) * kRowBytes;
+  using Frag = typename std::conditional<PATH == kPF8Native, i32x8, u32x4>::type;
+  Frag fa[2][4], fb[2][4];
+  uint32_t tra[4], trb[4];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    tra[b] = tr_addr(lane, wm * 128, b);
+    trb[b] = tr_addr(lane, wn * 128, b);
+  }
+  auto frag = [&](const uint8_t* st, int ks, Frag (&a)[4], Frag (&b)[4]) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+      if constexpr (PATH == kPF8Native) {
+        // 32 bytes of K per lane: logical chunks 4ks + 2h and 4ks + 2h + 1
+        const uint32_t y = (static_cast<uint32_t>(2 * h) ^ gsw) & 7u;
+        const uint32_t c0 = static_cast<uint32_t>(4 * ks) ^ static_cast<uint32_t>(4 * (mb & 1));
+        const uint8_t* pa = st + abase + mb * 32 * kRowBytes;
+        const uint8_t* pb = st + kOperandBytes + bbase + mb * 32 * kRowBytes;
+        const u32x4 al = *reinterpret_cast<const u32x4*>(pa + ((y ^ c0) << 4));
+        const u32x4 ah = *reinterpret_cast<const u32x4*>(pa + ((y ^ (c0 + 1)) << 4));
+        const u32x4 bl = *reinterpret_cast<const u32x4*>(pb + ((y ^ c0) << 4));
+        const u32x4 bh = *reinterpret_cast<const u32x4*>(pb + ((y ^ (c0 + 1)) << 4));
+        a[mb] = i32x8{(int)al[0], (int)al[1], (int)al[2], (int)al[3], (int)ah[0], (int)ah[1], (int)ah[2], (int)ah[3]};
+        b[mb] = i32x8{(int)bl[0], (int)bl[1], (int)bl[2], (int)bl[3], (int)bh[0], (int)bh[1], (int)bh[2], (int)bh[3]};
+      } else {
+        // 16 bytes of K per lane: logical chunk 2ks + h
+        const uint32_t y = (static_cast<uint32_t>(h) ^ gsw) & 7u;
+        const uint32_t c = static_cast<uint32_t>(2 * ks) ^ static_cast<uint32_t>(4 * (mb & 1));
+        if constexpr (A_KC)
+          a[mb] = *reinterpret_cast<const u32x4*>(st + abase + mb * 32 * kRowBytes + ((y ^ c) << 4));
+        else
+          a[mb] = frag_tr(st, tra[mb], ks);
+        if constexpr (B_KC)
+          b[mb] = *reinterpret_cast<const u32x4*>(st + kOperandBytes + bbase + mb * 32 * kRowBytes +
+                                                  ((y ^ c) << 4));
+        else
+          b[mb] = frag_tr(st + kOperandBytes, trb[mb], ks);
+      }
+    }
+  };
+  load_step(0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  frag(smem[0][0], 0, fa[0], fb[0]);
   for (int64_t kt = 0; kt < nk; ++kt) {
-    const int cur = static_cast<int>(kt & 1);
-    {
-      // past the end: reload the last step into the idle stage (never read)
-      const int64_t kn = kt + 1 < nk ? kt + 1 : nk - 1;
-      d2l_stage<EB>(g.A, g.lda, m0, kn * BK, smem[cur ^ 1][0]);
-      d2l_stage<EB>(g.B, g.ldb, n0, kn * BK, smem[cur ^ 1][1]);
-    }
-    const uint8_t* sa = smem[cur][0];
-    const uint8_t* sb = smem[cur][1];
-    if constexpr (PATH == kPF8Native) {
+    const uint8_t* st = smem[kt & 1][0];
+    load_step(kt + 1);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        i32x8 af[4], bfr[4];
-        const int ch = 4 * ks + 2 * (lane >> 5);
+    for (int ks = 0; ks < NS; ++ks) {
+      const int cur = ks & 1;
+      if (ks + 1 < NS) {
+        frag(st, ks + 1, fa[cur ^ 1], fb[cur ^ 1]);
+      } else {
+        // this step's fragments are all in registers and the next step has
+        // landed: after the barrier its stage may be read and this one refilled
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __syncthreads();
+        frag(smem[(kt + 1) & 1][0], 0, fa[cur ^ 1], fb[cur ^ 1]);
+      }
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb) {
-          const int row = wm * 128 + mb * 32 + (lane & 31);
-          const u32x4 lo = *reinterpret_cast<const u32x4*>(sa + swz(row, ch));
-          const u32x4 hi = *reinterpret_cast<const u32x4*>(sa + swz(row, ch + 1));
-          af[mb] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        }
+      for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
-          const int row = wn * 128 + nb * 32 + (lane & 31);
-          const u32x4 lo = *reinterpret_cast<const u32x4*>(sb + swz(row, ch));
-          const u32x4 hi = *reinterpret_cast<const u32x4*>(sb + swz(row, ch + 1));
-          bfr[nb] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        }
-        constexpr int fa = AT == AMP_E4M3 ? 0 : 1;
-        constexpr int fb = BT == AMP_E4M3 ? 0 : 1;
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < 4; ++nb)
-            acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[mb], bfr[nb], acc[mb][nb], fa, fb, 0, 127, 0, 127);
-      }
-      // per K-step: 32 MFMA, 32 LDS reads, 16 direct-to-LDS loads
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-    } else {
-      u32x4 af[2][4], bfr[2][4];
-      auto frag = [&](int ks, u32x4 (&a)[4], u32x4 (&b)[4]) {
-        const int ch = 2 * ks + (lane >> 5);
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-          a[mb] = *reinterpret_cast<const u32x4*>(sa + swz(wm * 128 + mb * 32 + (lane & 31), ch));
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          b[nb] = *reinterpret_cast<const u32x4*>(sb + swz(wn * 128 + nb * 32 + (lane & 31), ch));
-      };
-      frag(0, af[0], bfr[0]);
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        if (ks < 3) frag(ks + 1, af[(ks + 1) & 1], bfr[(ks + 1) & 1]);
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int nb = 0; nb < 4; ++nb) {
-            if constexpr (AT == AMP_F16)
-              acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, af[ks & 1][mb]), __builtin_bit_cast(f16x8_t, bfr[ks & 1][nb]), acc[mb][nb], 0, 0, 0);
-            else
-              acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, af[ks & 1][mb]), __builtin_bit_cast(bf16x8_t, bfr[ks & 1][nb]), acc[mb][nb], 0, 0, 0);
+          if constexpr (PATH == kPF8Native) {
+            constexpr int fa_ = AT == AMP_E4M3 ? 0 : 1;
+            constexpr int fb_ = BT == AMP_E4M3 ? 0 : 1;
+            acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[cur][mb], fb[cur][nb], acc[mb][nb],
+                                                                          fa_, fb_, 0, 127, 0, 127);
+          } else if constexpr (AT == AMP_F16) {
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, fa[cur][mb]),
+                                                                 __builtin_bit_cast(f16x8_t, fb[cur][nb]),
+                                                                 acc[mb][nb], 0, 0, 0);
+          } else {
+            acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, fa[cur][mb]),
+                                                                  __builtin_bit_cast(bf16x8_t, fb[cur][nb]),
+                                                                  acc[mb][nb], 0, 0, 0);
           }
-      }
-      // per K-step: 64 MFMA, 32 LDS reads, 16 direct-to-LDS loads, spread out
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      }
+        }
+      // 16 MFMA per slice with the next slice's fragment reads spread evenly
+      // (8 reads; 16 for FP8; two per transposed fragment)
+      constexpr int kReads = PATH == kPF8Native ? 16 : (A_KC ? 4 : 8) + (B_KC ? 4 : 8);
+      sched_slice<0, kReads>();
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
   }
   const float alpha = (g.alphaA ? *g.alphaA : 1.0f) * (g.alphaB ? *g.alphaB : 1.0f);
 #pragma unroll
@@ -633,14 +735,20 @@ hipError_t launch_mfma_c(const GemmArgs& g, int ct, hipStream_t s) {
 template <int AT, int BT, bool A_KC, bool B_KC, int PATH>
 hipError_t launch_mfma(const GemmArgs& g, int ct, hipStream_t s) {
   constexpr int64_t BK = PATH == kPF8Native ? 128 : 64;
-  if constexpr (A_KC && B_KC && (PATH == kP16 || PATH == kPF8Native)) {
+  if constexpr ((A_KC && B_KC && (PATH == kP16 || PATH == kPF8Native)) || PATH == kP16) {
     const int eb = PATH == kPF8Native ? 1 : 2;
-    if (g.M % kBM == 0 && g.N % kBN == 0 && g.K % BK == 0 && (g.lda * eb) % 16 == 0 && (g.ldb * eb) % 16 == 0) {
+    // buffer offsets are 32-bit: a 256-row (K-contiguous) or 64-K-row (M/N-
+    // contiguous) window of either operand must span < 2 GiB; M/N-contiguous
+    // rows hold 256-column windows at 16-byte boundaries
+    const int64_t wa = g.lda * eb * (A_KC ? kBM : BK), wb = g.ldb * eb * (B_KC ? kBN : BK);
+    const bool small = wa < (int64_t(1) << 31) && wb < (int64_t(1) << 31);
+    if (g.M % kBM == 0 && g.N % kBN == 0 && g.K % BK == 0 && (g.lda * eb) % 16 == 0 &&
+        (g.ldb * eb) % 16 == 0 && small) {
       const dim3 grid(static_cast<unsigned>((g.M / kBM) * (g.N / kBN)));
       switch (ct) {
-        case AMP_F32: gemm_mfma_d2l<AT, BT, PATH, AMP_F32><<<grid, kThreads, 0, s>>>(g); break;
-        case AMP_BF16: gemm_mfma_d2l<AT, BT, PATH, AMP_BF16><<<grid, kThreads, 0, s>>>(g); break;
-        default: gemm_mfma_d2l<AT, BT, PATH, AMP_F16><<<grid, kThreads, 0, s>>>(g); break;
+        case AMP_F32: gemm_mfma_d2l<AT, BT, A_KC, B_KC, PATH, AMP_F32><<<grid, kThreads, 0, s>>>(g); break;
+        case AMP_BF16: gemm_mfma_d2l<AT, BT, A_KC, B_KC, PATH, AMP_BF16><<<grid, kThreads, 0, s>>>(g); break;
+        default: gemm_mfma_d2l<AT, BT, A_KC, B_KC, PATH, AMP_F16><<<grid, kThreads, 0, s>>>(g); break;
       }
       return hipGetLastError();
     }

@@ -173,14 +173,21 @@ def test_gemm_bf16_full_size_sampled(name, M, N, K, opA, opB):
 
 
 @pytest.mark.parametrize("et,ct", [(amp.F16, amp.F32), (amp.BF16, amp.F16), (amp.BF16, amp.BF16)])
-def test_gemm_interior_direct_to_lds_path(et, ct):
-    """Full 256x256 tiles, K a multiple of the K-step, K-contiguous operands:
-    the direct-to-LDS kernel."""
+@pytest.mark.parametrize("opA,opB", [(amp.OP_N, amp.OP_T), (amp.OP_N, amp.OP_N),
+                                     (amp.OP_T, amp.OP_N), (amp.OP_T, amp.OP_T)])
+def test_gemm_interior_direct_to_lds_path(et, ct, opA, opB):
+    """Full 256x256 tiles and K a multiple of the K-step: the direct-to-LDS
+    kernel, with K-contiguous operands read as 16-byte rows and M/N-
+    contiguous ones through transposing LDS reads; padded leading dimensions."""
     M, N, K = 512, 768, 320
-    a = codes_16(et, (M, K), 21)
-    b = codes_16(et, (N, K), 22, 0.05)
-    out = run_gemm(amp.OP_N, amp.OP_T, M, N, K, a, et, K, b, et, K, ct, alphaA=2.0)
-    A, B = ref_values(amp.OP_N, amp.OP_T, M, N, K, a, et, b, et)
+    a_shape = (M, K) if opA == amp.OP_N else (K, M)
+    b_shape = (K, N) if opB == amp.OP_N else (N, K)
+    pad = 8
+    a = codes_16(et, (a_shape[0], a_shape[1] + pad), 21 + opA)
+    b = codes_16(et, (b_shape[0], b_shape[1] + pad), 22 + opB, 0.05)
+    out = run_gemm(opA, opB, M, N, K, a, et, a_shape[1] + pad, b, et, b_shape[1] + pad, ct,
+                   alphaA=2.0)
+    A, B = ref_values(opA, opB, M, N, K, a[:, :a_shape[1]], et, b[:, :b_shape[1]], et)
     cref, bound = OG.reference(A, B, alpha=2.0)
     check(out, ct, cref, bound, "d2l")
 

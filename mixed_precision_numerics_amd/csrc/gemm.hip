@@ -501,14 +501,17 @@ __device__ __forceinline__ uint32_t tr_addr(int lane, int c0, int b) {
 }
 
 // Scheduling hint for one K-slice: 16 MFMA, each followed by its share of
-// the R fragment reads of the next slice.
-template <int I, int R>
+// the R fragment reads of the next slice and of the V global loads issued in
+// this slice.
+template <int I, int R, int V>
 __device__ __forceinline__ void sched_slice() {
   if constexpr (I < 16) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
     constexpr int n = (I + 1) * R / 16 - I * R / 16;
     if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x100, n, 0);
-    sched_slice<I + 1, R>();
+    constexpr int v = (I + 1) * V / 16 - I * V / 16;
+    if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x020, v, 0);
+    sched_slice<I + 1, R, V>();
   }
 }
 
@@ -553,24 +556,28 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
       const_cast<uint8_t*>(gA + m0 * g.lda * EB), 0, static_cast<int>(kBM * lda_b), 0x00020000);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint8_t*>(gB + n0 * g.ldb * EB), 0, static_cast<int>(kBN * ldb_b), 0x00020000);
-  // past the end a step reloads the last one into the idle stage (never read)
-  auto load_step = [&](int64_t kt) {
+  // past the end a step reloads the last one into the idle stage (never
+  // read); operand 0 (A) and 1 (B) are fetched in different K-slices
+  auto load_part = [&](int64_t kt, int which) {
     const int64_t kc = kt < nk ? kt : nk - 1;
     const uint32_t koff = static_cast<uint32_t>(kc * kRowBytes);
-    if constexpr (A_KC) {
-      d2l_stage(ra, lda_b, koff, smem[kt & 1][0]);
+    if (which == 0) {
+      if constexpr (A_KC) {
+        d2l_stage(ra, lda_b, koff, smem[kt & 1][0]);
+      } else {
+        // M-contiguous: the step's 64 K-rows, columns m0 .. m0+255
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(gA + (kc * BK * g.lda + m0) * EB), 0, static_cast<int>(BK * lda_b), 0x00020000);
+        d2l_stage_mn(r, lda_b, smem[kt & 1][0]);
+      }
     } else {
-      // M-contiguous: the step's 64 K-rows, columns m0 .. m0+255
-      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint8_t*>(gA + (kc * BK * g.lda + m0) * EB), 0, static_cast<int>(BK * lda_b), 0x00020000);
-      d2l_stage_mn(r, lda_b, smem[kt & 1][0]);
-    }
-    if constexpr (B_KC) {
-      d2l_stage(rb, ldb_b, koff, smem[kt & 1][1]);
-    } else {
-      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint8_t*>(gB + (kc * BK * g.ldb + n0) * EB), 0, static_cast<int>(BK * ldb_b), 0x00020000);
-      d2l_stage_mn(r, ldb_b, smem[kt & 1][1]);
+      if constexpr (B_KC) {
+        d2l_stage(rb, ldb_b, koff, smem[kt & 1][1]);
+      } else {
+        const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(gB + (kc * BK * g.ldb + n0) * EB), 0, static_cast<int>(BK * ldb_b), 0x00020000);
+        d2l_stage_mn(r, ldb_b, smem[kt & 1][1]);
+      }
     }
   };
   // Fragment rows wm*128 + mb*32 + l%32 (A) and wn*128 + nb*32 + l%32 (B).
@@ -620,16 +627,24 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
       }
     }
   };
-  load_step(0);
+  load_part(0, 0);
+  load_part(0, 1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   frag(smem[0][0], 0, fa[0], fb[0]);
   for (int64_t kt = 0; kt < nk; ++kt) {
     const uint8_t* st = smem[kt & 1][0];
-    load_step(kt + 1);
 #pragma unroll
     for (int ks = 0; ks < NS; ++ks) {
       const int cur = ks & 1;
+      // K-contiguous operands: A's loads in slice 0 and B's in slice 1, spread
+      // among the MFMAs; with transposed operands both at the start of the step
+      constexpr bool kSplit = A_KC && B_KC;
+      if (kSplit && ks < 2) load_part(kt + 1, ks);
+      if (!kSplit && ks == 0) {
+        load_part(kt + 1, 0);
+        load_part(kt + 1, 1);
+      }
       if (ks + 1 < NS) {
         frag(st, ks + 1, fa[cur ^ 1], fb[cur ^ 1]);
       } else {
@@ -661,7 +676,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
       // 16 MFMA per slice with the next slice's fragment reads spread evenly
       // (8 reads; 16 for FP8; two per transposed fragment)
       constexpr int kReads = PATH == kPF8Native ? 16 : (A_KC ? 4 : 8) + (B_KC ? 4 : 8);
-      sched_slice<0, kReads>();
+      if (kSplit && ks < 2) sched_slice<0, kReads, 8>();
+      else sched_slice<0, kReads, 0>();
     }
   }
   const float alpha = (g.alphaA ? *g.alphaA : 1.0f) * (g.alphaB ? *g.alphaB : 1.0f);

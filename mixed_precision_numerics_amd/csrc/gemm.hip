@@ -525,9 +525,12 @@ template <int AT, int BT, bool A_KC, bool B_KC, int PATH, int CT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
   static_assert((A_KC && B_KC) || PATH == kP16, "M/N-contiguous operands are 16-bit");
   __shared__ __align__(16) uint8_t smem[2][2][kOperandBytes];
-  constexpr int BK = PATH == kPF8Native ? 128 : 64;
-  constexpr int EB = PATH == kPF8Native ? 1 : 2;
-  constexpr int NS = PATH == kPF8Native ? 2 : 4;          // MFMA K-slices per step
+  constexpr bool kF8 = PATH == kPF8Native || PATH == kPF8Exact;
+  constexpr int BK = kF8 ? 128 : 64;
+  constexpr int EB = kF8 ? 1 : 2;
+  // fragment reads per step: K-slices of 16 (16-bit), 64 (FP8 native), or
+  // pairs of 16-slices (FP8 widened to BF16 in registers)
+  constexpr int NS = PATH == kPF8Native ? 2 : 4;
   const int64_t nbm = g.M / kBM, nbn = g.N / kBN;
   const int64_t total = nbm * nbn;
   int64_t tile = blockIdx.x;
@@ -654,6 +657,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
         __syncthreads();
         frag(smem[(kt + 1) & 1][0], 0, fa[cur ^ 1], fb[cur ^ 1]);
       }
+      if constexpr (PATH == kPF8Exact) {
+        // 16 FP8 bytes per lane = K 32p + 16h + 8e + j for e = 0, 1: two BF16
+        // fragments (the same K order for A and B; products are exact)
+        u32x4 da[2][4], db[2][4];
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            da[e][mb] = u32x4{fp8x2_to_bf16x2<AT, false>(fa[cur][mb][2 * e]), fp8x2_to_bf16x2<AT, true>(fa[cur][mb][2 * e]),
+                              fp8x2_to_bf16x2<AT, false>(fa[cur][mb][2 * e + 1]), fp8x2_to_bf16x2<AT, true>(fa[cur][mb][2 * e + 1])};
+            db[e][mb] = u32x4{fp8x2_to_bf16x2<BT, false>(fb[cur][mb][2 * e]), fp8x2_to_bf16x2<BT, true>(fb[cur][mb][2 * e]),
+                              fp8x2_to_bf16x2<BT, false>(fb[cur][mb][2 * e + 1]), fp8x2_to_bf16x2<BT, true>(fb[cur][mb][2 * e + 1])};
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+              acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, da[e][mb]),
+                                                                    __builtin_bit_cast(bf16x8_t, db[e][nb]),
+                                                                    acc[mb][nb], 0, 0, 0);
+      } else
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
@@ -676,8 +703,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
       // 16 MFMA per slice with the next slice's fragment reads spread evenly
       // (8 reads; 16 for FP8; two per transposed fragment)
       constexpr int kReads = PATH == kPF8Native ? 16 : (A_KC ? 4 : 8) + (B_KC ? 4 : 8);
-      if (kSplit && ks < 2) sched_slice<0, kReads, 8>();
-      else sched_slice<0, kReads, 0>();
+      if constexpr (PATH != kPF8Exact) {
+        if (kSplit && ks < 2) sched_slice<0, kReads, 8>();
+        else sched_slice<0, kReads, 0>();
+      }
     }
   }
   const float alpha = (g.alphaA ? *g.alphaA : 1.0f) * (g.alphaB ? *g.alphaB : 1.0f);
@@ -751,14 +780,16 @@ hipError_t launch_mfma_c(const GemmArgs& g, int ct, hipStream_t s) {
 template <int AT, int BT, bool A_KC, bool B_KC, int PATH>
 hipError_t launch_mfma(const GemmArgs& g, int ct, hipStream_t s) {
   constexpr int64_t BK = PATH == kPF8Native ? 128 : 64;
-  if constexpr ((A_KC && B_KC && (PATH == kP16 || PATH == kPF8Native)) || PATH == kP16) {
-    const int eb = PATH == kPF8Native ? 1 : 2;
+  if constexpr ((A_KC && B_KC && (PATH == kP16 || PATH == kPF8Native || PATH == kPF8Exact)) ||
+                PATH == kP16) {
+    const int eb = PATH == kPF8Native || PATH == kPF8Exact ? 1 : 2;
     // buffer offsets are 32-bit: a 256-row (K-contiguous) or 64-K-row (M/N-
     // contiguous) window of either operand must span < 2 GiB; M/N-contiguous
     // rows hold 256-column windows at 16-byte boundaries
     const int64_t wa = g.lda * eb * (A_KC ? kBM : BK), wb = g.ldb * eb * (B_KC ? kBN : BK);
     const bool small = wa < (int64_t(1) << 31) && wb < (int64_t(1) << 31);
-    if (g.M % kBM == 0 && g.N % kBN == 0 && g.K % BK == 0 && (g.lda * eb) % 16 == 0 &&
+    const int64_t bk_d2l = eb == 1 ? 128 : 64;      // 128 bytes of K per row and step
+    if (g.M % kBM == 0 && g.N % kBN == 0 && g.K % bk_d2l == 0 && (g.lda * eb) % 16 == 0 &&
         (g.ldb * eb) % 16 == 0 && small) {
       const dim3 grid(static_cast<unsigned>((g.M / kBM) * (g.N / kBN)));
       switch (ct) {

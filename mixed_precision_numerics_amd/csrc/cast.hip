@@ -139,6 +139,8 @@ constexpr int kTileThreads = 256;
 // 128x128 tile per block.  Thread t owns rows r0..r0+7 and columns c0..c0+7
 // with c0 = 8*(t % 16), r0 = 8*(t / 16).  FULL: the tile is inside the tensor
 // and every access is 16-byte aligned (checked on the host).
+__device__ __forceinline__ int swz8(int c) { return (2 * (c >> 4)) & 14; }
+
 template <int XT, int YT, bool WY, bool WYT, bool VEC>
 __global__ __launch_bounds__(kTileThreads) void cast_tile(
     const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
@@ -188,11 +190,15 @@ __global__ __launch_bounds__(kTileThreads) void cast_tile(
   }
 
   if constexpr (WYT) {
-    // transposed 8x8 sub-block -> LDS rows c0+j, columns r0..r0+7
+    // transposed 8x8 sub-block -> LDS rows c0+j, columns r0..r0+7.  8-bit
+    // codes: the 8-byte unit r0/8 of row c is stored at unit (r0/8) ^ sw(c),
+    // sw(c) = 2*(c/16) mod 16 (even, so 16-byte pairs stay adjacent), which
+    // spreads a wave's stores (rows 8 apart) and the row reads over the banks
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       Code* dst = lds + (c0 + j) * kPitch + r0;
       if constexpr (sizeof(Code) == 1) {
+        dst = lds + (c0 + j) * kPitch + 8 * ((r0 / 8) ^ swz8(c0 + j));
         uint2 w;
         w.x = code[0][j] | (code[1][j] << 8) | (code[2][j] << 16) | (code[3][j] << 24);
         w.y = code[4][j] | (code[5][j] << 8) | (code[6][j] << 16) | (code[7][j] << 24);
@@ -217,6 +223,7 @@ __global__ __launch_bounds__(kTileThreads) void cast_tile(
       const int64_t orow = c_base + cc;
       const int64_t ocol = r_base + rr;
       const Code* src = lds + cc * kPitch + rr;
+      if constexpr (sizeof(Code) == 1) src = lds + cc * kPitch + 8 * ((rr / 8) ^ swz8(cc));
       if (full) {
         *reinterpret_cast<uint4*>(static_cast<Code*>(y_t) + orow * ldy_t + ocol) =
             *reinterpret_cast<const uint4*>(src);

@@ -89,12 +89,14 @@ def scalars(hp: AdamWHParams, ctr: AdamCounters, loss_scale: float):
 
 def apply(theta, m, v, g_codes, g_fmt: F.Fmt, hp: AdamWHParams,
           ctr: AdamCounters, loss_scale: float, w_fmt: F.Fmt = F.F16,
-          skip: bool | None = None):
+          skip: bool | None = None, grad_mult: float | None = None):
     """One optimizer step on float64 arrays holding FP32 values.
 
     Returns ``(theta, m, v, w_codes, applied)``; the inputs are not modified.
     ``skip`` overrides the overflow decision (used when a caller checks a
-    larger buffer than the sample it passes here).
+    larger buffer than the sample it passes here).  ``grad_mult`` (an FP32
+    value, e.g. the clip coefficient) multiplies the unscaled gradient in FP32
+    before the update: itwiki "FP16 학습 루프" clips after ``unscale_``.
     """
     theta = np.asarray(theta, dtype=np.float64)
     m = np.asarray(m, dtype=np.float64)
@@ -106,6 +108,8 @@ def apply(theta, m, v, g_codes, g_fmt: F.Fmt, hp: AdamWHParams,
     s = scalars(hp, ctr, loss_scale)
     f32 = F.f32
     g = f32(F.decode(g_codes, g_fmt) * s["inv_s"])
+    if grad_mult is not None:
+        g = f32(g * float(F.f32(grad_mult)))
     m1 = f32(f32(s["b1"] * m) + f32(s["c1"] * g))
     v1 = f32(f32(s["b2"] * v) + f32(s["c2"] * f32(g * g)))
     d = f32(f32(f32(np.sqrt(v1)) * s["rbc2"]) + s["eps"])

@@ -109,6 +109,15 @@ typedef struct {
   int32_t pad_;
 } amp_block_scales;
 
+/* Device-resident global-norm accumulator (caller-owned, 8 KiB + 8 B).
+ * sumsq holds the running sum of squares of the unscaled gradients; partial
+ * is the work area of one accumulation call (one float64 per work-group). */
+#define AMP_NORM_PARTIALS 1024
+typedef struct {
+  double sumsq;
+  double partial[AMP_NORM_PARTIALS];
+} amp_grad_norm_state;
+
 /* ------------------------------------------------------------------------ */
 
 /* Library version, status text and the calling thread's last HIP error. */
@@ -292,6 +301,52 @@ int amp_gelu_backward_f16(const void* dA16, const void* z16, int64_t n, void* dz
 
 /* out[c] = round16(fl32(sum_r x[r][c])) (sequential FP32 sum; bias grads). */
 int amp_colsum_f16(const void* x16, int64_t rows, int64_t cols, void* out16, void* stream);
+
+/* ---- gradient accumulation and global-norm clipping ----------------------
+ * Page "혼합 정밀도 학습" (itwiki), section "FP16 학습 루프": the loop unscales
+ * (unscale_) and only then clips the global gradient norm to max_norm = 1.0,
+ * so that the norm is measured on gradients of their true size; section
+ * "함께 쓰는 기법과 주의점": with gradient accumulation over micro-batches
+ * the loss-scale adjustment and the inf check run once per effective batch.
+ * Page "Mixed Precision Training/es" (marovi), "Operaciones que permanecen
+ * en FP32": reductions such as gradient norms stay in (at least) FP32; page
+ * hwlabs, "도입 체크리스트": keep gradient clipping (max_norm 1.0).
+ *
+ * Typical step: amp_grad_accumulate per micro-batch into an FP32 buffer;
+ * amp_grad_norm_init; amp_grad_norm_accumulate over every gradient buffer
+ * (it also sets found_inf, replacing amp_check_overflow); amp_clip_coefficient;
+ * amp_optimizer_step_ex(..., d_coef, AMP_OPT_SKIP_CHECK); amp_scaler_update. */
+
+/* acc[i] = f32(g[i]) if first, else fl32(acc[i] + f32(g[i])).  acc: [n] FP32
+ * (in place); grads: [n] of gt in {F16, BF16, F32}.  inf and NaN propagate,
+ * so one check of acc per effective batch sees every micro-batch. */
+int amp_grad_accumulate(float* acc, const void* grads, int gt, int64_t n, int first,
+                        void* stream);
+
+/* d_norm->sumsq = 0. */
+int amp_grad_norm_init(amp_grad_norm_state* d_norm, void* stream);
+
+/* d_norm->sumsq += sum_i (f32(g[i]) * (1/S))^2 over the finite elements, the
+ * squares exact in float64 and the sum in float64 (work-group partials added
+ * in a fixed order, so the result is reproducible); S = d_state->scale.  Any
+ * non-finite element sets d_state->found_inf = 1.  Calls on one d_norm must
+ * not overlap. */
+int amp_grad_norm_accumulate(const void* grads, int gt, int64_t n, amp_scaler_state* d_state,
+                             amp_grad_norm_state* d_norm, void* stream);
+
+/* d_out[0] = coef = min(1, fl32(max_norm / fl32(norm + 1e-6))) and d_out[1] =
+ * norm, with norm = fl32(sqrt(sumsq)) (float64 square root); if found_inf is
+ * set: d_out = {1, +inf} (the step will be skipped).  max_norm > 0. */
+int amp_clip_coefficient(const amp_grad_norm_state* d_norm, float max_norm,
+                         const amp_scaler_state* d_state, float* d_out, void* stream);
+
+/* amp_optimizer_step with an optional device FP32 gradient multiplier (the
+ * clip coefficient): g = f32(grad) * (1/S), then g = fl32(g * *d_grad_mult)
+ * when d_grad_mult != NULL; the rest as amp_optimizer_step. */
+int amp_optimizer_step_ex(float* master, float* m, float* v, const void* grads, int gt,
+                          void* w16, int wt, int64_t n, const amp_adamw_hparams* hp,
+                          amp_scaler_state* d_state, const float* d_grad_mult, int flags,
+                          void* stream);
 
 #ifdef __cplusplus
 }

@@ -23,10 +23,13 @@ __all__ = [
     "amp_cast", "amp_gemm", "amp_gemm_ex", "amp_scaler_init", "amp_optimizer_step", "amp_check_overflow",
     "amp_scaler_update", "amp_fp8_meta_init", "amp_delayed_scaling_update",
     "amp_nvfp4_quantize", "amp_bias_gelu_f16", "amp_softmax_xent_f16", "amp_gelu_backward_f16",
-    "amp_colsum_f16",
+    "amp_colsum_f16", "amp_grad_accumulate", "amp_grad_norm_init", "amp_grad_norm_accumulate",
+    "amp_clip_coefficient", "amp_optimizer_step_ex", "NORM_STATE_BYTES", "NORM_PARTIALS",
 ]
 
 F32, F16, BF16, E4M3, E5M2, E2M1X2 = 0, 1, 2, 3, 4, 5
+NORM_PARTIALS = 1024                       # amp_grad_norm_state: sumsq + partials
+NORM_STATE_BYTES = 8 * (1 + NORM_PARTIALS)
 OP_N, OP_T = 0, 1
 ROUND_RNE, ROUND_SR = 0, 1
 AMAX_MAX, AMAX_MOST_RECENT = 0, 1
@@ -85,6 +88,11 @@ _SIGS = {
     "amp_scaler_init": ([_P, ctypes.c_float, _P], _I),
     "amp_optimizer_step": ([_P, _P, _P, _P, _I, _P, _I, _I64, _P, _P, _I, _P], _I),
     "amp_check_overflow": ([_P, _I, _I64, _P, _P], _I),
+    "amp_optimizer_step_ex": ([_P, _P, _P, _P, _I, _P, _I, _I64, _P, _P, _P, _I, _P], _I),
+    "amp_grad_accumulate": ([_P, _P, _I, _I64, _I, _P], _I),
+    "amp_grad_norm_init": ([_P, _P], _I),
+    "amp_grad_norm_accumulate": ([_P, _I, _I64, _P, _P, _P], _I),
+    "amp_clip_coefficient": ([_P, ctypes.c_float, _P, _P, _P], _I),
     "amp_scaler_update": ([_P, _P, _P], _I),
     "amp_fp8_meta_init": ([_P, _P, ctypes.c_int32, ctypes.c_int32, _P], _I),
     "amp_delayed_scaling_update": ([_P, _P, ctypes.c_int32, _P, _P], _I),
@@ -190,6 +198,32 @@ def amp_optimizer_step(master, m, v, grads, gt, w16, wt, n, hp: AdamWHParams, d_
     _check("amp_optimizer_step", load().amp_optimizer_step(
         _ptr(master), _ptr(m), _ptr(v), _ptr(grads), gt, _ptr(w16), wt, n, ctypes.byref(hp),
         _ptr(d_state), flags, _stream(stream)))
+
+
+def amp_optimizer_step_ex(master, m, v, grads, gt, w16, wt, n, hp: AdamWHParams, d_state,
+                          d_grad_mult=None, flags=0, stream=None):
+    _check("amp_optimizer_step_ex", load().amp_optimizer_step_ex(
+        _ptr(master), _ptr(m), _ptr(v), _ptr(grads), gt, _ptr(w16), wt, n, ctypes.byref(hp),
+        _ptr(d_state), _ptr(d_grad_mult), flags, _stream(stream)))
+
+
+def amp_grad_accumulate(acc, grads, gt, n, first, stream=None):
+    _check("amp_grad_accumulate", load().amp_grad_accumulate(_ptr(acc), _ptr(grads), gt, n,
+                                                             int(bool(first)), _stream(stream)))
+
+
+def amp_grad_norm_init(d_norm, stream=None):
+    _check("amp_grad_norm_init", load().amp_grad_norm_init(_ptr(d_norm), _stream(stream)))
+
+
+def amp_grad_norm_accumulate(grads, gt, n, d_state, d_norm, stream=None):
+    _check("amp_grad_norm_accumulate", load().amp_grad_norm_accumulate(
+        _ptr(grads), gt, n, _ptr(d_state), _ptr(d_norm), _stream(stream)))
+
+
+def amp_clip_coefficient(d_norm, max_norm, d_state, d_out, stream=None):
+    _check("amp_clip_coefficient", load().amp_clip_coefficient(
+        _ptr(d_norm), float(max_norm), _ptr(d_state), _ptr(d_out), _stream(stream)))
 
 
 def amp_check_overflow(x, xt, n, d_state, stream=None):

@@ -150,9 +150,10 @@ int amp_check_overflow(const void* x, int xt, int64_t n, amp_scaler_state* d_sta
   return hip_status(amp::launch_check_overflow(x, xt, n, d_state, static_cast<hipStream_t>(stream)));
 }
 
-int amp_optimizer_step(float* master, float* m, float* v, const void* grads, int gt, void* w16,
-                       int wt, int64_t n, const amp_adamw_hparams* hp,
-                       amp_scaler_state* d_state, int flags, void* stream) {
+int amp_optimizer_step_ex(float* master, float* m, float* v, const void* grads, int gt,
+                          void* w16, int wt, int64_t n, const amp_adamw_hparams* hp,
+                          amp_scaler_state* d_state, const float* d_grad_mult, int flags,
+                          void* stream) {
   if (n < 0 || !hp || !d_state) return AMP_EINVAL;
   if (!is_grad(gt)) return AMP_EUNSUPPORTED;
   if (w16 && wt != AMP_F16 && wt != AMP_BF16) return AMP_EUNSUPPORTED;
@@ -167,10 +168,54 @@ int amp_optimizer_step(float* master, float* m, float* v, const void* grads, int
       if (int st = hip_status(amp::launch_check_overflow(grads, gt, n, d_state, s))) return st;
     }
     if (int st = hip_status(amp::launch_optimizer_apply(master, m, v, grads, gt, w16, wt, n, *hp,
-                                                        d_state, s)))
+                                                        d_state, d_grad_mult, s)))
       return st;
   }
   return hip_status(amp::launch_optimizer_commit(d_state, *hp, s));
+}
+
+int amp_optimizer_step(float* master, float* m, float* v, const void* grads, int gt, void* w16,
+                       int wt, int64_t n, const amp_adamw_hparams* hp,
+                       amp_scaler_state* d_state, int flags, void* stream) {
+  return amp_optimizer_step_ex(master, m, v, grads, gt, w16, wt, n, hp, d_state, nullptr, flags,
+                               stream);
+}
+
+int amp_grad_accumulate(float* acc, const void* grads, int gt, int64_t n, int first,
+                        void* stream) {
+  if (n < 0) return AMP_EINVAL;
+  if (!is_grad(gt)) return AMP_EUNSUPPORTED;
+  if (n == 0) return AMP_OK;
+  if (!acc || !grads) return AMP_EINVAL;
+  if (int st = check_device()) return st;
+  return hip_status(amp::launch_grad_accumulate(acc, grads, gt, n, first ? 1 : 0,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+int amp_grad_norm_init(amp_grad_norm_state* d_norm, void* stream) {
+  if (!d_norm) return AMP_EINVAL;
+  if (int st = check_device()) return st;
+  return hip_status(amp::launch_grad_norm_init(d_norm, static_cast<hipStream_t>(stream)));
+}
+
+int amp_grad_norm_accumulate(const void* grads, int gt, int64_t n, amp_scaler_state* d_state,
+                             amp_grad_norm_state* d_norm, void* stream) {
+  if (n < 0 || !d_state || !d_norm) return AMP_EINVAL;
+  if (!is_grad(gt)) return AMP_EUNSUPPORTED;
+  if (n == 0) return AMP_OK;
+  if (!grads) return AMP_EINVAL;
+  if (int st = check_device()) return st;
+  return hip_status(amp::launch_grad_norm(grads, gt, n, d_state, d_norm,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int amp_clip_coefficient(const amp_grad_norm_state* d_norm, float max_norm,
+                         const amp_scaler_state* d_state, float* d_out, void* stream) {
+  if (!d_norm || !d_state || !d_out || !(max_norm > 0.0f) || !(max_norm < 3.0e38f))
+    return AMP_EINVAL;
+  if (int st = check_device()) return st;
+  return hip_status(amp::launch_clip_coefficient(d_norm, max_norm, d_state, d_out,
+                                                 static_cast<hipStream_t>(stream)));
 }
 
 int amp_scaler_update(amp_scaler_state* d_state, const amp_scaler_params* p, void* stream) {

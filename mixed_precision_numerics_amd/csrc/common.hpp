@@ -64,7 +64,14 @@ hipError_t launch_check_overflow(const void* g, int gt, int64_t n, amp_scaler_st
                                  hipStream_t s);
 hipError_t launch_optimizer_apply(float* master, float* m, float* v, const void* g, int gt,
                                   void* w16, int wt, int64_t n, const amp_adamw_hparams& hp,
-                                  amp_scaler_state* st, hipStream_t s);
+                                  amp_scaler_state* st, const float* mult, hipStream_t s);
+hipError_t launch_grad_accumulate(float* acc, const void* g, int gt, int64_t n, int first,
+                                  hipStream_t s);
+hipError_t launch_grad_norm_init(amp_grad_norm_state* ns, hipStream_t s);
+hipError_t launch_grad_norm(const void* g, int gt, int64_t n, amp_scaler_state* st,
+                            amp_grad_norm_state* ns, hipStream_t s);
+hipError_t launch_clip_coefficient(const amp_grad_norm_state* ns, float max_norm,
+                                   const amp_scaler_state* st, float* out, hipStream_t s);
 hipError_t launch_optimizer_commit(amp_scaler_state* st, const amp_adamw_hparams& hp,
                                    hipStream_t s);
 hipError_t launch_scaler_init(amp_scaler_state* st, float init_scale, hipStream_t s);

@@ -84,6 +84,7 @@ __global__ __launch_bounds__(kThreads) void check_kernel(const void* __restrict_
 // ---------------------------------------------------------------- apply ---
 struct StepScalars {
   float inv_s, b1, b2, c1, c2, eps, rbc2, decay, step;
+  float mult;      // gradient multiplier (the clip coefficient) when MULT
 };
 
 __device__ __forceinline__ StepScalars make_scalars(const amp_scaler_state& st,
@@ -116,9 +117,11 @@ __device__ __forceinline__ uint32_t w16_code(float t) {
   else return f32_to_f16(t);
 }
 
+template <bool MULT>
 __device__ __forceinline__ void adam_elem(const StepScalars& k, float g16, float& th, float& m,
                                           float& v) {
-  const float g = g16 * k.inv_s;
+  float g = g16 * k.inv_s;
+  if constexpr (MULT) g = g * k.mult;
   m = k.b1 * m + k.c1 * g;
   v = k.b2 * v + k.c2 * (g * g);
   const float d = sqrtf(v) * k.rbc2 + k.eps;
@@ -128,17 +131,19 @@ __device__ __forceinline__ void adam_elem(const StepScalars& k, float g16, float
 // Vector path: 8 elements per thread per iteration, 16-byte accesses.
 // (Measured on MI355X: plain loads/stores beat the non-temporal hints for
 // this 50/50 read/write stream.)
-template <int GT, int WT, bool HAS_W>
+template <int GT, int WT, bool HAS_W, bool MULT>
 __global__ __launch_bounds__(kThreads) void apply_kernel(float* __restrict__ th_p,
                                                          float* __restrict__ m_p,
                                                          float* __restrict__ v_p,
                                                          const void* __restrict__ g_p,
                                                          void* __restrict__ w_p, int64_t n,
                                                          amp_adamw_hparams hp,
-                                                         const amp_scaler_state* __restrict__ st_p) {
+                                                         const amp_scaler_state* __restrict__ st_p,
+                                                         const float* __restrict__ mult_p) {
   const amp_scaler_state st = *st_p;
   if (st.found_inf) return;
-  const StepScalars k = make_scalars(st, hp);
+  StepScalars k = make_scalars(st, hp);
+  if constexpr (MULT) k.mult = *mult_p;
   const int64_t tid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   const int64_t nthr = static_cast<int64_t>(gridDim.x) * kThreads;
   const int64_t nv = n / 8;
@@ -173,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(float* __restrict__ th_
     float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
     float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
-    for (int q = 0; q < 8; ++q) adam_elem(k, gg[q], th[q], mm[q], vv[q]);
+    for (int q = 0; q < 8; ++q) adam_elem<MULT>(k, gg[q], th[q], mm[q], vv[q]);
     th4[2 * j] = f32x4{th[0], th[1], th[2], th[3]};
     th4[2 * j + 1] = f32x4{th[4], th[5], th[6], th[7]};
     m4[2 * j] = f32x4{mm[0], mm[1], mm[2], mm[3]};
@@ -191,28 +196,30 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(float* __restrict__ th_
   }
   for (int64_t i = nv * 8 + tid; i < n; i += nthr) {
     float th = th_p[i], m = m_p[i], v = v_p[i];
-    adam_elem(k, grad_at<GT>(g_p, i), th, m, v);
+    adam_elem<MULT>(k, grad_at<GT>(g_p, i), th, m, v);
     th_p[i] = th; m_p[i] = m; v_p[i] = v;
     if constexpr (HAS_W) static_cast<uint16_t*>(w_p)[i] = static_cast<uint16_t>(w16_code<WT>(th));
   }
 }
 
 // Scalar path for buffers that are not 16-byte aligned.
-template <int GT, int WT, bool HAS_W>
+template <int GT, int WT, bool HAS_W, bool MULT>
 __global__ __launch_bounds__(kThreads) void apply_kernel_scalar(float* __restrict__ th_p,
                                                                 float* __restrict__ m_p,
                                                                 float* __restrict__ v_p,
                                                                 const void* __restrict__ g_p,
                                                                 void* __restrict__ w_p, int64_t n,
                                                                 amp_adamw_hparams hp,
-                                                                const amp_scaler_state* __restrict__ st_p) {
+                                                                const amp_scaler_state* __restrict__ st_p,
+                                                                const float* __restrict__ mult_p) {
   const amp_scaler_state st = *st_p;
   if (st.found_inf) return;
-  const StepScalars k = make_scalars(st, hp);
+  StepScalars k = make_scalars(st, hp);
+  if constexpr (MULT) k.mult = *mult_p;
   const int64_t nthr = static_cast<int64_t>(gridDim.x) * kThreads;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; i < n; i += nthr) {
     float th = th_p[i], m = m_p[i], v = v_p[i];
-    adam_elem(k, grad_at<GT>(g_p, i), th, m, v);
+    adam_elem<MULT>(k, grad_at<GT>(g_p, i), th, m, v);
     th_p[i] = th; m_p[i] = m; v_p[i] = v;
     if constexpr (HAS_W) static_cast<uint16_t*>(w_p)[i] = static_cast<uint16_t>(w16_code<WT>(th));
   }
@@ -302,6 +309,147 @@ __global__ __launch_bounds__(kThreads) void delayed_update_kernel(amp_fp8_meta* 
   }
 }
 
+
+// ------------------------------------------- accumulation, norm, clip ---
+// Page "혼합 정밀도 학습" (itwiki), section "FP16 학습 루프" (clip the global
+// norm after unscaling) and section "함께 쓰는 기법과 주의점" (with gradient
+// accumulation, scale changes and the inf check once per effective batch).
+
+template <int GT>
+__device__ __forceinline__ void widen8(const void* g, int64_t j, float (&x)[8]) {
+  if constexpr (GT == AMP_F32) {
+    const f32x4 a = reinterpret_cast<const f32x4*>(g)[2 * j];
+    const f32x4 b = reinterpret_cast<const f32x4*>(g)[2 * j + 1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  } else {
+    const u32x4 w = reinterpret_cast<const u32x4*>(g)[j];
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (GT == AMP_BF16) {
+        x[2 * q] = bitsf(ww[q] << 16);
+        x[2 * q + 1] = bitsf(ww[q] & 0xffff0000u);
+      } else {
+        x[2 * q] = f16_to_f32(ww[q] & 0xffffu);
+        x[2 * q + 1] = f16_to_f32(ww[q] >> 16);
+      }
+    }
+  }
+}
+
+// acc = first ? f32(g) : fl32(acc + f32(g)); 8 elements per thread per step
+// when every buffer is 16-byte aligned.
+template <int GT, bool VEC>
+__global__ __launch_bounds__(kThreads) void accumulate_kernel(float* __restrict__ acc,
+                                                              const void* __restrict__ g,
+                                                              int64_t n, int first) {
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t nthr = static_cast<int64_t>(gridDim.x) * kThreads;
+  int64_t done = 0;
+  if constexpr (VEC) {
+    const int64_t nv = n / 8;
+    f32x4* a4 = reinterpret_cast<f32x4*>(acc);
+    for (int64_t j = tid; j < nv; j += nthr) {
+      float x[8];
+      widen8<GT>(g, j, x);
+      f32x4 lo = f32x4{x[0], x[1], x[2], x[3]}, hi = f32x4{x[4], x[5], x[6], x[7]};
+      if (!first) {
+        const f32x4 p = a4[2 * j], q = a4[2 * j + 1];
+        lo = f32x4{p.x + lo.x, p.y + lo.y, p.z + lo.z, p.w + lo.w};
+        hi = f32x4{q.x + hi.x, q.y + hi.y, q.z + hi.z, q.w + hi.w};
+      }
+      a4[2 * j] = lo;
+      a4[2 * j + 1] = hi;
+    }
+    done = nv * 8;
+  }
+  for (int64_t i = done + tid; i < n; i += nthr) {
+    const float x = grad_at<GT>(g, i);
+    acc[i] = first ? x : acc[i] + x;
+  }
+}
+
+// Fixed-order float64 block sum (wave xor-tree, then waves in order).
+__device__ __forceinline__ double block_sum_f64(double v, double* red) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  if (lane == 0) red[wid] = v;
+  __syncthreads();
+  double t = 0.0;
+  if (threadIdx.x == 0)
+    for (int w = 0; w < kThreads / kWave; ++w) t += red[w];
+  return t;
+}
+
+// Sum of squares of the finite gradients (float64; a float32 square is exact
+// in float64), one partial per work-group; non-finite elements set found_inf.
+template <int GT, bool VEC>
+__global__ __launch_bounds__(kThreads) void norm_kernel(const void* __restrict__ g, int64_t n,
+                                                        amp_scaler_state* __restrict__ st,
+                                                        double* __restrict__ partial) {
+  __shared__ double red[kThreads / kWave];
+  __shared__ uint32_t bad_any;
+  if (threadIdx.x == 0) bad_any = 0;
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  const int64_t nthr = static_cast<int64_t>(gridDim.x) * kThreads;
+  double acc = 0.0;
+  uint32_t bad = 0;
+  auto add = [&](float x) {
+    const uint32_t fin = static_cast<uint32_t>((fbits(x) & 0x7f800000u) != 0x7f800000u);
+    bad |= fin ^ 1u;
+    const double d = fin ? static_cast<double>(x) : 0.0;
+    acc = __builtin_fma(d, d, acc);
+  };
+  int64_t done = 0;
+  if constexpr (VEC) {
+    const int64_t nv = n / 8;
+    for (int64_t j = tid; j < nv; j += nthr) {
+      float x[8];
+      widen8<GT>(g, j, x);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) add(x[q]);
+    }
+    done = nv * 8;
+  }
+  for (int64_t i = done + tid; i < n; i += nthr) add(grad_at<GT>(g, i));
+  __syncthreads();
+  if (bad) bad_any = 1u;
+  const double t = block_sum_f64(acc, red);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    partial[blockIdx.x] = t;
+    if (bad_any) st->found_inf = 1;
+  }
+}
+
+// sumsq += (partials in order) * (1/S)^2 -- exact scaling by a power of two.
+__global__ void norm_finalize(amp_grad_norm_state* ns, int nb, const amp_scaler_state* st) {
+  if (threadIdx.x != 0) return;
+  double t = 0.0;
+  for (int b = 0; b < nb; ++b) t += ns->partial[b];
+  const double inv = static_cast<double>(1.0f / st->scale);
+  ns->sumsq += t * inv * inv;
+}
+
+__global__ void norm_init_kernel(amp_grad_norm_state* ns) {
+  if (threadIdx.x == 0) ns->sumsq = 0.0;
+}
+
+__global__ void clip_kernel(const amp_grad_norm_state* ns, float max_norm,
+                            const amp_scaler_state* st, float* out) {
+  if (threadIdx.x != 0) return;
+  if (st->found_inf) {
+    out[0] = 1.0f;
+    out[1] = __builtin_inff();
+    return;
+  }
+  const float norm = static_cast<float>(__builtin_sqrt(ns->sumsq));
+  const float c = max_norm / (norm + 1e-6f);
+  out[0] = c < 1.0f ? c : 1.0f;
+  out[1] = norm;
+}
+
 // Grid-stride launches: up to 64 blocks per CU keeps enough 16-byte requests
 // in flight to saturate HBM (measured).
 int64_t grid_for(int64_t work_items) {
@@ -310,26 +458,36 @@ int64_t grid_for(int64_t work_items) {
   return b < 1 ? 1 : b;
 }
 
-template <int GT, int WT, bool HAS_W>
+template <int GT, int WT, bool HAS_W, bool MULT>
 hipError_t launch_apply_t(float* th, float* m, float* v, const void* g, void* w, int64_t n,
-                          const amp_adamw_hparams& hp, amp_scaler_state* st, hipStream_t s) {
+                          const amp_adamw_hparams& hp, amp_scaler_state* st, const float* mult,
+                          hipStream_t s) {
   const bool vec = aligned(th, 16) && aligned(m, 16) && aligned(v, 16) && aligned(g, 16) &&
                    (!HAS_W || aligned(w, 16));
   if (vec)
-    apply_kernel<GT, WT, HAS_W><<<dim3(static_cast<unsigned>(grid_for(n / 8))), kThreads, 0, s>>>(
-        th, m, v, g, w, n, hp, st);
+    apply_kernel<GT, WT, HAS_W, MULT><<<dim3(static_cast<unsigned>(grid_for(n / 8))), kThreads, 0, s>>>(
+        th, m, v, g, w, n, hp, st, mult);
   else
-    apply_kernel_scalar<GT, WT, HAS_W><<<dim3(static_cast<unsigned>(grid_for(n))), kThreads, 0, s>>>(
-        th, m, v, g, w, n, hp, st);
+    apply_kernel_scalar<GT, WT, HAS_W, MULT><<<dim3(static_cast<unsigned>(grid_for(n))), kThreads, 0, s>>>(
+        th, m, v, g, w, n, hp, st, mult);
   return hipGetLastError();
+}
+
+template <int GT, bool MULT>
+hipError_t launch_apply_m(float* th, float* m, float* v, const void* g, void* w, int wt, int64_t n,
+                          const amp_adamw_hparams& hp, amp_scaler_state* st, const float* mult,
+                          hipStream_t s) {
+  if (w == nullptr) return launch_apply_t<GT, AMP_F16, false, MULT>(th, m, v, g, w, n, hp, st, mult, s);
+  if (wt == AMP_BF16) return launch_apply_t<GT, AMP_BF16, true, MULT>(th, m, v, g, w, n, hp, st, mult, s);
+  return launch_apply_t<GT, AMP_F16, true, MULT>(th, m, v, g, w, n, hp, st, mult, s);
 }
 
 template <int GT>
 hipError_t launch_apply_g(float* th, float* m, float* v, const void* g, void* w, int wt, int64_t n,
-                          const amp_adamw_hparams& hp, amp_scaler_state* st, hipStream_t s) {
-  if (w == nullptr) return launch_apply_t<GT, AMP_F16, false>(th, m, v, g, w, n, hp, st, s);
-  if (wt == AMP_BF16) return launch_apply_t<GT, AMP_BF16, true>(th, m, v, g, w, n, hp, st, s);
-  return launch_apply_t<GT, AMP_F16, true>(th, m, v, g, w, n, hp, st, s);
+                          const amp_adamw_hparams& hp, amp_scaler_state* st, const float* mult,
+                          hipStream_t s) {
+  if (mult) return launch_apply_m<GT, true>(th, m, v, g, w, wt, n, hp, st, mult, s);
+  return launch_apply_m<GT, false>(th, m, v, g, w, wt, n, hp, st, mult, s);
 }
 
 }  // namespace
@@ -354,12 +512,59 @@ hipError_t launch_check_overflow(const void* g, int gt, int64_t n, amp_scaler_st
 
 hipError_t launch_optimizer_apply(float* th, float* m, float* v, const void* g, int gt, void* w,
                                   int wt, int64_t n, const amp_adamw_hparams& hp,
-                                  amp_scaler_state* st, hipStream_t s) {
+                                  amp_scaler_state* st, const float* mult, hipStream_t s) {
   switch (gt) {
-    case AMP_F32: return launch_apply_g<AMP_F32>(th, m, v, g, w, wt, n, hp, st, s);
-    case AMP_BF16: return launch_apply_g<AMP_BF16>(th, m, v, g, w, wt, n, hp, st, s);
-    default: return launch_apply_g<AMP_F16>(th, m, v, g, w, wt, n, hp, st, s);
+    case AMP_F32: return launch_apply_g<AMP_F32>(th, m, v, g, w, wt, n, hp, st, mult, s);
+    case AMP_BF16: return launch_apply_g<AMP_BF16>(th, m, v, g, w, wt, n, hp, st, mult, s);
+    default: return launch_apply_g<AMP_F16>(th, m, v, g, w, wt, n, hp, st, mult, s);
   }
+}
+
+hipError_t launch_grad_accumulate(float* acc, const void* g, int gt, int64_t n, int first,
+                                  hipStream_t s) {
+  const bool vec = aligned(acc, 16) && aligned(g, 16);
+  const dim3 grid(static_cast<unsigned>(grid_for(vec ? n / 8 + 1 : n)));
+#define AMP_ACC(T)                                                                      \
+  if (vec) accumulate_kernel<T, true><<<grid, kThreads, 0, s>>>(acc, g, n, first);      \
+  else accumulate_kernel<T, false><<<grid, kThreads, 0, s>>>(acc, g, n, first);
+  switch (gt) {
+    case AMP_F32: AMP_ACC(AMP_F32) break;
+    case AMP_BF16: AMP_ACC(AMP_BF16) break;
+    default: AMP_ACC(AMP_F16) break;
+  }
+#undef AMP_ACC
+  return hipGetLastError();
+}
+
+hipError_t launch_grad_norm_init(amp_grad_norm_state* ns, hipStream_t s) {
+  norm_init_kernel<<<1, 64, 0, s>>>(ns);
+  return hipGetLastError();
+}
+
+hipError_t launch_grad_norm(const void* g, int gt, int64_t n, amp_scaler_state* st,
+                            amp_grad_norm_state* ns, hipStream_t s) {
+  const bool vec = aligned(g, 16);
+  int64_t nb = (n + 8 * kThreads - 1) / (8 * kThreads);
+  if (nb > AMP_NORM_PARTIALS) nb = AMP_NORM_PARTIALS;
+  if (nb < 1) nb = 1;
+  const dim3 grid(static_cast<unsigned>(nb));
+#define AMP_NORM(T)                                                                        \
+  if (vec) norm_kernel<T, true><<<grid, kThreads, 0, s>>>(g, n, st, ns->partial);           \
+  else norm_kernel<T, false><<<grid, kThreads, 0, s>>>(g, n, st, ns->partial);
+  switch (gt) {
+    case AMP_F32: AMP_NORM(AMP_F32) break;
+    case AMP_BF16: AMP_NORM(AMP_BF16) break;
+    default: AMP_NORM(AMP_F16) break;
+  }
+#undef AMP_NORM
+  norm_finalize<<<1, 64, 0, s>>>(ns, static_cast<int>(nb), st);
+  return hipGetLastError();
+}
+
+hipError_t launch_clip_coefficient(const amp_grad_norm_state* ns, float max_norm,
+                                   const amp_scaler_state* st, float* out, hipStream_t s) {
+  clip_kernel<<<1, 64, 0, s>>>(ns, max_norm, st, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_optimizer_commit(amp_scaler_state* st, const amp_adamw_hparams& hp,

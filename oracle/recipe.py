@@ -16,6 +16,12 @@ Readings (the pages are silent):
 * If ``amax_max`` is not finite or is zero, the previous scale is kept.
 * ``scale_inv = fl32(1 / scale)``, used to dequantise in the GEMM epilogue.
 * Initial state: history all zero, ``pos = 0``, ``scale = scale_inv = 1``.
+
+Current (just-in-time) scaling, the alternative the same section contrasts
+with delayed scaling: the tensor is read once to find its amax and then cast
+with ``scale = fp8_max / (margin * amax)`` from that amax (two reads instead of
+one).  Reading: with a zero or non-finite amax there is no history to fall
+back on, so the scale is 1.
 """
 from __future__ import annotations
 
@@ -66,3 +72,13 @@ def update(meta: FP8Meta, fp8_max: float, margin: float = 1.0,
     meta.pos = (meta.pos + 1) % meta.history_len
     meta.amax_cur_bits = 0
     return meta
+
+
+def current_scale(amax_bits: int, fp8_max: float, margin: float = 1.0):
+    """(scale, scale_inv) of current scaling from this tensor's amax bits."""
+    amax = float(F.from_f32_bits(np.uint32(amax_bits)))
+    if np.isfinite(amax) and amax > 0.0:
+        denom = float(F.f32(np.float64(F.f32(margin)) * amax))
+        scale = float(F.f32(np.float64(F.f32(fp8_max)) / denom))
+        return scale, float(F.f32(1.0 / scale))
+    return 1.0, 1.0

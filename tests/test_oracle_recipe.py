@@ -139,3 +139,24 @@ def test_scaler_collapse_no_floor():
     for _ in range(40):
         S.update(st, True)
     assert st.scale == 2.0 ** (16 - 40)
+
+
+def test_current_scaling_closed_forms():
+    """Current scaling uses this tensor's amax: 2^t -> 448 * 2^-t; the largest
+    element then casts to exactly +-448 (E4M3 max); zero or NaN amax -> 1."""
+    bits = lambda v: int(synth.f32_bits(np.array([v], np.float32))[0])
+    for t in range(-10, 11):
+        sc, inv = R.current_scale(bits(2.0 ** t), R.E4M3_MAX)
+        assert sc == 448.0 * 2.0 ** -t
+        assert inv == float(np.float32(1.0) / np.float32(sc))
+    x = synth.normal_f32(7, 1000, 3.0)
+    am = C.amax_bits(synth.f32_bits(np.abs(x)))
+    sc, _ = R.current_scale(int(am), R.E4M3_MAX)
+    codes, _ = C.cast(synth.f32_bits(x), F.F32, F.E4M3, sc)
+    i = int(np.argmax(np.abs(x)))
+    assert abs(F.decode(codes[i:i + 1], F.E4M3)[0]) == 448.0       # no saturation loss
+    assert np.all(np.abs(F.decode(codes, F.E4M3)) <= 448.0)
+    assert R.current_scale(0, R.E4M3_MAX) == (1.0, 1.0)
+    assert R.current_scale(0x7FC00000, R.E5M2_MAX) == (1.0, 1.0)
+    sc, _ = R.current_scale(bits(100.0), R.E5M2_MAX, 2.0)
+    assert sc == float(F.f32(57344.0 / 200.0))

@@ -230,6 +230,17 @@ int amp_check_overflow(const void* x, int xt, int64_t n, amp_scaler_state* d_sta
  * found_inf = 0.  No floor on the scale.  p == NULL uses (2, 0.5, 2000). */
 int amp_scaler_update(amp_scaler_state* d_state, const amp_scaler_params* p, void* stream);
 
+/* amp_cast_current_scaling -- current (just-in-time) scaling: one pass finds
+ * amax(|x|) -> d_meta->amax_cur, then d_meta->scale = fp8_max / (margin *
+ * amax) in FP32 (1 if the amax is zero or non-finite) and scale_inv = 1/scale,
+ * then amp_cast with that scale (x read twice; pos and the history are not
+ * touched).  Source: hwlabs "Delayed Scaling 동작 원리" (the contrast with
+ * delayed scaling, which reads x once using earlier steps' amax).  Arguments
+ * as amp_cast; r supplies fp8_max and margin. */
+int amp_cast_current_scaling(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
+                             void* y, int yt, int64_t ldy, void* y_t, int64_t ldy_t,
+                             const amp_delayed_recipe* r, amp_fp8_meta* d_meta, void* stream);
+
 /* amp_fp8_meta_init -- n metas: amax_cur 0, scale = scale_inv = 1, pos 0,
  * and d_history[n * history_len] zero-filled. */
 int amp_fp8_meta_init(amp_fp8_meta* d_metas, float* d_history, int32_t n,

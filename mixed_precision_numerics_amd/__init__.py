@@ -25,6 +25,7 @@ __all__ = [
     "amp_nvfp4_quantize", "amp_bias_gelu_f16", "amp_softmax_xent_f16", "amp_gelu_backward_f16",
     "amp_colsum_f16", "amp_grad_accumulate", "amp_grad_norm_init", "amp_grad_norm_accumulate",
     "amp_clip_coefficient", "amp_optimizer_step_ex", "NORM_STATE_BYTES", "NORM_PARTIALS",
+    "amp_cast_current_scaling",
 ]
 
 F32, F16, BF16, E4M3, E5M2, E2M1X2 = 0, 1, 2, 3, 4, 5
@@ -90,6 +91,8 @@ _SIGS = {
     "amp_check_overflow": ([_P, _I, _I64, _P, _P], _I),
     "amp_optimizer_step_ex": ([_P, _P, _P, _P, _I, _P, _I, _I64, _P, _P, _P, _I, _P], _I),
     "amp_grad_accumulate": ([_P, _P, _I, _I64, _I, _P], _I),
+    "amp_cast_current_scaling": ([_P, _I, _I64, _I64, _I64, _P, _I, _I64, _P, _I64, _P, _P, _P],
+                                 _I),
     "amp_grad_norm_init": ([_P, _P], _I),
     "amp_grad_norm_accumulate": ([_P, _I, _I64, _P, _P, _P], _I),
     "amp_clip_coefficient": ([_P, ctypes.c_float, _P, _P, _P], _I),
@@ -205,6 +208,13 @@ def amp_optimizer_step_ex(master, m, v, grads, gt, w16, wt, n, hp: AdamWHParams,
     _check("amp_optimizer_step_ex", load().amp_optimizer_step_ex(
         _ptr(master), _ptr(m), _ptr(v), _ptr(grads), gt, _ptr(w16), wt, n, ctypes.byref(hp),
         _ptr(d_state), _ptr(d_grad_mult), flags, _stream(stream)))
+
+
+def amp_cast_current_scaling(x, xt, rows, cols, ldx, y, yt, ldy, y_t, ldy_t,
+                             r: "DelayedRecipe", d_meta, stream=None):
+    _check("amp_cast_current_scaling", load().amp_cast_current_scaling(
+        _ptr(x), xt, rows, cols, ldx, _ptr(y), yt, ldy, _ptr(y_t), ldy_t, ctypes.byref(r),
+        _ptr(d_meta), _stream(stream)))
 
 
 def amp_grad_accumulate(acc, grads, gt, n, first, stream=None):

@@ -86,6 +86,21 @@ int amp_cast(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx, voi
                                      d_amax, static_cast<hipStream_t>(stream)));
 }
 
+int amp_cast_current_scaling(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
+                             void* y, int yt, int64_t ldy, void* y_t, int64_t ldy_t,
+                             const amp_delayed_recipe* r, amp_fp8_meta* d_meta, void* stream) {
+  if (rows < 0 || cols < 0 || !r || !d_meta) return AMP_EINVAL;
+  if (!(r->fp8_max > 0.0f) || !(r->margin > 0.0f)) return AMP_EINVAL;
+  if (!is_cast_in(xt) || !is_cast_out(yt)) return AMP_EUNSUPPORTED;
+  if (rows == 0 || cols == 0) return AMP_OK;
+  if (!x || (!y && !y_t)) return AMP_EINVAL;
+  if (ldx < cols || (y && ldy < cols) || (y_t && ldy_t < rows)) return AMP_EINVAL;
+  if (int st = check_device()) return st;
+  return hip_status(amp::launch_cast_current(x, xt, rows, cols, ldx, y, yt, ldy, y_t, ldy_t,
+                                             r->fp8_max, r->margin, d_meta,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 int amp_gemm(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A, int at,
              int64_t lda, const float* d_alphaA, const void* B, int bt, int64_t ldb,
              const float* d_alphaB, void* C, int ct, int64_t ldc, const amp_block_scales* bsA,

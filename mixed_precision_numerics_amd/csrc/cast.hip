@@ -288,6 +288,59 @@ hipError_t dispatch_out(int yt, const void* x, int64_t rows, int64_t cols, int64
   }
 }
 
+
+// ------------------------------------------------- current scaling ---
+// Page hwlabs, section "Delayed Scaling 동작 원리": current (just-in-time)
+// scaling reads the tensor once for its amax and once more for the cast.
+
+// amax (FP32 bit-max of |x|) of a [rows, cols] tensor with row stride ldx.
+template <int XT, bool VEC>
+__global__ __launch_bounds__(kFlatThreads) void amax_kernel(const void* __restrict__ x,
+                                                           int64_t rows, int64_t cols,
+                                                           int64_t ldx, float* __restrict__ d_amax) {
+  __shared__ uint32_t red[kFlatThreads / kWave];
+  uint32_t am = 0;
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * kFlatThreads + threadIdx.x;
+  const int64_t nthr = static_cast<int64_t>(gridDim.x) * kFlatThreads;
+  const int64_t n = rows * cols;
+  auto take = [&](float v) {
+    const uint32_t a = fbits(v) & 0x7fffffffu;
+    am = am > a ? am : a;
+  };
+  if constexpr (VEC) {       // contiguous rows (ldx == cols), 16-byte aligned
+    const int64_t nv = n / 8;
+    for (int64_t j = tid; j < nv; j += nthr) {
+      float v[8];
+      load8<XT>(x, j * 8, v);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) take(v[k]);
+    }
+    for (int64_t i = nv * 8 + tid; i < n; i += nthr) take(load_one<XT>(x, i));
+  } else {
+    for (int64_t i = tid; i < n; i += nthr) {
+      const int64_t r = i / cols;
+      take(load_one<XT>(x, r * ldx + (i - r * cols)));
+    }
+  }
+  am = block_max_u32<kFlatThreads>(am, red);
+  if (threadIdx.x == 0 && am != 0)
+    atomicMax(reinterpret_cast<unsigned int*>(d_amax), canon_amax(am));
+}
+
+__global__ void meta_zero_amax(amp_fp8_meta* mt) {
+  if (threadIdx.x == 0) mt->amax_cur = 0.0f;
+}
+
+// scale = fp8_max / (margin * amax) in FP32; 1 for a zero or non-finite amax.
+__global__ void current_scale_kernel(amp_fp8_meta* mt, float fp8_max, float margin) {
+  if (threadIdx.x != 0) return;
+  const uint32_t b = fbits(mt->amax_cur);
+  float scale = 1.0f;
+  if (b < 0x7f800000u && b != 0u) scale = fp8_max / (margin * bitsf(b));
+  mt->scale = scale;
+  mt->scale_inv = 1.0f / scale;
+}
+
 }  // namespace
 
 hipError_t launch_cast(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx, void* y,
@@ -298,6 +351,30 @@ hipError_t launch_cast(const void* x, int xt, int64_t rows, int64_t cols, int64_
     case AMP_BF16: return dispatch_out<AMP_BF16>(yt, x, rows, cols, ldx, y, ldy, y_t, ldy_t, d_scale, d_amax, s);
     default: return dispatch_out<AMP_F16>(yt, x, rows, cols, ldx, y, ldy, y_t, ldy_t, d_scale, d_amax, s);
   }
+}
+
+hipError_t launch_cast_current(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
+                               void* y, int yt, int64_t ldy, void* y_t, int64_t ldy_t,
+                               float fp8_max, float margin, amp_fp8_meta* meta, hipStream_t s) {
+  meta_zero_amax<<<1, 64, 0, s>>>(meta);
+  const bool vec = ldx == cols && aligned(x, 16);
+  int64_t blocks = (rows * cols / (vec ? 8 : 1) + kFlatThreads - 1) / kFlatThreads;
+  if (blocks > 256 * 16) blocks = 256 * 16;
+  if (blocks < 1) blocks = 1;
+  const dim3 grid(static_cast<unsigned>(blocks));
+  float* am = &meta->amax_cur;
+#define AMP_AMAX(T)                                                                     \
+  if (vec) amax_kernel<T, true><<<grid, kFlatThreads, 0, s>>>(x, rows, cols, ldx, am);   \
+  else amax_kernel<T, false><<<grid, kFlatThreads, 0, s>>>(x, rows, cols, ldx, am);
+  switch (xt) {
+    case AMP_F32: AMP_AMAX(AMP_F32) break;
+    case AMP_BF16: AMP_AMAX(AMP_BF16) break;
+    default: AMP_AMAX(AMP_F16) break;
+  }
+#undef AMP_AMAX
+  current_scale_kernel<<<1, 64, 0, s>>>(meta, fp8_max, margin);
+  if (hipError_t e = hipGetLastError()) return e;
+  return launch_cast(x, xt, rows, cols, ldx, y, yt, ldy, y_t, ldy_t, &meta->scale, nullptr, s);
 }
 
 }  // namespace amp

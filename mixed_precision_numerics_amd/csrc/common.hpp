@@ -60,6 +60,9 @@ inline bool aligned(const void* p, uintptr_t a) {
 hipError_t launch_cast(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
                        void* y, int yt, int64_t ldy, void* y_t, int64_t ldy_t,
                        const float* d_scale, float* d_amax, hipStream_t s);
+hipError_t launch_cast_current(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
+                               void* y, int yt, int64_t ldy, void* y_t, int64_t ldy_t,
+                               float fp8_max, float margin, amp_fp8_meta* meta, hipStream_t s);
 hipError_t launch_check_overflow(const void* g, int gt, int64_t n, amp_scaler_state* st,
                                  hipStream_t s);
 hipError_t launch_optimizer_apply(float* master, float* m, float* v, const void* g, int gt,

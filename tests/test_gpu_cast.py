@@ -141,3 +141,57 @@ def test_cast_structured_sweep_of_all_binades(yt, low, pats):
     bad = np.nonzero(got != want)[0]
     assert bad.size == 0, (bad[:8], bits[bad[:8]], got[bad[:8]], want[bad[:8]])
     assert host(amax, np.uint32)[0] == want_amax
+
+
+@pytest.mark.parametrize("xt,yt,ld_pad,transposed", [
+    (amp.BF16, amp.E4M3, 0, True), (amp.F32, amp.E4M3, 5, True), (amp.BF16, amp.E5M2, 0, False),
+    (amp.F16, amp.E5M2, 3, False)])
+def test_current_scaling_cast(xt, yt, ld_pad, transposed):
+    """amp_cast_current_scaling: amax of this tensor, scale from it, cast with
+    it -- meta and codes bit-exact (oracle recipe.current_scale + cast)."""
+    from oracle import recipe as OR
+    rows, cols = 515, 389
+    ldx = cols + ld_pad
+    x = synth.student_t_f32(60 + xt, rows * ldx, scale=7.0).reshape(rows, ldx)
+    if xt == amp.F32:
+        codes = synth.f32_bits(x).copy()
+    elif xt == amp.BF16:
+        codes = synth.to_bf16_codes(x)
+    else:
+        codes = synth.to_f16_codes(np.clip(x, -65504, 65504))
+    fin, _ = IN[xt]
+    fout, odt = OUT[yt]
+    fmax = 448.0 if yt == amp.E4M3 else 57344.0
+    r = amp.DelayedRecipe(fmax, 1.0, 1024, amp.AMAX_MAX)
+    meta = empty(16)
+    y = empty(rows * cols, fill=0xAB)
+    yt_buf = empty(rows * cols, fill=0xAB) if transposed else None
+    amp.amp_cast_current_scaling(dev(codes), xt, rows, cols, ldx, y, yt, cols, yt_buf, rows, r, meta)
+    view = codes[:, :cols]
+    am = int(OC.amax_bits(OC.widen_to_f32_bits(view.ravel(), fin)))
+    sc, inv = OR.current_scale(am, fmax, 1.0)
+    m = host(meta, amp.FP8_META_DTYPE)[0]
+    assert int(np.float32(m["amax_cur"]).view(np.uint32)) == am
+    assert m["scale"] == np.float32(sc) and m["scale_inv"] == np.float32(inv)
+    want, _ = OC.cast(view.ravel(), fin, fout, sc)
+    assert np.array_equal(host(y, odt)[:rows * cols], want)
+    if transposed:
+        assert np.array_equal(host(yt_buf, odt)[:rows * cols].reshape(cols, rows),
+                              want.reshape(rows, cols).T)
+
+
+@pytest.mark.parametrize("fill", ["zero", "nan"])
+def test_current_scaling_degenerate(fill):
+    from oracle import recipe as OR
+    n = 4096
+    codes = np.zeros(n, np.uint16) if fill == "zero" else np.full(n, 0x3C00, np.uint16)
+    if fill == "nan":
+        codes[100] = 0x7FC1
+    r = amp.DelayedRecipe(448.0, 1.0, 1024, amp.AMAX_MAX)
+    meta = empty(16)
+    y = empty(n)
+    amp.amp_cast_current_scaling(dev(codes), amp.BF16, 1, n, n, y, amp.E4M3, n, None, 0, r, meta)
+    m = host(meta, amp.FP8_META_DTYPE)[0]
+    assert m["scale"] == 1.0 and m["scale_inv"] == 1.0
+    want, _ = OC.cast(codes, F.BF16, F.E4M3, 1.0)
+    assert np.array_equal(host(y, np.uint8)[:n], want)

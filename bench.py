@@ -16,7 +16,9 @@ Also measured in the same run (reported under "components"):
   * the NVFP4 weight-gradient GEMM 20480 x 5120 x 16384 and its two
     quantizer calls (RHT on both operands, stochastic rounding on dY);
   * the scaled casts (BF16 -> E4M3 flat 2^31, BF16 -> E5M2 [8192 x 28672]
-    with its transposed copy).
+    with its transposed copy), and delayed against current scaling;
+  * the global-norm pass (2^31 FP16 gradients) and FP32 gradient
+    accumulation.
 The CPU oracle is timed on a bounded sample of the optimizer workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-components]
@@ -322,6 +324,58 @@ def nvfp4_workload(torch, amp):
             "tflop_per_step": round(flops / 1e12, 3)}
 
 
+def scaling_workload(torch, amp):
+    """Delayed scaling (one read: the scale comes from earlier steps) against
+    current scaling (amax pass, then the cast) on the FP8 block's activation
+    [8192 x 4096] and FFN output gradient [8192 x 28672], each with its
+    transposed copy."""
+    out = {}
+    gen = torch.Generator(device="cuda").manual_seed(9)
+    for name, R, C, yt, fmax in (("x_e4m3", 8192, 4096, amp.E4M3, 448.0),
+                                 ("dy_e5m2", 8192, 28672, amp.E5M2, 57344.0)):
+        x = torch.randn(R, C, device="cuda", generator=gen).to(torch.bfloat16)
+        y = torch.empty(R * C, device="cuda", dtype=torch.uint8)
+        y_t = torch.empty(R * C, device="cuda", dtype=torch.uint8)
+        meta = torch.empty(16, device="cuda", dtype=torch.uint8)
+        hist = torch.empty(4 * 1024, device="cuda", dtype=torch.uint8)
+        amp.amp_fp8_meta_init(meta, hist, 1, 1024)
+        r = amp.DelayedRecipe(fmax, 1.0, 1024, amp.AMAX_MAX)
+        mp = meta.data_ptr()
+        d_ms = _timed(torch, lambda: amp.amp_cast(x, amp.BF16, R, C, C, y, yt, C, y_t, R, mp + 4, mp),
+                      10)
+        c_ms = _timed(torch, lambda: amp.amp_cast_current_scaling(x, amp.BF16, R, C, C, y, yt, C,
+                                                                  y_t, R, r, meta), 10)
+        out[name] = {"delayed_ms": round(d_ms, 4), "current_ms": round(c_ms, 4),
+                     "current_over_delayed": round(c_ms / d_ms, 3)}
+        del x, y, y_t
+    torch.cuda.empty_cache()
+    return out
+
+
+def clip_workload(torch, amp):
+    """Global-norm pass over 2^31 FP16 gradients (2 B/param read; also the
+    overflow check) and FP32 micro-batch accumulation of 2^30 FP16 gradients
+    (10 B/param)."""
+    n = 1 << 31
+    g = torch.randn(n, device="cuda", dtype=torch.float16)
+    st = torch.empty(40, device="cuda", dtype=torch.uint8)
+    amp.amp_scaler_init(st, 1024.0)
+    ns = torch.empty(amp.NORM_STATE_BYTES, device="cuda", dtype=torch.uint8)
+    amp.amp_grad_norm_init(ns)
+    n_ms = _timed(torch, lambda: amp.amp_grad_norm_accumulate(g, amp.F16, n, st, ns), 5)
+    na = 1 << 30
+    acc = torch.empty(na, device="cuda", dtype=torch.float32)
+    amp.amp_grad_accumulate(acc, g, amp.F16, na, True)
+    a_ms = _timed(torch, lambda: amp.amp_grad_accumulate(acc, g, amp.F16, na, False), 5)
+    del g, acc
+    torch.cuda.empty_cache()
+    return {"norm_2pow31_f16": {"ms": round(n_ms, 4), "gbs": round(2 * n / n_ms / 1e6, 1),
+                                "frac": round(2 * n / n_ms / 1e6 / HBM_PEAK_GBS, 4)},
+            "accumulate_2pow30_f16_to_f32": {"ms": round(a_ms, 4),
+                                            "gbs": round(10 * na / a_ms / 1e6, 1),
+                                            "frac": round(10 * na / a_ms / 1e6 / HBM_PEAK_GBS, 4)}}
+
+
 def measured_traffic():
     """HBM bytes per launch of the apply kernel, from the committed rocprofv3
     counter summary, or None when the kernel sources changed since then."""
@@ -403,6 +457,10 @@ def main():
         comps["cast_t"] = cast_t_workload(torch, amp)
         log("components: NVFP4 weight-gradient quantize + GEMM")
         comps["nvfp4_wgrad"] = nvfp4_workload(torch, amp)
+        log("components: delayed vs current scaling casts")
+        comps["scaling"] = scaling_workload(torch, amp)
+        log("components: gradient norm and accumulation")
+        comps["clip"] = clip_workload(torch, amp)
     traffic = measured_traffic()
     cpu = None
     if not args.no_cpu_baseline:

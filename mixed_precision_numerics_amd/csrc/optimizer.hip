@@ -369,7 +369,10 @@ __global__ __launch_bounds__(kThreads) void accumulate_kernel(float* __restrict_
   }
 }
 
+constexpr int kNormThreads = 1024;
+
 // Fixed-order float64 block sum (wave xor-tree, then waves in order).
+template <int NT>
 __device__ __forceinline__ double block_sum_f64(double v, double* red) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, kWave);
@@ -378,44 +381,55 @@ __device__ __forceinline__ double block_sum_f64(double v, double* red) {
   __syncthreads();
   double t = 0.0;
   if (threadIdx.x == 0)
-    for (int w = 0; w < kThreads / kWave; ++w) t += red[w];
+    for (int w = 0; w < NT / kWave; ++w) t += red[w];
   return t;
 }
 
 // Sum of squares of the finite gradients (float64; a float32 square is exact
 // in float64), one partial per work-group; non-finite elements set found_inf.
 template <int GT, bool VEC>
-__global__ __launch_bounds__(kThreads) void norm_kernel(const void* __restrict__ g, int64_t n,
-                                                        amp_scaler_state* __restrict__ st,
-                                                        double* __restrict__ partial) {
-  __shared__ double red[kThreads / kWave];
+__global__ __launch_bounds__(kNormThreads) void norm_kernel(const void* __restrict__ g, int64_t n,
+                                                            amp_scaler_state* __restrict__ st,
+                                                            double* __restrict__ partial) {
+  __shared__ double red[kNormThreads / kWave];
   __shared__ uint32_t bad_any;
   if (threadIdx.x == 0) bad_any = 0;
-  const int64_t tid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  const int64_t nthr = static_cast<int64_t>(gridDim.x) * kThreads;
-  double acc = 0.0;
+  const int64_t tid = static_cast<int64_t>(blockIdx.x) * kNormThreads + threadIdx.x;
+  const int64_t nthr = static_cast<int64_t>(gridDim.x) * kNormThreads;
+  double accs[4] = {0.0, 0.0, 0.0, 0.0};   // independent chains, summed in a fixed order
   uint32_t bad = 0;
-  auto add = [&](float x) {
+  auto add = [&](float x, int c) {
     const uint32_t fin = static_cast<uint32_t>((fbits(x) & 0x7f800000u) != 0x7f800000u);
     bad |= fin ^ 1u;
     const double d = fin ? static_cast<double>(x) : 0.0;
-    acc = __builtin_fma(d, d, acc);
+    accs[c] = __builtin_fma(d, d, accs[c]);
   };
   int64_t done = 0;
   if constexpr (VEC) {
+    // four independent 16-byte loads in flight per thread
     const int64_t nv = n / 8;
-    for (int64_t j = tid; j < nv; j += nthr) {
+    int64_t j = tid;
+    for (; j + 3 * nthr < nv; j += 4 * nthr) {
+      float x[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) widen8<GT>(g, j + u * nthr, x[u]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int q = 0; q < 8; ++q) add(x[u][q], q & 3);
+    }
+    for (; j < nv; j += nthr) {
       float x[8];
       widen8<GT>(g, j, x);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) add(x[q]);
+      for (int q = 0; q < 8; ++q) add(x[q], q & 3);
     }
     done = nv * 8;
   }
-  for (int64_t i = done + tid; i < n; i += nthr) add(grad_at<GT>(g, i));
+  for (int64_t i = done + tid; i < n; i += nthr) add(grad_at<GT>(g, i), 0);
   __syncthreads();
   if (bad) bad_any = 1u;
-  const double t = block_sum_f64(acc, red);
+  const double t = block_sum_f64<kNormThreads>((accs[0] + accs[1]) + (accs[2] + accs[3]), red);
   __syncthreads();
   if (threadIdx.x == 0) {
     partial[blockIdx.x] = t;
@@ -544,13 +558,13 @@ hipError_t launch_grad_norm_init(amp_grad_norm_state* ns, hipStream_t s) {
 hipError_t launch_grad_norm(const void* g, int gt, int64_t n, amp_scaler_state* st,
                             amp_grad_norm_state* ns, hipStream_t s) {
   const bool vec = aligned(g, 16);
-  int64_t nb = (n + 8 * kThreads - 1) / (8 * kThreads);
+  int64_t nb = (n + 8 * kNormThreads - 1) / (8 * kNormThreads);
   if (nb > AMP_NORM_PARTIALS) nb = AMP_NORM_PARTIALS;
   if (nb < 1) nb = 1;
   const dim3 grid(static_cast<unsigned>(nb));
 #define AMP_NORM(T)                                                                        \
-  if (vec) norm_kernel<T, true><<<grid, kThreads, 0, s>>>(g, n, st, ns->partial);           \
-  else norm_kernel<T, false><<<grid, kThreads, 0, s>>>(g, n, st, ns->partial);
+  if (vec) norm_kernel<T, true><<<grid, kNormThreads, 0, s>>>(g, n, st, ns->partial);       \
+  else norm_kernel<T, false><<<grid, kNormThreads, 0, s>>>(g, n, st, ns->partial);
   switch (gt) {
     case AMP_F32: AMP_NORM(AMP_F32) break;
     case AMP_BF16: AMP_NORM(AMP_BF16) break;

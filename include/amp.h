@@ -313,6 +313,23 @@ int amp_gelu_backward_f16(const void* dA16, const void* z16, int64_t n, void* dz
 /* out[c] = round16(fl32(sum_r x[r][c])) (sequential FP32 sum; bias grads). */
 int amp_colsum_f16(const void* x16, int64_t rows, int64_t cols, void* out16, void* stream);
 
+/* amp_mx_quantize -- MX block quantization of one GEMM operand.
+ * Source: itwiki "FP8 혼합 정밀도" (MX formats: one power-of-two scale per 32
+ * elements), gist 2.1 (MXFP4: 32-element blocks, UE8M0 scales), with the OCP
+ * microscaling conversion the page points to.
+ * x: [rows, cols] of xt in {F32, F16, BF16}, stride ldx; op = x (transpose 0)
+ *    or x^T (1), shape [R, K], K a multiple of 32, blocks along K.
+ * yt: AMP_E4M3 / AMP_E5M2 (q: [R, K] bytes) or AMP_E2M1X2 (q: [R, K/2], two
+ *    codes per byte, lower K in the low nibble).
+ * scales: UE8M0 codes [R, K/32]: e = floor(log2(block amax)) - emax (8, 15,
+ *    2 for E4M3, E5M2, E2M1) clamped to [-127, 127], stored as e + 127; 0 for
+ *    an all-zero block, 0xFF for a block holding inf/NaN (its elements are
+ *    then encoded unscaled).  Elements: x * 2^-e to the element format,
+ *    nearest-even, saturating.  q and scales rows are contiguous; q 16-byte
+ *    aligned. */
+int amp_mx_quantize(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
+                    int transpose, int yt, uint8_t* q, uint8_t* scales, void* stream);
+
 /* ---- gradient accumulation and global-norm clipping ----------------------
  * Page "혼합 정밀도 학습" (itwiki), section "FP16 학습 루프": the loop unscales
  * (unscale_) and only then clips the global gradient norm to max_norm = 1.0,

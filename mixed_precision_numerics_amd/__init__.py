@@ -25,7 +25,7 @@ __all__ = [
     "amp_nvfp4_quantize", "amp_bias_gelu_f16", "amp_softmax_xent_f16", "amp_gelu_backward_f16",
     "amp_colsum_f16", "amp_grad_accumulate", "amp_grad_norm_init", "amp_grad_norm_accumulate",
     "amp_clip_coefficient", "amp_optimizer_step_ex", "NORM_STATE_BYTES", "NORM_PARTIALS",
-    "amp_cast_current_scaling",
+    "amp_cast_current_scaling", "amp_mx_quantize", "GEMM_MX",
 ]
 
 F32, F16, BF16, E4M3, E5M2, E2M1X2 = 0, 1, 2, 3, 4, 5
@@ -36,6 +36,7 @@ ROUND_RNE, ROUND_SR = 0, 1
 AMAX_MAX, AMAX_MOST_RECENT = 0, 1
 OPT_SKIP_CHECK = 1
 GEMM_FP8_NATIVE = 1
+GEMM_MX = 2
 
 # Device-resident state layouts (mirror the C structs; for reading back).
 SCALER_STATE_DTYPE = np.dtype([("scale", "<f4"), ("growth_tracker", "<i4"),
@@ -91,6 +92,7 @@ _SIGS = {
     "amp_check_overflow": ([_P, _I, _I64, _P, _P], _I),
     "amp_optimizer_step_ex": ([_P, _P, _P, _P, _I, _P, _I, _I64, _P, _P, _P, _I, _P], _I),
     "amp_grad_accumulate": ([_P, _P, _I, _I64, _I, _P], _I),
+    "amp_mx_quantize": ([_P, _I, _I64, _I64, _I64, _I, _I, _P, _P, _P], _I),
     "amp_cast_current_scaling": ([_P, _I, _I64, _I64, _I64, _P, _I, _I64, _P, _I64, _P, _P, _P],
                                  _I),
     "amp_grad_norm_init": ([_P, _P], _I),
@@ -215,6 +217,12 @@ def amp_cast_current_scaling(x, xt, rows, cols, ldx, y, yt, ldy, y_t, ldy_t,
     _check("amp_cast_current_scaling", load().amp_cast_current_scaling(
         _ptr(x), xt, rows, cols, ldx, _ptr(y), yt, ldy, _ptr(y_t), ldy_t, ctypes.byref(r),
         _ptr(d_meta), _stream(stream)))
+
+
+def amp_mx_quantize(x, xt, rows, cols, ldx, transpose, yt, q, scales, stream=None):
+    _check("amp_mx_quantize", load().amp_mx_quantize(_ptr(x), xt, rows, cols, ldx,
+                                                     int(transpose), yt, _ptr(q), _ptr(scales),
+                                                     _stream(stream)))
 
 
 def amp_grad_accumulate(acc, grads, gt, n, first, stream=None):

@@ -196,6 +196,20 @@ int amp_optimizer_step(float* master, float* m, float* v, const void* grads, int
                                stream);
 }
 
+int amp_mx_quantize(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
+                    int transpose, int yt, uint8_t* q, uint8_t* scales, void* stream) {
+  if (rows < 0 || cols < 0 || ldx < cols) return AMP_EINVAL;
+  if (!is_cast_in(xt)) return AMP_EUNSUPPORTED;
+  if (yt != AMP_E4M3 && yt != AMP_E5M2 && yt != AMP_E2M1X2) return AMP_EUNSUPPORTED;
+  const int64_t K = transpose ? rows : cols;
+  if (K % 32) return AMP_EINVAL;
+  if (rows == 0 || cols == 0) return AMP_OK;
+  if (!x || !q || !scales || !amp::aligned(q, 16)) return AMP_EINVAL;
+  if (int st = check_device()) return st;
+  return hip_status(amp::launch_mx_quantize(x, xt, rows, cols, ldx, transpose ? 1 : 0, yt, q,
+                                            scales, static_cast<hipStream_t>(stream)));
+}
+
 int amp_grad_accumulate(float* acc, const void* grads, int gt, int64_t n, int first,
                         void* stream) {
   if (n < 0) return AMP_EINVAL;

@@ -94,6 +94,8 @@ hipError_t launch_nvfp4_quantize(const void* x, int xt, int64_t rows, int64_t co
                                  uint64_t rht_seed, int rnd, uint64_t sr_seed, uint8_t* q,
                                  uint8_t* scales, float* d_tensor, hipStream_t s);
 
+hipError_t launch_mx_quantize(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
+                              int transpose, int yt, uint8_t* q, uint8_t* scales, hipStream_t s);
 hipError_t launch_bias_gelu(const float* acc, int64_t rows, int64_t cols, const void* b16,
                             void* z16, void* a16, hipStream_t s);
 hipError_t launch_softmax_xent(const void* logits16, const int32_t* labels, int64_t rows,

@@ -114,9 +114,8 @@ __device__ __forceinline__ uint32_t e2m1_rne(float y) {
   cn = cn > 7u ? 7u : cn;
   // a < 1: midpoints 0.25 (tie to 0) and 0.75 (tie to 1)
   const uint32_t cs = static_cast<uint32_t>(a > 0.25f) + static_cast<uint32_t>(a >= 0.75f);
-  uint32_t c = b >= 0x3f800000u ? cn : cs;
-  c = b > 0x7f800000u ? 0u : c;             // NaN -> 0 (E2M1 has no NaN)
-  return c | ((fbits(y) >> 28) & 0x8u);
+  const uint32_t c = (b >= 0x3f800000u ? cn : cs) | ((fbits(y) >> 28) & 0x8u);
+  return b > 0x7f800000u ? 0u : c;          // NaN -> +0 (E2M1 has no NaN)
 }
 
 // Stochastic rounding with u in [0, 1): round the magnitude up iff u < frac,
@@ -133,8 +132,8 @@ __device__ __forceinline__ uint32_t e2m1_sr(float y, float u) {
   const uint32_t lo = nrm ? lo_n : lo_s;
   const float frac = nrm ? frac_n : frac_s;
   const uint32_t up = static_cast<uint32_t>(lo < 7u) & static_cast<uint32_t>(u < frac);
-  const uint32_t c = (fbits(y) & 0x7fffffffu) > 0x7f800000u ? 0u : lo + up;   // NaN -> 0
-  return c | ((fbits(y) >> 28) & 0x8u);
+  const uint32_t c = (lo + up) | ((fbits(y) >> 28) & 0x8u);
+  return (fbits(y) & 0x7fffffffu) > 0x7f800000u ? 0u : c;   // NaN -> +0
 }
 
 __device__ __forceinline__ float e2m1_to_f32(uint32_t c) {

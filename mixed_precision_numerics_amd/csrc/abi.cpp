@@ -114,13 +114,21 @@ int amp_gemm_ex(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A
                 const float* d_alphaB, void* C, int ct, int64_t ldc,
                 const amp_block_scales* bsA, const amp_block_scales* bsB, int flags,
                 void* stream) {
-  if (flags & ~AMP_GEMM_FP8_NATIVE) return AMP_EINVAL;
+  if (flags & ~(AMP_GEMM_FP8_NATIVE | AMP_GEMM_MX)) return AMP_EINVAL;
   if (M < 0 || N < 0 || K < 0) return AMP_EINVAL;
   if ((opA != AMP_OP_N && opA != AMP_OP_T) || (opB != AMP_OP_N && opB != AMP_OP_T))
     return AMP_EINVAL;
   if (ct != AMP_F32 && ct != AMP_F16 && ct != AMP_BF16) return AMP_EUNSUPPORTED;
+  const bool mx = (flags & AMP_GEMM_MX) != 0;
   const bool nvfp4 = at == AMP_E2M1X2 || bt == AMP_E2M1X2;
-  if (nvfp4) {
+  if (mx) {
+    const bool fp4 = at == AMP_E2M1X2 && bt == AMP_E2M1X2;
+    if (!fp4 && !(is_fp8(at) && is_fp8(bt))) return AMP_EUNSUPPORTED;
+    if (opA != AMP_OP_N || opB != AMP_OP_T || (flags & AMP_GEMM_FP8_NATIVE)) return AMP_EINVAL;
+    if (!bsA || !bsB || !bsA->scales || !bsB->scales || bsA->block2d || bsB->block2d)
+      return AMP_EINVAL;
+    if (K % 32 != 0) return AMP_EINVAL;
+  } else if (nvfp4) {
     if (at != bt || opA != AMP_OP_N || opB != AMP_OP_T) return AMP_EUNSUPPORTED;
     if (!bsA || !bsB || !bsA->scales || !bsB->scales) return AMP_EINVAL;
     if (K % 16 != 0) return AMP_EINVAL;
@@ -139,13 +147,13 @@ int amp_gemm_ex(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A
     const int64_t kA = nvfp4 ? K / 2 : K, kB = nvfp4 ? K / 2 : K;
     if (opA == AMP_OP_N ? lda < kA : lda < M) return AMP_EINVAL;
     if (opB == AMP_OP_T ? ldb < kB : ldb < N) return AMP_EINVAL;
-    if (nvfp4 && (bsA->ld < (bsA->block2d ? K / 16 : K / 16) || bsB->ld < K / 16)) return AMP_EINVAL;
-    if (nvfp4 && ((bsA->block2d && M % 16) || (bsB->block2d && N % 16))) return AMP_EINVAL;
+    if (mx && (bsA->ld < K / 32 || bsB->ld < K / 32)) return AMP_EINVAL;
+    if (!mx && nvfp4 && (bsA->ld < K / 16 || bsB->ld < K / 16)) return AMP_EINVAL;
+    if (!mx && nvfp4 && ((bsA->block2d && M % 16) || (bsB->block2d && N % 16))) return AMP_EINVAL;
   }
   if (int st = check_device()) return st;
   return hip_status(amp::launch_gemm(opA, opB, M, N, K, A, at, lda, d_alphaA, B, bt, ldb,
-                                     d_alphaB, C, ct, ldc, bsA, bsB,
-                                     (flags & AMP_GEMM_FP8_NATIVE) != 0,
+                                     d_alphaB, C, ct, ldc, bsA, bsB, flags,
                                      static_cast<hipStream_t>(stream)));
 }
 

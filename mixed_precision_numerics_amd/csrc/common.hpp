@@ -88,7 +88,7 @@ hipError_t launch_gemm(int opA, int opB, int64_t M, int64_t N, int64_t K, const 
                        int at, int64_t lda, const float* alphaA, const void* B, int bt,
                        int64_t ldb, const float* alphaB, void* C, int ct, int64_t ldc,
                        const amp_block_scales* bsA, const amp_block_scales* bsB,
-                       bool fp8_native, hipStream_t s);
+                       int flags, hipStream_t s);
 hipError_t launch_nvfp4_quantize(const void* x, int xt, int64_t rows, int64_t cols,
                                  int64_t ldx, int transpose, int block2d, int rht,
                                  uint64_t rht_seed, int rnd, uint64_t sr_seed, uint8_t* q,

@@ -54,6 +54,8 @@ enum Path : int {
   kPF8Exact = 1,  // FP8 operands decoded to BF16 on the way to LDS, BF16 MFMA, BK = 64
   kPF8Native = 2, // FP8 operands in LDS, FP8 MFMA 32x32x64, BK = 128
   kPFP4 = 3,      // NVFP4 operands decoded (x block scale) to BF16, BF16 MFMA, BK = 64
+  kPMX8 = 4,      // MX, FP8 elements + UE8M0 scale per 32: block-scaled MFMA, BK = 128
+  kPMX4 = 5,      // MX, E2M1 elements + UE8M0 scale per 32: block-scaled MFMA, BK = 256
 };
 
 struct GemmArgs {
@@ -67,6 +69,7 @@ struct GemmArgs {
   const uint8_t* sB;
   int64_t ldsA, ldsB;
   int s2dA, s2dB;
+  int mx;          // block scales are UE8M0 per 32 (MX) instead of NVFP4's E4M3 per 16
 };
 
 __device__ __forceinline__ int swz(int row, int chunk) {
@@ -500,6 +503,18 @@ __device__ __forceinline__ uint32_t tr_addr(int lane, int c0, int b) {
   return static_cast<uint32_t>(k * 512 + chunk * 16 + 8 * (s & 1));
 }
 
+// Block-scaled MFMA with the scale byte chosen by `sel` (a constant after
+// unrolling; the instruction takes it as an immediate).
+template <int FA, int FB>
+__device__ __forceinline__ f32x16 mfma_scaled(i32x8 a, i32x8 b, f32x16 c, int sa, int sb, int sel) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 0, sa, 0, sb);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 1, sa, 1, sb);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 2, sa, 2, sb);
+    default: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FA, FB, 3, sa, 3, sb);
+  }
+}
+
 // Scheduling hint for one K-slice: 16 MFMA, each followed by its share of
 // the R fragment reads of the next slice and of the V global loads issued in
 // this slice.
@@ -525,12 +540,13 @@ template <int AT, int BT, bool A_KC, bool B_KC, int PATH, int CT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
   static_assert((A_KC && B_KC) || PATH == kP16, "M/N-contiguous operands are 16-bit");
   __shared__ __align__(16) uint8_t smem[2][2][kOperandBytes];
-  constexpr bool kF8 = PATH == kPF8Native || PATH == kPF8Exact;
-  constexpr int BK = kF8 ? 128 : 64;
-  constexpr int EB = kF8 ? 1 : 2;
-  // fragment reads per step: K-slices of 16 (16-bit), 64 (FP8 native), or
-  // pairs of 16-slices (FP8 widened to BF16 in registers)
-  constexpr int NS = PATH == kPF8Native ? 2 : 4;
+  constexpr bool kF8 = PATH == kPF8Native || PATH == kPF8Exact || PATH == kPMX8;
+  constexpr bool kMX = PATH == kPMX8 || PATH == kPMX4;
+  constexpr int BK = PATH == kPMX4 ? 256 : (kF8 ? 128 : 64);     // K elements per step
+  constexpr int EB = kF8 || PATH == kPMX4 ? 1 : 2;                // row stride unit (bytes for FP4)
+  // fragment reads per step: K-slices of 16 (16-bit), 64 (FP8 native, MX),
+  // or pairs of 16-slices (FP8 widened to BF16 in registers)
+  constexpr int NS = PATH == kPF8Native || PATH == kPMX8 ? 2 : 4;
   const int64_t nbm = g.M / kBM, nbn = g.N / kBN;
   const int64_t total = nbm * nbn;
   int64_t tile = blockIdx.x;
@@ -591,7 +607,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
   const uint32_t gsw = static_cast<uint32_t>((l32 & 7) ^ (l32 >> 3));
   const uint32_t abase = static_cast<uint32_t>(wm * 128 + l32) * kRowBytes;
   const uint32_t bbase = static_cast<uint32_t>(wn * 128 + l32) * kRowBytes;
-  using Frag = typename std::conditional<PATH == kPF8Native, i32x8, u32x4>::type;
+  using Frag = typename std::conditional<PATH == kPF8Native || PATH == kPMX8, i32x8, u32x4>::type;
+  // MX: this lane's UE8M0 block scales of the step for its 4 rows of A and B
+  // (row wm*128 + mb*32 + l%32): 4 bytes (FP8, 4 blocks) or 8 (FP4, 8 blocks)
+  constexpr int kSW = PATH == kPMX4 ? 2 : 1;                       // scale dwords per row
+  uint32_t scA[4][kSW], scB[4][kSW], nscA[4][kSW], nscB[4][kSW];
+  auto load_scales = [&](int64_t kt, uint32_t (&a)[4][kSW], uint32_t (&b)[4][kSW]) {
+    if constexpr (kMX) {
+      const int64_t kc = kt < nk ? kt : nk - 1;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const uint8_t* pa = g.sA + (m0 + wm * 128 + mb * 32 + (lane & 31)) * g.ldsA + kc * 4 * kSW;
+        const uint8_t* pb = g.sB + (n0 + wn * 128 + mb * 32 + (lane & 31)) * g.ldsB + kc * 4 * kSW;
+        if constexpr (kSW == 2) {
+          const u32x2 va = *reinterpret_cast<const u32x2*>(pa);
+          const u32x2 vb = *reinterpret_cast<const u32x2*>(pb);
+          a[mb][0] = va[0]; a[mb][kSW - 1] = va[1];
+          b[mb][0] = vb[0]; b[mb][kSW - 1] = vb[1];
+        } else {
+          a[mb][0] = *reinterpret_cast<const uint32_t*>(pa);
+          b[mb][0] = *reinterpret_cast<const uint32_t*>(pb);
+        }
+      }
+    }
+  };
   Frag fa[2][4], fb[2][4];
   uint32_t tra[4], trb[4];
 #pragma unroll
@@ -602,16 +641,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
   auto frag = [&](const uint8_t* st, int ks, Frag (&a)[4], Frag (&b)[4]) {
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      if constexpr (PATH == kPF8Native) {
-        // 32 bytes of K per lane: logical chunks 4ks + 2h and 4ks + 2h + 1
-        const uint32_t y = (static_cast<uint32_t>(2 * h) ^ gsw) & 7u;
+      if constexpr (PATH == kPF8Native || PATH == kPMX8) {
+        // 32 bytes of K per lane.  Native FP8: logical chunks 4ks + 2h and
+        // 4ks + 2h + 1 (any K order shared by A and B will do).  MX: the
+        // instruction's K block 0 is made of bytes 0-15 of both lane halves
+        // and block 1 of bytes 16-31, so lane half h takes chunks 4ks + h
+        // (16 elements of MX block 2ks) and 4ks + 2 + h (of block 2ks + 1)
+        constexpr bool kMXO = PATH == kPMX8;
+        const uint32_t y = (static_cast<uint32_t>(kMXO ? h : 2 * h) ^ gsw) & 7u;
         const uint32_t c0 = static_cast<uint32_t>(4 * ks) ^ static_cast<uint32_t>(4 * (mb & 1));
+        const uint32_t c1 = c0 + (kMXO ? 2u : 1u);
         const uint8_t* pa = st + abase + mb * 32 * kRowBytes;
         const uint8_t* pb = st + kOperandBytes + bbase + mb * 32 * kRowBytes;
         const u32x4 al = *reinterpret_cast<const u32x4*>(pa + ((y ^ c0) << 4));
-        const u32x4 ah = *reinterpret_cast<const u32x4*>(pa + ((y ^ (c0 + 1)) << 4));
+        const u32x4 ah = *reinterpret_cast<const u32x4*>(pa + ((y ^ c1) << 4));
         const u32x4 bl = *reinterpret_cast<const u32x4*>(pb + ((y ^ c0) << 4));
-        const u32x4 bh = *reinterpret_cast<const u32x4*>(pb + ((y ^ (c0 + 1)) << 4));
+        const u32x4 bh = *reinterpret_cast<const u32x4*>(pb + ((y ^ c1) << 4));
         a[mb] = i32x8{(int)al[0], (int)al[1], (int)al[2], (int)al[3], (int)ah[0], (int)ah[1], (int)ah[2], (int)ah[3]};
         b[mb] = i32x8{(int)bl[0], (int)bl[1], (int)bl[2], (int)bl[3], (int)bh[0], (int)bh[1], (int)bh[2], (int)bh[3]};
       } else {
@@ -632,11 +677,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
   };
   load_part(0, 0);
   load_part(0, 1);
+  load_scales(0, scA, scB);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   frag(smem[0][0], 0, fa[0], fb[0]);
   for (int64_t kt = 0; kt < nk; ++kt) {
     const uint8_t* st = smem[kt & 1][0];
+    load_scales(kt + 1, nscA, nscB);
 #pragma unroll
     for (int ks = 0; ks < NS; ++ks) {
       const int cur = ks & 1;
@@ -690,6 +737,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
             constexpr int fb_ = BT == AMP_E4M3 ? 0 : 1;
             acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fa[cur][mb], fb[cur][nb], acc[mb][nb],
                                                                           fa_, fb_, 0, 127, 0, 127);
+          } else if constexpr (PATH == kPMX8) {
+            // lane l covers K block 2ks + l/32 of the step: its scale byte is
+            // byte 2ks of (scale dword >> 8*(l/32))
+            constexpr int fa_ = AT == AMP_E4M3 ? 0 : 1;
+            constexpr int fb_ = BT == AMP_E4M3 ? 0 : 1;
+            const int sa = static_cast<int>(scA[mb][0] >> (8 * h));
+            const int sb = static_cast<int>(scB[nb][0] >> (8 * h));
+            acc[mb][nb] = mfma_scaled<fa_, fb_>(fa[cur][mb], fb[cur][nb], acc[mb][nb], sa, sb, 2 * ks);
+          } else if constexpr (PATH == kPMX4) {
+            // E2M1 (format 4): 16 bytes = 32 K per lane in the low 4 dwords
+            const u32x4 a4 = fa[cur][mb], b4 = fb[cur][nb];
+            const i32x8 av = i32x8{(int)a4[0], (int)a4[1], (int)a4[2], (int)a4[3], 0, 0, 0, 0};
+            const i32x8 bv = i32x8{(int)b4[0], (int)b4[1], (int)b4[2], (int)b4[3], 0, 0, 0, 0};
+            const int sa = static_cast<int>(scA[mb][ks >> 1] >> (8 * h));
+            const int sb = static_cast<int>(scB[nb][ks >> 1] >> (8 * h));
+            acc[mb][nb] = mfma_scaled<4, 4>(av, bv, acc[mb][nb], sa, sb, 2 * (ks & 1));
           } else if constexpr (AT == AMP_F16) {
             acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, fa[cur][mb]),
                                                                  __builtin_bit_cast(f16x8_t, fb[cur][nb]),
@@ -702,11 +765,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
         }
       // 16 MFMA per slice with the next slice's fragment reads spread evenly
       // (8 reads; 16 for FP8; two per transposed fragment)
-      constexpr int kReads = PATH == kPF8Native ? 16 : (A_KC ? 4 : 8) + (B_KC ? 4 : 8);
+      constexpr int kReads = PATH == kPF8Native || PATH == kPMX8 ? 16 : (A_KC ? 4 : 8) + (B_KC ? 4 : 8);
       if constexpr (PATH != kPF8Exact) {
         if (kSplit && ks < 2) sched_slice<0, kReads, 8>();
         else sched_slice<0, kReads, 0>();
       }
+    }
+    if constexpr (kMX) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int w = 0; w < kSW; ++w) {
+          scA[mb][w] = nscA[mb][w];
+          scB[mb][w] = nscB[mb][w];
+        }
     }
   }
   const float alpha = (g.alphaA ? *g.alphaA : 1.0f) * (g.alphaB ? *g.alphaB : 1.0f);
@@ -736,15 +808,22 @@ __device__ __forceinline__ float load_elem(const void* X, int64_t idx) {
 
 template <int ET>
 __device__ __forceinline__ float operand(const void* X, int64_t ld, bool kc, int64_t r, int64_t k,
-                                         const uint8_t* sc, int64_t lds_, int s2d) {
+                                         const uint8_t* sc, int64_t lds_, int s2d, int mx) {
+  float v;
   if constexpr (ET == AMP_E2M1X2) {
     const uint8_t byte = static_cast<const uint8_t*>(X)[r * ld + k / 2];
-    const float e = e2m1_to_f32((k & 1) ? (byte >> 4) : (byte & 0xf));
-    const float S = e4m3_to_f32(sc[(s2d ? r / 16 : r) * lds_ + k / 16]);
-    return e * S;
+    v = e2m1_to_f32((k & 1) ? (byte >> 4) : (byte & 0xf));
   } else {
-    return load_elem<ET>(X, kc ? r * ld + k : k * ld + r);
+    v = load_elem<ET>(X, kc ? r * ld + k : k * ld + r);
   }
+  if (mx) {
+    // UE8M0 per 32 along K: 2^(code - 127), 0xFF = NaN
+    const uint32_t c = sc[r * lds_ + k / 32];
+    const float S = c == 0xffu ? __builtin_nanf("") : __builtin_ldexpf(1.0f, static_cast<int>(c) - 127);
+    return v * S;
+  }
+  if constexpr (ET == AMP_E2M1X2) return v * e4m3_to_f32(sc[(s2d ? r / 16 : r) * lds_ + k / 16]);
+  return v;
 }
 
 template <int AT, int BT, int CT>
@@ -754,8 +833,8 @@ __global__ __launch_bounds__(256) void gemm_generic(GemmArgs g, int a_kc, int b_
   if (row >= g.M || col >= g.N) return;
   float acc = 0.0f;
   for (int64_t k = 0; k < g.K; ++k) {
-    const float a = operand<AT>(g.A, g.lda, a_kc, row, k, g.sA, g.ldsA, g.s2dA);
-    const float b = operand<BT>(g.B, g.ldb, b_kc, col, k, g.sB, g.ldsB, g.s2dB);
+    const float a = operand<AT>(g.A, g.lda, a_kc, row, k, g.sA, g.ldsA, g.s2dA, g.mx);
+    const float b = operand<BT>(g.B, g.ldb, b_kc, col, k, g.sB, g.ldsB, g.s2dB, g.mx);
     acc = __builtin_fmaf(a, b, acc);
   }
   const float alpha = (g.alphaA ? *g.alphaA : 1.0f) * (g.alphaB ? *g.alphaB : 1.0f);
@@ -832,6 +911,35 @@ hipError_t launch_f8(const GemmArgs& g, bool fast, bool native, int ct, hipStrea
   return launch_mfma<AT, BT, true, true, kPF8Exact>(g, ct, s);
 }
 
+// MX operands (both K-contiguous): the block-scaled matrix-core path for full
+// tiles with aligned rows and scale rows, the generic kernel otherwise.
+template <int AT, int BT, int PATH>
+hipError_t launch_mx_t(const GemmArgs& g, int ct, hipStream_t s) {
+  constexpr int64_t BK = PATH == kPMX4 ? 256 : 128;
+  constexpr int64_t kSB = PATH == kPMX4 ? 8 : 4;           // scale bytes per row per step
+  const bool fast = g.M % kBM == 0 && g.N % kBN == 0 && g.K % BK == 0 && aligned(g.A, 16) &&
+                    aligned(g.B, 16) && g.lda % 16 == 0 && g.ldb % 16 == 0 &&
+                    g.lda * kBM < (int64_t(1) << 31) && g.ldb * kBN < (int64_t(1) << 31) &&
+                    aligned(g.sA, kSB) && aligned(g.sB, kSB) && g.ldsA % kSB == 0 &&
+                    g.ldsB % kSB == 0;
+  if (!fast) return launch_generic<AT, BT>(g, true, true, ct, s);
+  const dim3 grid(static_cast<unsigned>((g.M / kBM) * (g.N / kBN)));
+  switch (ct) {
+    case AMP_F32: gemm_mfma_d2l<AT, BT, true, true, PATH, AMP_F32><<<grid, kThreads, 0, s>>>(g); break;
+    case AMP_BF16: gemm_mfma_d2l<AT, BT, true, true, PATH, AMP_BF16><<<grid, kThreads, 0, s>>>(g); break;
+    default: gemm_mfma_d2l<AT, BT, true, true, PATH, AMP_F16><<<grid, kThreads, 0, s>>>(g); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_mx(const GemmArgs& g, int at, int bt, int ct, hipStream_t s) {
+  if (at == AMP_E2M1X2) return launch_mx_t<AMP_E2M1X2, AMP_E2M1X2, kPMX4>(g, ct, s);
+  if (at == AMP_E4M3 && bt == AMP_E4M3) return launch_mx_t<AMP_E4M3, AMP_E4M3, kPMX8>(g, ct, s);
+  if (at == AMP_E4M3) return launch_mx_t<AMP_E4M3, AMP_E5M2, kPMX8>(g, ct, s);
+  if (bt == AMP_E4M3) return launch_mx_t<AMP_E5M2, AMP_E4M3, kPMX8>(g, ct, s);
+  return launch_mx_t<AMP_E5M2, AMP_E5M2, kPMX8>(g, ct, s);
+}
+
 }  // namespace
 
 // fp8_native: use the FP8 matrix-core dot product (reduced internal precision
@@ -840,11 +948,14 @@ hipError_t launch_gemm(int opA, int opB, int64_t M, int64_t N, int64_t K, const 
                        int at, int64_t lda, const float* alphaA, const void* B, int bt,
                        int64_t ldb, const float* alphaB, void* C, int ct, int64_t ldc,
                        const amp_block_scales* bsA, const amp_block_scales* bsB,
-                       bool fp8_native, hipStream_t s) {
+                       int flags, hipStream_t s) {
+  const bool fp8_native = (flags & AMP_GEMM_FP8_NATIVE) != 0;
+  const bool mx = (flags & AMP_GEMM_MX) != 0;
   GemmArgs g{A, B, C, M, N, K, lda, ldb, ldc, alphaA, alphaB,
              bsA ? bsA->scales : nullptr, bsB ? bsB->scales : nullptr,
              bsA ? bsA->ld : 0, bsB ? bsB->ld : 0, bsA ? bsA->block2d : 0,
-             bsB ? bsB->block2d : 0};
+             bsB ? bsB->block2d : 0, mx ? 1 : 0};
+  if (mx) return launch_mx(g, at, bt, ct, s);
   const bool a_kc = opA == AMP_OP_N, b_kc = opB == AMP_OP_T;
   if (at == AMP_E2M1X2) {
     const bool fast = aligned(A, 16) && aligned(B, 16) && lda % 16 == 0 && ldb % 16 == 0 &&

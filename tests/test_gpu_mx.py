@@ -47,3 +47,85 @@ def test_mx_quantize_bit_exact(xt, yt, transpose):
     got = host(q, np.uint8)[:qbytes].reshape(wq.shape)
     bad = np.argwhere(got != wq)
     assert bad.size == 0, (bad[:5], got[tuple(bad[0])], wq[tuple(bad[0])])
+
+
+def mx_operand(seed, rows, k, yt):
+    """Random MX operand: element codes and UE8M0 scales around 2^0."""
+    g = synth.rng(seed)
+    if yt == amp.E2M1X2:
+        q = g.integers(0, 256, size=(rows, k // 2), dtype=np.uint8)
+        codes = np.stack([q & 0xF, q >> 4], axis=2).reshape(rows, k)
+    else:
+        codes = g.integers(0, 256, size=(rows, k), dtype=np.uint8)
+        nan = 0x7F if yt == amp.E4M3 else None
+        fin = np.isfinite(F.decode(codes, YF[yt]))
+        codes = np.where(fin, codes, 0x38).astype(np.uint8)      # replace inf/NaN codes by 1.0
+        q = codes
+    sc = g.integers(120, 135, size=(rows, k // 32), dtype=np.uint8)
+    return q, codes.astype(np.uint8), sc
+
+
+def run_mx_gemm(M, N, K, at, bt, ct=amp.F32, seed=0):
+    qa, ca, sa = mx_operand(seed + 1, M, K, at)
+    qb, cb, sb = mx_operand(seed + 2, N, K, bt)
+    lda = K // 2 if at == amp.E2M1X2 else K
+    ldb = K // 2 if bt == amp.E2M1X2 else K
+    c = empty(M * N * 4)
+    sa_d, sb_d = dev(sa), dev(sb)
+    amp.amp_gemm_ex(amp.OP_N, amp.OP_T, M, N, K, dev(qa), at, lda, None, dev(qb), bt, ldb, None,
+                    c, ct, N, amp.BlockScales(sa_d.data_ptr(), K // 32, 0, 0),
+                    amp.BlockScales(sb_d.data_ptr(), K // 32, 0, 0), flags=amp.GEMM_MX)
+    A = OM.dequantize(ca, sa, YF[at])
+    B = OM.dequantize(cb, sb, YF[bt])
+    cref, bound = OG.reference(A, B.T)
+    return host(c, np.float32).reshape(M, N).astype(np.float64), cref, bound
+
+
+@pytest.mark.parametrize("M,N,K", [(512, 768, 512), (200, 100, 96)])
+def test_mxfp4_gemm_within_fp32_accumulation_bound(M, N, K):
+    """E2M1 x E2M1 with UE8M0 scales: full tiles on the block-scaled matrix
+    cores (products of E2M1 values are short, so the per-instruction sums are
+    exact), ragged shapes on the element-wise kernel: both within the FP32
+    accumulation bound."""
+    out, cref, bound = run_mx_gemm(M, N, K, amp.E2M1X2, amp.E2M1X2)
+    ok = OG.check_f32(out, cref, bound)
+    assert ok.all(), (np.argwhere(~ok)[:5], np.max(np.abs(out - cref) / np.maximum(bound, 1e-300)))
+
+
+@pytest.mark.parametrize("at,bt", [(amp.E4M3, amp.E4M3), (amp.E5M2, amp.E4M3)])
+def test_mxfp8_gemm_precision_report(at, bt):
+    """FP8 elements on the block-scaled matrix cores: the 64-term sums have the
+    reduced internal precision of the FP8 instruction (documented); assert
+    the measured bound and report how many outputs meet 1e-5 * sum|ab|."""
+    out, cref, bound = run_mx_gemm(512, 512, 1024, at, bt, seed=5)
+    rel = np.abs(out - cref) / np.maximum(bound, 1e-300)
+    frac = float(np.mean(rel <= OG.RTOL))
+    print(f"MXFP8 {at}x{bt}: max |err|/sum|ab| = {rel.max():.3g}, within 1e-5: {frac:.4f}")
+    assert rel.max() <= 2.0 ** -10
+
+
+def test_mxfp8_gemm_ragged_is_exact_route():
+    out, cref, bound = run_mx_gemm(100, 130, 64, amp.E4M3, amp.E5M2, seed=9)
+    assert OG.check_f32(out, cref, bound).all()
+
+
+def test_mx_quantize_then_gemm_matches_oracle_quantization():
+    """X [512 x 1024] and W [768 x 1024] (BF16) quantized to MXFP4 on the GPU,
+    multiplied on the block-scaled matrix cores; the oracle quantizes the same
+    inputs and forms the float64 product."""
+    M, N, K = 512, 768, 1024
+    xc = synth.outlier_bf16_codes(81, (M, K))
+    wc = synth.to_bf16_codes(synth.normal_f32(82, (N, K), 0.05))
+    qx, sx = empty(M * K // 2), empty(M * K // 32)
+    qw, sw = empty(N * K // 2), empty(N * K // 32)
+    amp.amp_mx_quantize(dev(xc), amp.BF16, M, K, K, 0, amp.E2M1X2, qx, sx)
+    amp.amp_mx_quantize(dev(wc), amp.BF16, N, K, K, 0, amp.E2M1X2, qw, sw)
+    c = empty(M * N * 2)
+    amp.amp_gemm_ex(amp.OP_N, amp.OP_T, M, N, K, qx, amp.E2M1X2, K // 2, None, qw, amp.E2M1X2,
+                    K // 2, None, c, amp.BF16, N, amp.BlockScales(sx.data_ptr(), K // 32, 0, 0),
+                    amp.BlockScales(sw.data_ptr(), K // 32, 0, 0), flags=amp.GEMM_MX)
+    cx, scx = OM.quantize(F.decode(xc, F.BF16), F.E2M1)
+    cw, scw = OM.quantize(F.decode(wc, F.BF16), F.E2M1)
+    cref, bound = OG.reference(OM.dequantize(cx, scx, F.E2M1), OM.dequantize(cw, scw, F.E2M1).T)
+    ok = OG.check_rounded(host(c, np.uint16).reshape(M, N), F.BF16, cref, bound)
+    assert ok.all(), np.argwhere(~ok)[:5]

@@ -18,7 +18,9 @@ Also measured in the same run (reported under "components"):
   * the scaled casts (BF16 -> E4M3 flat 2^31, BF16 -> E5M2 [8192 x 28672]
     with its transposed copy), and delayed against current scaling;
   * the global-norm pass (2^31 FP16 gradients) and FP32 gradient
-    accumulation.
+    accumulation;
+  * MXFP4 and MXFP8 GEMMs of the FFN up projection on the block-scaled
+    matrix cores, with their quantizer.
 The CPU oracle is timed on a bounded sample of the optimizer workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-components]
@@ -376,6 +378,41 @@ def clip_workload(torch, amp):
                                             "frac": round(10 * na / a_ms / 1e6 / HBM_PEAK_GBS, 4)}}
 
 
+def mx_workload(torch, amp):
+    """MX GEMMs on the block-scaled matrix cores at the FFN up projection
+    (8192 x 28672 x 4096, K-contiguous operands as the forward pass has them),
+    plus the MX quantizer of the activation: MXFP4 (E2M1) and MXFP8 (E4M3)."""
+    T, I, O = 8192, 4096, 28672
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    X = torch.randn(T, I, device="cuda", generator=gen).to(torch.bfloat16)
+    W = (torch.randn(O, I, device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
+    out = {}
+    flops = 2 * T * O * I
+    for name, yt, peak in (("mxfp4", amp.E2M1X2, FP4_PEAK_TFLOPS), ("mxfp8", amp.E4M3, FP8_PEAK_TFLOPS)):
+        div = 2 if yt == amp.E2M1X2 else 1
+        qx = torch.empty(T * I // div, device="cuda", dtype=torch.uint8)
+        qw = torch.empty(O * I // div, device="cuda", dtype=torch.uint8)
+        sx = torch.empty(T * I // 32, device="cuda", dtype=torch.uint8)
+        sw = torch.empty(O * I // 32, device="cuda", dtype=torch.uint8)
+        q_ms = _timed(torch, lambda: amp.amp_mx_quantize(X, amp.BF16, T, I, I, 0, yt, qx, sx), 5)
+        amp.amp_mx_quantize(W, amp.BF16, O, I, I, 0, yt, qw, sw)
+        Y = torch.empty(T, O, device="cuda", dtype=torch.bfloat16)
+        bsx = amp.BlockScales(sx.data_ptr(), I // 32, 0, 0)
+        bsw = amp.BlockScales(sw.data_ptr(), I // 32, 0, 0)
+        g_ms = _timed(torch, lambda: amp.amp_gemm_ex(amp.OP_N, amp.OP_T, T, O, I, qx, yt, I // div,
+                                                     None, qw, yt, I // div, None, Y, amp.BF16, O,
+                                                     bsx, bsw, flags=amp.GEMM_MX), 10)
+        tf = flops / g_ms / 1e9
+        qbytes = T * I * (2 + 1.0 / div + 1.0 / 32)
+        out[name] = {"gemm_ms": round(g_ms, 4), "gemm_tflops": round(tf, 1), "peak_tflops": peak,
+                     "frac": round(tf / peak, 4), "quantize_ms": round(q_ms, 4),
+                     "quantize_gbs": round(qbytes / q_ms / 1e6, 1)}
+        del qx, qw, sx, sw, Y
+    del X, W
+    torch.cuda.empty_cache()
+    return out
+
+
 def measured_traffic():
     """HBM bytes per launch of the apply kernel, from the committed rocprofv3
     counter summary, or None when the kernel sources changed since then."""
@@ -457,6 +494,8 @@ def main():
         comps["cast_t"] = cast_t_workload(torch, amp)
         log("components: NVFP4 weight-gradient quantize + GEMM")
         comps["nvfp4_wgrad"] = nvfp4_workload(torch, amp)
+        log("components: MX GEMMs (block-scaled matrix cores)")
+        comps["mx"] = mx_workload(torch, amp)
         log("components: delayed vs current scaling casts")
         comps["scaling"] = scaling_workload(torch, amp)
         log("components: gradient norm and accumulation")

@@ -43,6 +43,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = 256, kBN = 256, kThreads = 256;
 constexpr int kRowBytes = 128;                       // LDS bytes per tile row per K-step
@@ -607,7 +608,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
   const uint32_t gsw = static_cast<uint32_t>((l32 & 7) ^ (l32 >> 3));
   const uint32_t abase = static_cast<uint32_t>(wm * 128 + l32) * kRowBytes;
   const uint32_t bbase = static_cast<uint32_t>(wn * 128 + l32) * kRowBytes;
-  using Frag = typename std::conditional<PATH == kPF8Native || PATH == kPMX8, i32x8, u32x4>::type;
+  // 8-register operands for the f8f6f4 instruction; an E2M1 operand uses the
+  // low 4 registers only (the high half is left undefined)
+  using Frag = typename std::conditional<PATH == kPF8Native || PATH == kPMX8 || PATH == kPMX4,
+                                         i32x8, u32x4>::type;
   // MX: this lane's UE8M0 block scales of the step for its 4 rows of A and B
   // (row wm*128 + mb*32 + l%32): 4 bytes (FP8, 4 blocks) or 8 (FP4, 8 blocks)
   constexpr int kSW = PATH == kPMX4 ? 2 : 1;                       // scale dwords per row
@@ -659,6 +663,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
         const u32x4 bh = *reinterpret_cast<const u32x4*>(pb + ((y ^ c1) << 4));
         a[mb] = i32x8{(int)al[0], (int)al[1], (int)al[2], (int)al[3], (int)ah[0], (int)ah[1], (int)ah[2], (int)ah[3]};
         b[mb] = i32x8{(int)bl[0], (int)bl[1], (int)bl[2], (int)bl[3], (int)bh[0], (int)bh[1], (int)bh[2], (int)bh[3]};
+      } else if constexpr (PATH == kPMX4) {
+        // 16 bytes = 32 E2M1 of K per lane: logical chunk 2ks + h (MX block 2ks + h)
+        const uint32_t y = (static_cast<uint32_t>(h) ^ gsw) & 7u;
+        const uint32_t c = static_cast<uint32_t>(2 * ks) ^ static_cast<uint32_t>(4 * (mb & 1));
+        const i32x4 av = *reinterpret_cast<const i32x4*>(st + abase + mb * 32 * kRowBytes + ((y ^ c) << 4));
+        const i32x4 bv = *reinterpret_cast<const i32x4*>(st + kOperandBytes + bbase + mb * 32 * kRowBytes +
+                                                         ((y ^ c) << 4));
+        a[mb] = __builtin_shufflevector(av, av, 0, 1, 2, 3, -1, -1, -1, -1);
+        b[mb] = __builtin_shufflevector(bv, bv, 0, 1, 2, 3, -1, -1, -1, -1);
       } else {
         // 16 bytes of K per lane: logical chunk 2ks + h
         const uint32_t y = (static_cast<uint32_t>(h) ^ gsw) & 7u;
@@ -747,9 +760,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
             acc[mb][nb] = mfma_scaled<fa_, fb_>(fa[cur][mb], fb[cur][nb], acc[mb][nb], sa, sb, 2 * ks);
           } else if constexpr (PATH == kPMX4) {
             // E2M1 (format 4): 16 bytes = 32 K per lane in the low 4 dwords
-            const u32x4 a4 = fa[cur][mb], b4 = fb[cur][nb];
-            const i32x8 av = i32x8{(int)a4[0], (int)a4[1], (int)a4[2], (int)a4[3], 0, 0, 0, 0};
-            const i32x8 bv = i32x8{(int)b4[0], (int)b4[1], (int)b4[2], (int)b4[3], 0, 0, 0, 0};
+            const i32x8 av = fa[cur][mb], bv = fb[cur][nb];
             const int sa = static_cast<int>(scA[mb][ks >> 1] >> (8 * h));
             const int sb = static_cast<int>(scB[nb][ks >> 1] >> (8 * h));
             acc[mb][nb] = mfma_scaled<4, 4>(av, bv, acc[mb][nb], sa, sb, 2 * (ks & 1));

@@ -32,6 +32,9 @@ philox    Philox4x32-10 counter-based generator
 hadamard  16-point random Hadamard transform
 nvfp4     NVFP4 two-level quantizer (1x16 / 16x16 blocks, RNE / SR)
 mlp       the tiny FP16 AMP training step (512->2048->GELU->10)
+clip      FP32 gradient accumulation, global norm, clip coefficient
+mx        MX block formats (UE8M0 scale per 32 elements)
+blockwise fine-grained FP8 scaling (1x128 tiles, 128x128 blocks) and GEMM
 
 Functions whose correctness cannot be pinned against anything outside the
 oracle say "parity unpinned" in their docstring.

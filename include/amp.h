@@ -294,6 +294,52 @@ int amp_nvfp4_quantize(const void* x, int xt, int64_t rows, int64_t cols, int64_
                        int rnd, uint64_t sr_seed, uint8_t* q, uint8_t* scales,
                        float* d_tensor, void* stream);
 
+/* ---- Fine-grained FP8 scaling (tile and block scales) ----
+ * Page "혼합 정밀도 학습" (itwiki), section "FP8 혼합 정밀도": DeepSeek-V3
+ * computes FP8 scales on the fly per 1x128 tile of activations and per
+ * 128x128 block of weights and keeps every tensor in E4M3; page hwlabs,
+ * section "GEMM 누적 정밀도 문제": partial sums inside a tile, FP32 across
+ * tiles.  Scales are stored K-block-major (the scales of one 128-wide K-block
+ * are contiguous). */
+
+/* amp_quantize_blockwise -- x [rows, cols] of xt in {F32, F16, BF16} (row
+ * stride ldx >= cols) to yt in {E4M3, E5M2}, one FP32 scale per tile:
+ *   block == 0: 1x128 tiles along the output's contiguous (K) dimension;
+ *   block == 1: 128x128 blocks.
+ * Outputs (device memory owned by the caller; either pair may be NULL, not
+ * both):
+ *   q  [rows, cols] codes of x (K = cols), row stride ldq >= cols, with
+ *      s  FP32 scale_inv at s[(c/128)*lds + r] (block: r/128);
+ *      lds >= rows (block: ceil(rows/128));
+ *   qt [cols, rows] codes of x^T (K = rows), row stride ldqt >= rows, with
+ *      st at st[(r/128)*ldst + c] (block: c/128); ldst >= cols (block:
+ *      ceil(cols/128)).  Row tiles of x^T are 128x1 column tiles of x; a
+ *      128x128 block has the same scale in both outputs.
+ * Per tile: scale = fp8_max / amax(tile) in FP32 (448 for E4M3, 57344 for
+ * E5M2; 1 if the amax is 0 or not finite); code = round(fl32(x * scale)),
+ * nearest-even, saturating, NaN -> 0x7F; scale_inv = fl32(1 / scale).
+ * Edge tiles may be short.  rows or cols == 0 is a no-op. */
+int amp_quantize_blockwise(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
+                           int yt, int block, uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                           uint8_t* qt, int64_t ldqt, float* st, int64_t ldst, void* stream);
+
+/* amp_gemm_blockwise -- C = out_cast( sum_k (A[m,k] sa) (B[n,k] sb) ), the
+ * GEMM of two fine-grained FP8 operands (C = A B^T; both K-contiguous, as
+ * amp_quantize_blockwise writes them).
+ *   A [M, K] of at in {E4M3, E5M2}, stride lda >= K; scale_inv sA[kb*ldsA +
+ *     (a_block ? m/128 : m)], kb = k/128, ldsA >= M (a_block: ceil(M/128));
+ *   B [N, K] of bt in {E4M3, E5M2}, stride ldb >= K; sB likewise with n;
+ *   C [M, N] of ct in {F32, F16, BF16}, stride ldc >= N.
+ * Each 128-K block's products are summed in FP32 (exact FP8 products) and
+ * promoted as acc += P * fl32(sa * sb).  Full 256x128 tiles with K a multiple
+ * of 128, per-row A scales (16-byte aligned, ldsA % 4 == 0) and bt == E4M3
+ * run on the matrix cores; other shapes on an element-wise kernel.  M or
+ * N == 0 is a no-op; K == 0 writes zeros. */
+int amp_gemm_blockwise(int64_t M, int64_t N, int64_t K,
+                       const void* A, int at, int64_t lda, const float* sA, int64_t ldsA,
+                       int a_block, const void* B, int bt, int64_t ldb, const float* sB,
+                       int64_t ldsB, int b_block, void* C, int ct, int64_t ldc, void* stream);
+
 /* ---- FP16 AMP training step of a two-layer MLP: the element-wise glue ----
  * Page "혼합 정밀도 학습" (itwiki), section "FP16 학습 루프": Linear(512, 2048)
  * -> GELU -> Linear(2048, 10) under FP16 autocast with cross-entropy in FP32

@@ -26,6 +26,7 @@ __all__ = [
     "amp_colsum_f16", "amp_grad_accumulate", "amp_grad_norm_init", "amp_grad_norm_accumulate",
     "amp_clip_coefficient", "amp_optimizer_step_ex", "NORM_STATE_BYTES", "NORM_PARTIALS",
     "amp_cast_current_scaling", "amp_mx_quantize", "GEMM_MX",
+    "amp_quantize_blockwise", "amp_gemm_blockwise",
 ]
 
 F32, F16, BF16, E4M3, E5M2, E2M1X2 = 0, 1, 2, 3, 4, 5
@@ -93,6 +94,10 @@ _SIGS = {
     "amp_optimizer_step_ex": ([_P, _P, _P, _P, _I, _P, _I, _I64, _P, _P, _P, _I, _P], _I),
     "amp_grad_accumulate": ([_P, _P, _I, _I64, _I, _P], _I),
     "amp_mx_quantize": ([_P, _I, _I64, _I64, _I64, _I, _I, _P, _P, _P], _I),
+    "amp_quantize_blockwise": ([_P, _I, _I64, _I64, _I64, _I, _I, _P, _I64, _P, _I64, _P, _I64,
+                                _P, _I64, _P], _I),
+    "amp_gemm_blockwise": ([_I64, _I64, _I64, _P, _I, _I64, _P, _I64, _I, _P, _I, _I64, _P, _I64,
+                            _I, _P, _I, _I64, _P], _I),
     "amp_cast_current_scaling": ([_P, _I, _I64, _I64, _I64, _P, _I, _I64, _P, _I64, _P, _P, _P],
                                  _I),
     "amp_grad_norm_init": ([_P, _P], _I),
@@ -217,6 +222,20 @@ def amp_cast_current_scaling(x, xt, rows, cols, ldx, y, yt, ldy, y_t, ldy_t,
     _check("amp_cast_current_scaling", load().amp_cast_current_scaling(
         _ptr(x), xt, rows, cols, ldx, _ptr(y), yt, ldy, _ptr(y_t), ldy_t, ctypes.byref(r),
         _ptr(d_meta), _stream(stream)))
+
+
+def amp_quantize_blockwise(x, xt, rows, cols, ldx, yt, block, q, ldq, s, lds, qt=None, ldqt=0,
+                           st=None, ldst=0, stream=None):
+    _check("amp_quantize_blockwise", load().amp_quantize_blockwise(
+        _ptr(x), xt, rows, cols, ldx, yt, int(block), _ptr(q), ldq, _ptr(s), lds, _ptr(qt), ldqt,
+        _ptr(st), ldst, _stream(stream)))
+
+
+def amp_gemm_blockwise(M, N, K, A, at, lda, sA, ldsA, a_block, B, bt, ldb, sB, ldsB, b_block,
+                       C, ct, ldc, stream=None):
+    _check("amp_gemm_blockwise", load().amp_gemm_blockwise(
+        M, N, K, _ptr(A), at, lda, _ptr(sA), ldsA, int(a_block), _ptr(B), bt, ldb, _ptr(sB),
+        ldsB, int(b_block), _ptr(C), ct, ldc, _stream(stream)))
 
 
 def amp_mx_quantize(x, xt, rows, cols, ldx, transpose, yt, q, scales, stream=None):

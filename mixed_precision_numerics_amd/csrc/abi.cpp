@@ -218,6 +218,44 @@ int amp_mx_quantize(const void* x, int xt, int64_t rows, int64_t cols, int64_t l
                                             scales, static_cast<hipStream_t>(stream)));
 }
 
+int amp_quantize_blockwise(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
+                           int yt, int block, uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                           uint8_t* qt, int64_t ldqt, float* st, int64_t ldst, void* stream) {
+  if (rows < 0 || cols < 0 || ldx < cols || (block != 0 && block != 1)) return AMP_EINVAL;
+  if (!is_cast_in(xt)) return AMP_EUNSUPPORTED;
+  if (!is_fp8(yt)) return AMP_EUNSUPPORTED;
+  if (rows == 0 || cols == 0) return AMP_OK;
+  if (!x || (!q && !qt) || (!q != !s) || (!qt != !st)) return AMP_EINVAL;
+  const int64_t rb = (rows + 127) / 128, cb = (cols + 127) / 128;
+  if (q && (ldq < cols || lds < (block ? rb : rows))) return AMP_EINVAL;
+  if (qt && (ldqt < rows || ldst < (block ? cb : cols))) return AMP_EINVAL;
+  if (int e = check_device()) return e;
+  return hip_status(amp::launch_quantize_blockwise(x, xt, rows, cols, ldx, yt, block, q, ldq, s,
+                                                   lds, qt, ldqt, st, ldst,
+                                                   static_cast<hipStream_t>(stream)));
+}
+
+int amp_gemm_blockwise(int64_t M, int64_t N, int64_t K, const void* A, int at, int64_t lda,
+                       const float* sA, int64_t ldsA, int a_block, const void* B, int bt,
+                       int64_t ldb, const float* sB, int64_t ldsB, int b_block, void* C, int ct,
+                       int64_t ldc, void* stream) {
+  if (M < 0 || N < 0 || K < 0) return AMP_EINVAL;
+  if ((a_block != 0 && a_block != 1) || (b_block != 0 && b_block != 1)) return AMP_EINVAL;
+  if (!is_fp8(at) || !is_fp8(bt)) return AMP_EUNSUPPORTED;
+  if (ct != AMP_F32 && ct != AMP_F16 && ct != AMP_BF16) return AMP_EUNSUPPORTED;
+  if (M == 0 || N == 0) return AMP_OK;
+  if (!C || ldc < N) return AMP_EINVAL;
+  if (K > 0) {
+    if (!A || !B || !sA || !sB || lda < K || ldb < K) return AMP_EINVAL;
+    if (ldsA < (a_block ? (M + 127) / 128 : M) || ldsB < (b_block ? (N + 127) / 128 : N))
+      return AMP_EINVAL;
+  }
+  if (int e = check_device()) return e;
+  return hip_status(amp::launch_gemm_blockwise(M, N, K, A, at, lda, sA, ldsA, a_block, B, bt, ldb,
+                                               sB, ldsB, b_block, C, ct, ldc,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 int amp_grad_accumulate(float* acc, const void* grads, int gt, int64_t n, int first,
                         void* stream) {
   if (n < 0) return AMP_EINVAL;

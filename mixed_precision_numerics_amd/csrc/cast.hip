@@ -341,6 +341,215 @@ __global__ void current_scale_kernel(amp_fp8_meta* mt, float fp8_max, float marg
   mt->scale_inv = 1.0f / scale;
 }
 
+
+// ------------------------------------------- fine-grained (tile) scaling ---
+// Page itwiki, section "FP8 혼합 정밀도": DeepSeek-V3 computes FP8 scales on
+// the fly per 1x128 tile of activations and per 128x128 block of weights.
+// Each tile is scaled as by current scaling: scale = fp8_max / amax(tile)
+// in FP32 (1 for a zero or non-finite amax), y = round(fl32(x * scale)).
+// One 256-thread block per 128x128 region of x with cast_tile's thread
+// layout.  Row tiles (1x128 of x) scale the plain output q; column tiles
+// (1x128 of x^T, i.e. 128x1 of x) scale the transposed output qt; in block
+// mode the whole region shares one scale in both orientations.  scale_inv is
+// stored K-block-major: s[(c / 128) * lds + r] (row tiles) or
+// s[(c / 128) * lds + r / 128] (blocks), and st likewise with rows and
+// columns exchanged.
+
+// Max over the 16 lanes of a DPP row (row_ror 8, 4, 2, 1).
+__device__ __forceinline__ uint32_t max16(uint32_t v) {
+  uint32_t o;
+  o = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x128, 0xf, 0xf, false));
+  v = v > o ? v : o;
+  o = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x124, 0xf, 0xf, false));
+  v = v > o ? v : o;
+  o = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x122, 0xf, 0xf, false));
+  v = v > o ? v : o;
+  o = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v), 0x121, 0xf, 0xf, false));
+  return v > o ? v : o;
+}
+
+// Current-scaling scale of one tile from its |x| bit-pattern maximum.
+__device__ __forceinline__ float tile_scale(uint32_t amax_bits, float fp8_max) {
+  return (amax_bits == 0u || amax_bits >= 0x7f800000u) ? 1.0f : fp8_max / bitsf(amax_bits);
+}
+
+template <int XT, int YT, bool BLOCK, bool WQ, bool WQT, bool VEC>
+__global__ __launch_bounds__(kTileThreads) void bw_quant_tile(
+    const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
+    uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t lds,
+    uint8_t* __restrict__ qt, int64_t ldqt, float* __restrict__ st, int64_t ldst) {
+  constexpr int kPitch = kTile + 16;
+  constexpr bool kCols = WQT && !BLOCK;              // column tiles need a cross-wave max
+  __shared__ __align__(16) uint8_t tl[WQT ? kTile * kPitch : 1];
+  __shared__ uint32_t cpart[kCols ? 16 : 1][kCols ? kTile : 1];
+  __shared__ float cscale[kCols ? kTile : 1];
+  __shared__ uint32_t red[kTileThreads / kWave];
+  __shared__ float bscale;
+  constexpr float kMax = YT == AMP_E4M3 ? 448.0f : 57344.0f;
+
+  const int64_t r_base = static_cast<int64_t>(blockIdx.y) * kTile;
+  const int64_t c_base = static_cast<int64_t>(blockIdx.x) * kTile;
+  const int t = threadIdx.x;
+  const int c0 = 8 * (t % 16), r0 = 8 * (t / 16);
+  const bool full = VEC && (r_base + kTile <= rows) && (c_base + kTile <= cols);
+  float v[8][8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int64_t r = r_base + r0 + i, c = c_base + c0;
+    if (full) {
+      load8<XT>(x, r * ldx + c, v[i]);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        v[i][j] = (r < rows && c + j < cols) ? load_one<XT>(x, r * ldx + c + j) : 0.0f;
+    }
+  }
+  // |x| bit maxima of this thread's 8 rows and 8 columns (padding is 0)
+  uint32_t ra[8], ca[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) ca[j] = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    ra[i] = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t a = fbits(v[i][j]) & 0x7fffffffu;
+      ra[i] = ra[i] > a ? ra[i] : a;
+      ca[j] = ca[j] > a ? ca[j] : a;
+    }
+  }
+  float rs[8], cs[8];
+  const int64_t kb_q = c_base / kTile, kb_t = r_base / kTile;
+  if constexpr (BLOCK) {
+    uint32_t m = ra[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) m = m > ra[i] ? m : ra[i];
+    m = block_max_u32<kTileThreads>(m, red);
+    if (t == 0) {
+      const float sc = tile_scale(m, kMax);
+      bscale = sc;
+      if (WQ) s[kb_q * lds + r_base / kTile] = 1.0f / sc;
+      if (WQT) st[kb_t * ldst + c_base / kTile] = 1.0f / sc;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) rs[i] = cs[i] = bscale;
+  } else {
+    if constexpr (WQ) {
+      // the 16 threads of a row of the region are the 16 lanes of a DPP row
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        rs[i] = tile_scale(max16(ra[i]), kMax);
+        const int64_t r = r_base + r0 + i;
+        if (t % 16 == 0 && r < rows) s[kb_q * lds + r] = 1.0f / rs[i];
+      }
+    }
+    if constexpr (WQT) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) cpart[t / 16][c0 + j] = ca[j];
+      __syncthreads();
+      if (t < kTile) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int g = 0; g < 16; ++g) m = m > cpart[g][t] ? m : cpart[g][t];
+        const float sc = tile_scale(m, kMax);
+        cscale[t] = sc;
+        if (c_base + t < cols) st[kb_t * ldst + c_base + t] = 1.0f / sc;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < 8; ++j) cs[j] = cscale[c0 + j];
+    }
+  }
+  if constexpr (WQ) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t r = r_base + r0 + i, c = c_base + c0;
+      uint32_t code[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) code[j] = to_code<YT>(v[i][j] * rs[i]);
+      if (full) {
+        store8<YT>(q, r * ldq + c, code);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (r < rows && c + j < cols) q[r * ldq + c + j] = static_cast<uint8_t>(code[j]);
+      }
+    }
+  }
+  if constexpr (WQT) {
+    // column j of the sub-block -> LDS row c0 + j (cast_tile's swizzled layout)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      uint32_t c8[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c8[i] = to_code<YT>(v[i][j] * cs[j]);
+      uint2 w;
+      w.x = c8[0] | (c8[1] << 8) | (c8[2] << 16) | (c8[3] << 24);
+      w.y = c8[4] | (c8[5] << 8) | (c8[6] << 16) | (c8[7] << 24);
+      *reinterpret_cast<uint2*>(tl + (c0 + j) * kPitch + 8 * ((r0 / 8) ^ swz8(c0 + j))) = w;
+    }
+    __syncthreads();
+    constexpr int kIters = kTile * (kTile / 16) / kTileThreads;
+#pragma unroll
+    for (int it = 0; it < kIters; ++it) {
+      const int idx = it * kTileThreads + t;
+      const int cc = idx / (kTile / 16);
+      const int rr = (idx % (kTile / 16)) * 16;
+      const int64_t orow = c_base + cc, ocol = r_base + rr;
+      const uint8_t* src = tl + cc * kPitch + 8 * ((rr / 8) ^ swz8(cc));
+      if (full) {
+        *reinterpret_cast<uint4*>(qt + orow * ldqt + ocol) = *reinterpret_cast<const uint4*>(src);
+      } else if (orow < cols) {
+#pragma unroll
+        for (int k = 0; k < 16; ++k)
+          if (ocol + k < rows) qt[orow * ldqt + ocol + k] = src[k];
+      }
+    }
+  }
+}
+
+template <int XT, int YT>
+hipError_t dispatch_bw(const void* x, int64_t rows, int64_t cols, int64_t ldx, int block,
+                       uint8_t* q, int64_t ldq, float* s, int64_t lds, uint8_t* qt,
+                       int64_t ldqt, float* st, int64_t ldst, hipStream_t hs) {
+  const int xb = dtype_bytes(XT);
+  bool vec = aligned(x, 16) && (ldx * xb) % 16 == 0;
+  if (q) vec = vec && aligned(q, 8) && ldq % 8 == 0;
+  if (qt) vec = vec && aligned(qt, 16) && ldqt % 16 == 0;
+  const dim3 grid(static_cast<unsigned>((cols + kTile - 1) / kTile),
+                  static_cast<unsigned>((rows + kTile - 1) / kTile));
+#define AMP_BW(B, WQ, WQT)                                                                      \
+  do {                                                                                         \
+    if (vec)                                                                                   \
+      bw_quant_tile<XT, YT, B, WQ, WQT, true><<<grid, kTileThreads, 0, hs>>>(                 \
+          x, rows, cols, ldx, q, ldq, s, lds, qt, ldqt, st, ldst);                             \
+    else                                                                                       \
+      bw_quant_tile<XT, YT, B, WQ, WQT, false><<<grid, kTileThreads, 0, hs>>>(                \
+          x, rows, cols, ldx, q, ldq, s, lds, qt, ldqt, st, ldst);                             \
+  } while (0)
+  if (block) {
+    if (q && qt) AMP_BW(true, true, true);
+    else if (q) AMP_BW(true, true, false);
+    else AMP_BW(true, false, true);
+  } else {
+    if (q && qt) AMP_BW(false, true, true);
+    else if (q) AMP_BW(false, true, false);
+    else AMP_BW(false, false, true);
+  }
+#undef AMP_BW
+  return hipGetLastError();
+}
+
+template <int XT>
+hipError_t dispatch_bw_out(int yt, const void* x, int64_t rows, int64_t cols, int64_t ldx,
+                           int block, uint8_t* q, int64_t ldq, float* s, int64_t lds,
+                           uint8_t* qt, int64_t ldqt, float* st, int64_t ldst, hipStream_t hs) {
+  if (yt == AMP_E4M3)
+    return dispatch_bw<XT, AMP_E4M3>(x, rows, cols, ldx, block, q, ldq, s, lds, qt, ldqt, st, ldst, hs);
+  return dispatch_bw<XT, AMP_E5M2>(x, rows, cols, ldx, block, q, ldq, s, lds, qt, ldqt, st, ldst, hs);
+}
+
 }  // namespace
 
 hipError_t launch_cast(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx, void* y,
@@ -375,6 +584,17 @@ hipError_t launch_cast_current(const void* x, int xt, int64_t rows, int64_t cols
   current_scale_kernel<<<1, 64, 0, s>>>(meta, fp8_max, margin);
   if (hipError_t e = hipGetLastError()) return e;
   return launch_cast(x, xt, rows, cols, ldx, y, yt, ldy, y_t, ldy_t, &meta->scale, nullptr, s);
+}
+
+hipError_t launch_quantize_blockwise(const void* x, int xt, int64_t rows, int64_t cols,
+                                     int64_t ldx, int yt, int block, uint8_t* q, int64_t ldq,
+                                     float* s, int64_t lds, uint8_t* qt, int64_t ldqt, float* st,
+                                     int64_t ldst, hipStream_t hs) {
+  switch (xt) {
+    case AMP_F32: return dispatch_bw_out<AMP_F32>(yt, x, rows, cols, ldx, block, q, ldq, s, lds, qt, ldqt, st, ldst, hs);
+    case AMP_BF16: return dispatch_bw_out<AMP_BF16>(yt, x, rows, cols, ldx, block, q, ldq, s, lds, qt, ldqt, st, ldst, hs);
+    default: return dispatch_bw_out<AMP_F16>(yt, x, rows, cols, ldx, block, q, ldq, s, lds, qt, ldqt, st, ldst, hs);
+  }
 }
 
 }  // namespace amp

@@ -63,6 +63,10 @@ hipError_t launch_cast(const void* x, int xt, int64_t rows, int64_t cols, int64_
 hipError_t launch_cast_current(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
                                void* y, int yt, int64_t ldy, void* y_t, int64_t ldy_t,
                                float fp8_max, float margin, amp_fp8_meta* meta, hipStream_t s);
+hipError_t launch_quantize_blockwise(const void* x, int xt, int64_t rows, int64_t cols,
+                                     int64_t ldx, int yt, int block, uint8_t* q, int64_t ldq,
+                                     float* s, int64_t lds, uint8_t* qt, int64_t ldqt, float* st,
+                                     int64_t ldst, hipStream_t hs);
 hipError_t launch_check_overflow(const void* g, int gt, int64_t n, amp_scaler_state* st,
                                  hipStream_t s);
 hipError_t launch_optimizer_apply(float* master, float* m, float* v, const void* g, int gt,
@@ -89,6 +93,11 @@ hipError_t launch_gemm(int opA, int opB, int64_t M, int64_t N, int64_t K, const 
                        int64_t ldb, const float* alphaB, void* C, int ct, int64_t ldc,
                        const amp_block_scales* bsA, const amp_block_scales* bsB,
                        int flags, hipStream_t s);
+hipError_t launch_gemm_blockwise(int64_t M, int64_t N, int64_t K, const void* A, int at,
+                                 int64_t lda, const float* sA, int64_t ldsA, int a_block,
+                                 const void* B, int bt, int64_t ldb, const float* sB,
+                                 int64_t ldsB, int b_block, void* C, int ct, int64_t ldc,
+                                 hipStream_t s);
 hipError_t launch_nvfp4_quantize(const void* x, int xt, int64_t rows, int64_t cols,
                                  int64_t ldx, int transpose, int block2d, int rht,
                                  uint64_t rht_seed, int rnd, uint64_t sr_seed, uint8_t* q,

@@ -852,6 +852,248 @@ __global__ __launch_bounds__(256) void gemm_generic(GemmArgs g, int a_kc, int b_
   store_c<CT>(g.C, row * g.ldc + col, acc * alpha);
 }
 
+
+// ------------------------------------------- fine-grained FP8 (blockwise)
+// Page itwiki, section "FP8 혼합 정밀도": DeepSeek-V3's operands carry one
+// FP32 scale per 1x128 tile (activations, gradients) or 128x128 block
+// (weights); page hwlabs, section "GEMM 누적 정밀도 문제": each tile's
+// partial sum is promoted to an FP32 accumulator.  Here every 128-K block's
+// partial sum P (exact FP8 products widened to BF16, FP32 matrix-core sums)
+// is added as C += P * fl32(sa * sb).
+//
+// Shape: one 512-thread block (8 waves, 4x2) per 256x128 output tile, each
+// wave 64x64 = 2x2 MFMA 32x32 blocks, with 16 FP32 accumulators and 16
+// partial-sum registers per block (two waves per SIMD).  The K-step is the
+// 128-element scale block; A, B and the step's 256 A-row scales travel to
+// LDS by direct-to-LDS loads.  A's scales are per row, B's per row or per
+// 128-row block.
+
+struct BwArgs {
+  const uint8_t* A;
+  const uint8_t* B;
+  void* C;
+  int64_t M, N, K, lda, ldb, ldc;
+  const float* sA;
+  const float* sB;
+  int64_t ldsA, ldsB;
+  int a_block, b_block;
+};
+
+constexpr int kBwBM = 256, kBwBN = 128, kBwThreads = 512;
+
+// A stage of ROWS 128-byte rows filled by NW waves (ROWS / NW rows each, 8
+// rows per 1 KB load), in the XOR-swizzled layout of swz().
+template <int ROWS, int NW>
+__device__ __forceinline__ void d2l_rows(__amdgpu_buffer_rsrc_t rsrc, uint32_t ld, uint32_t koff,
+                                         uint8_t* stage) {
+  constexpr int RPW = ROWS / NW;
+  static_assert(RPW % 8 == 0, "whole 8-row loads per wave");
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint32_t vrow = static_cast<uint32_t>(w * RPW + lane / 8) * ld;
+  const uint32_t x = static_cast<uint32_t>((lane & 7) ^ (lane >> 3));
+#pragma unroll
+  for (int i = 0; i < RPW / 8; ++i) {
+    const uint32_t chunk = (x ^ static_cast<uint32_t>(w * (RPW / 8) + i)) & 7u;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(stage + (w * RPW + i * 8) * kRowBytes),
+                                             16, vrow + (chunk << 4),
+                                             koff + static_cast<uint32_t>(8 * i) * ld, 0, 0);
+  }
+}
+
+template <int AT, int BT, bool B_BLOCK, int CT>
+__global__ __launch_bounds__(kBwThreads, 1) void gemm_bw_d2l(BwArgs g) {
+  constexpr int kOffB = kBwBM * kRowBytes;                  // B rows after A's
+  constexpr int kOffS = kOffB + kBwBN * kRowBytes;          // then A's 256 scales
+  constexpr int kStage = kOffS + kBwBM * 4;
+  __shared__ __align__(16) uint8_t smem[2][kStage];
+  const int64_t nbm = g.M / kBwBM, nbn = g.N / kBwBN;
+  const int64_t total = nbm * nbn;
+  int64_t tile = blockIdx.x;
+  if (total % 8 == 0) tile = (tile % 8) * (total / 8) + tile / 8;
+  constexpr int64_t kGroup = 8;
+  const int64_t group = tile / (kGroup * nbn);
+  const int64_t first_m = group * kGroup;
+  const int64_t gsz = nbm - first_m < kGroup ? nbm - first_m : kGroup;
+  const int64_t in_group = tile % (kGroup * nbn);
+  const int64_t m0 = (first_m + in_group % gsz) * kBwBM, n0 = (in_group / gsz) * kBwBN;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, h = lane >> 5;
+  f32x16 acc[2][2], P[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  const f32x16 zero = {};
+  const int64_t nk = g.K / 128;
+  const uint32_t lda = static_cast<uint32_t>(g.lda), ldb = static_cast<uint32_t>(g.ldb);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(g.A + m0 * g.lda), 0, static_cast<int>(kBwBM * lda), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(g.B + n0 * g.ldb), 0, static_cast<int>(kBwBN * ldb), 0x00020000);
+  // A's scales of K-block kb: 256 floats at sA[kb * ldsA + m0 ..]
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(g.sA + m0), 0, static_cast<int>(((nk - 1) * g.ldsA + kBwBM) * 4), 0x00020000);
+  // past the end a step reloads the last one into the idle stage (never read)
+  auto load_part = [&](int64_t kt, int which) {
+    const int64_t kc = kt < nk ? kt : nk - 1;
+    uint8_t* st = smem[kt & 1];
+    if (which == 0) {
+      d2l_rows<kBwBM, 8>(ra, lda, static_cast<uint32_t>(kc * 128), st);
+      if (wave == 0)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(st + kOffS), 16,
+                                                 static_cast<uint32_t>(lane * 16),
+                                                 static_cast<uint32_t>(kc * g.ldsA * 4), 0, 0);
+    } else {
+      d2l_rows<kBwBN, 8>(rb, ldb, static_cast<uint32_t>(kc * 128), st + kOffB);
+    }
+  };
+  // B's scales for this lane's columns n0 + wn*64 + nb*32 + l%32 (one value
+  // per wave in block mode), fetched one step ahead
+  float sb[2], nsb[2];
+  auto load_sb = [&](int64_t kt, float (&v)[2]) {
+    const int64_t kc = kt < nk ? kt : nk - 1;
+    if constexpr (B_BLOCK) {
+      v[0] = v[1] = g.sB[kc * g.ldsB + (n0 >> 7)];
+    } else {
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) v[nb] = g.sB[kc * g.ldsB + n0 + wn * 64 + nb * 32 + l32];
+    }
+  };
+  const uint32_t gsw = static_cast<uint32_t>((l32 & 7) ^ (l32 >> 3));
+  const uint32_t abase = static_cast<uint32_t>(wm * 64 + l32) * kRowBytes;
+  const uint32_t bbase = kOffB + static_cast<uint32_t>(wn * 64 + l32) * kRowBytes;
+  u32x4 fa[2][2], fb[2][2];
+  // slice ks: 16 FP8 bytes per lane = logical chunk 2ks + h of rows
+  // wm*64 + mb*32 + l%32 (A) and wn*64 + nb*32 + l%32 (B)
+  auto frag = [&](const uint8_t* st, int ks, u32x4 (&a)[2], u32x4 (&b)[2]) {
+    const uint32_t y = (static_cast<uint32_t>(h) ^ gsw) & 7u;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t c = static_cast<uint32_t>(2 * ks) ^ static_cast<uint32_t>(4 * (i & 1));
+      a[i] = *reinterpret_cast<const u32x4*>(st + abase + i * 32 * kRowBytes + ((y ^ c) << 4));
+      b[i] = *reinterpret_cast<const u32x4*>(st + bbase + i * 32 * kRowBytes + ((y ^ c) << 4));
+    }
+  };
+  load_part(0, 0);
+  load_part(0, 1);
+  load_sb(0, sb);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  frag(smem[0], 0, fa[0], fb[0]);
+  for (int64_t kt = 0; kt < nk; ++kt) {
+    const uint8_t* st = smem[kt & 1];
+    load_sb(kt + 1, nsb);
+    f32x4 sav[2][4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int cur = ks & 1;
+      if (ks < 2) load_part(kt + 1, ks);
+      if (ks < 3) {
+        frag(st, ks + 1, fa[cur ^ 1], fb[cur ^ 1]);
+      } else {
+        // this step's A-row scales: rows wm*64 + mb*32 + 8q + 4h + (0..3)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4)
+            sav[mb][q4] = *reinterpret_cast<const f32x4*>(st + kOffS + (wm * 64 + mb * 32 + 8 * q4 + 4 * h) * 4);
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+        __syncthreads();
+        frag(smem[(kt + 1) & 1], 0, fa[cur ^ 1], fb[cur ^ 1]);
+      }
+      u32x4 da[2][2], db[2][2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          da[e][i] = u32x4{fp8x2_to_bf16x2<AT, false>(fa[cur][i][2 * e]), fp8x2_to_bf16x2<AT, true>(fa[cur][i][2 * e]),
+                           fp8x2_to_bf16x2<AT, false>(fa[cur][i][2 * e + 1]), fp8x2_to_bf16x2<AT, true>(fa[cur][i][2 * e + 1])};
+          db[e][i] = u32x4{fp8x2_to_bf16x2<BT, false>(fb[cur][i][2 * e]), fp8x2_to_bf16x2<BT, true>(fb[cur][i][2 * e]),
+                           fp8x2_to_bf16x2<BT, false>(fb[cur][i][2 * e + 1]), fp8x2_to_bf16x2<BT, true>(fb[cur][i][2 * e + 1])};
+        }
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+            P[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                __builtin_bit_cast(bf16x8_t, da[e][mb]), __builtin_bit_cast(bf16x8_t, db[e][nb]),
+                (ks == 0 && e == 0) ? zero : P[mb][nb], 0, 0, 0);
+    }
+    // promote the K-block's partial sums: acc += P * fl32(sa * sb)
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float sc = sav[mb][r >> 2][r & 3] * sb[nb];
+          acc[mb][nb][r] = __builtin_fmaf(P[mb][nb][r], sc, acc[mb][nb][r]);
+        }
+    sb[0] = nsb[0];
+    sb[1] = nsb[1];
+  }
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int64_t col = n0 + wn * 64 + nb * 32 + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t row = m0 + wm * 64 + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        store_c<CT>(g.C, row * g.ldc + col, acc[mb][nb][r]);
+      }
+    }
+}
+
+// Any shape: one output per thread; each K-block's exact products are summed
+// in FP32 and promoted with its scales.
+template <int AT, int BT, int CT>
+__global__ __launch_bounds__(256) void gemm_bw_generic(BwArgs g) {
+  const int64_t col = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x & 15);
+  const int64_t row = static_cast<int64_t>(blockIdx.y) * 16 + (threadIdx.x >> 4);
+  if (row >= g.M || col >= g.N) return;
+  float acc = 0.0f;
+  for (int64_t k0 = 0; k0 < g.K; k0 += 128) {
+    const int64_t k1 = k0 + 128 < g.K ? k0 + 128 : g.K;
+    float p = 0.0f;
+    for (int64_t k = k0; k < k1; ++k)
+      p = __builtin_fmaf(load_elem<AT>(g.A, row * g.lda + k), load_elem<BT>(g.B, col * g.ldb + k), p);
+    const int64_t kb = k0 / 128;
+    const float sa = g.sA[kb * g.ldsA + (g.a_block ? row / 128 : row)];
+    const float sb = g.sB[kb * g.ldsB + (g.b_block ? col / 128 : col)];
+    acc = __builtin_fmaf(p, sa * sb, acc);
+  }
+  store_c<CT>(g.C, row * g.ldc + col, acc);
+}
+
+template <int AT, int BT>
+hipError_t launch_bw_t(const BwArgs& g, bool fast, int ct, hipStream_t s) {
+  if (fast) {
+    const dim3 grid(static_cast<unsigned>((g.M / kBwBM) * (g.N / kBwBN)));
+#define AMP_BWK(BB)                                                                              \
+    switch (ct) {                                                                               \
+      case AMP_F32: gemm_bw_d2l<AT, BT, BB, AMP_F32><<<grid, kBwThreads, 0, s>>>(g); break;     \
+      case AMP_BF16: gemm_bw_d2l<AT, BT, BB, AMP_BF16><<<grid, kBwThreads, 0, s>>>(g); break;   \
+      default: gemm_bw_d2l<AT, BT, BB, AMP_F16><<<grid, kBwThreads, 0, s>>>(g); break;          \
+    }
+    if (g.b_block) { AMP_BWK(true) } else { AMP_BWK(false) }
+#undef AMP_BWK
+    return hipGetLastError();
+  }
+  const dim3 grid(static_cast<unsigned>((g.N + 15) / 16), static_cast<unsigned>((g.M + 15) / 16));
+  switch (ct) {
+    case AMP_F32: gemm_bw_generic<AT, BT, AMP_F32><<<grid, 256, 0, s>>>(g); break;
+    case AMP_BF16: gemm_bw_generic<AT, BT, AMP_BF16><<<grid, 256, 0, s>>>(g); break;
+    default: gemm_bw_generic<AT, BT, AMP_F16><<<grid, 256, 0, s>>>(g); break;
+  }
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- dispatch
 template <int AT, int BT, bool A_KC, bool B_KC, int PATH, bool CHECK>
 hipError_t launch_mfma_c(const GemmArgs& g, int ct, hipStream_t s) {
@@ -989,6 +1231,26 @@ hipError_t launch_gemm(int opA, int opB, int64_t M, int64_t N, int64_t K, const 
   fast = fast && (a_kc ? K % 8 == 0 : M % 8 == 0) && (b_kc ? K % 8 == 0 : N % 8 == 0);
   if (at == AMP_BF16) return launch_16<AMP_BF16>(g, a_kc, b_kc, fast, ct, s);
   return launch_16<AMP_F16>(g, a_kc, b_kc, fast, ct, s);
+}
+
+hipError_t launch_gemm_blockwise(int64_t M, int64_t N, int64_t K, const void* A, int at,
+                                 int64_t lda, const float* sA, int64_t ldsA, int a_block,
+                                 const void* B, int bt, int64_t ldb, const float* sB,
+                                 int64_t ldsB, int b_block, void* C, int ct, int64_t ldc,
+                                 hipStream_t s) {
+  BwArgs g{static_cast<const uint8_t*>(A), static_cast<const uint8_t*>(B), C, M, N, K, lda, ldb,
+           ldc, sA, sB, ldsA, ldsB, a_block, b_block};
+  // matrix-core path: full 256x128 tiles, whole K-blocks, A's scales per row
+  // (16-byte aligned scale rows), 32-bit buffer offsets
+  constexpr int64_t kLim = int64_t(1) << 31;
+  const bool fast = M % kBwBM == 0 && N % kBwBN == 0 && K % 128 == 0 && K > 0 && !a_block &&
+                    aligned(A, 16) && aligned(B, 16) && lda % 16 == 0 && ldb % 16 == 0 &&
+                    lda * kBwBM < kLim && ldb * kBwBN < kLim && aligned(sA, 16) && ldsA % 4 == 0 &&
+                    ((K / 128) * ldsA + kBwBM) * 4 < kLim && bt == AMP_E4M3;
+  if (at == AMP_E4M3 && bt == AMP_E4M3) return launch_bw_t<AMP_E4M3, AMP_E4M3>(g, fast, ct, s);
+  if (at == AMP_E5M2 && bt == AMP_E4M3) return launch_bw_t<AMP_E5M2, AMP_E4M3>(g, fast, ct, s);
+  if (at == AMP_E4M3) return launch_bw_t<AMP_E4M3, AMP_E5M2>(g, false, ct, s);
+  return launch_bw_t<AMP_E5M2, AMP_E5M2>(g, false, ct, s);
 }
 
 }  // namespace amp

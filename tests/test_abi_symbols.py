@@ -52,5 +52,21 @@ def test_invalid_arguments_rejected_before_any_device_work():
                         None, None, None) == -2
     assert lib.amp_optimizer_step(None, None, None, None, 1, None, 1, -5, None, None, 0, None) == -1
     assert lib.amp_nvfp4_quantize(None, 2, 17, 32, 32, 0, 0, 0, 0, 0, 0, None, None, None, None) == -1
+    # fine-grained FP8: bad block flag, non-FP8 output, missing scale buffer,
+    # short scale stride, non-FP8 GEMM operand
+    assert lib.amp_quantize_blockwise(None, 2, 4, 4, 4, 3, 2, None, 4, None, 4, None, 0, None, 0,
+                                      None) == -1
+    assert lib.amp_quantize_blockwise(None, 2, 4, 4, 4, 1, 0, None, 4, None, 4, None, 0, None, 0,
+                                      None) == -2
+    assert lib.amp_quantize_blockwise(8, 2, 4, 4, 4, 3, 0, 8, 4, None, 4, None, 0, None, 0,
+                                      None) == -1
+    assert lib.amp_quantize_blockwise(8, 2, 4, 4, 4, 3, 0, 8, 4, 8, 3, None, 0, None, 0,
+                                      None) == -1
+    assert lib.amp_gemm_blockwise(4, 4, 4, 8, 2, 4, 8, 4, 0, 8, 3, 4, 8, 4, 0, 8, 0, 4,
+                                  None) == -2
+    assert lib.amp_gemm_blockwise(4, 4, 4, 8, 3, 4, 8, 3, 0, 8, 3, 4, 8, 4, 0, 8, 0, 4,
+                                  None) == -1
     # empty work is a successful no-op
     assert lib.amp_cast(None, 0, 0, 4, 4, None, 1, 4, None, 0, None, None, None) == 0
+    assert lib.amp_gemm_blockwise(0, 4, 4, None, 3, 4, None, 0, 0, None, 3, 4, None, 0, 0, None,
+                                  0, 4, None) == 0

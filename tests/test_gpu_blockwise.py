@@ -1,0 +1,187 @@
+"""Fine-grained FP8 scaling on the GPU: amp_quantize_blockwise bit-exact
+against oracle/blockwise.py (1x128 tiles and 128x128 blocks, plain and
+transposed outputs, ragged edges, strided input, zero and non-finite tiles)
+and amp_gemm_blockwise against the float64 product of the dequantized
+operands (matrix-core path and element-wise path), including the FFN up
+projection at full size on sampled outputs."""
+import numpy as np
+import pytest
+import torch
+
+import mixed_precision_numerics_amd as amp
+from oracle import blockwise as OB
+from oracle import formats as F
+from oracle import gemm as OG
+import synth
+from gpu_util import dev, empty, host
+
+pytestmark = pytest.mark.gpu
+
+YF = {amp.E4M3: F.E4M3, amp.E5M2: F.E5M2}
+XF = {amp.F32: F.F32, amp.BF16: F.BF16, amp.F16: F.F16}
+
+
+def bw_input(seed, rows, cols, xt, ldx):
+    x = synth.student_t_f32(seed, (rows, cols), 3.0, 3.0)
+    x[4, :] *= 1e4                       # a loud row
+    x[:, 9] *= 1e-4                      # a quiet column
+    x[128:256, 0:128] = 0.0              # a zero block (and zero row/column tiles)
+    x[7, 130] = np.inf
+    x[200, 3] = np.nan
+    if xt == amp.F32:
+        codes = synth.f32_bits(x)
+    elif xt == amp.BF16:
+        codes = synth.to_bf16_codes(x)
+    else:
+        codes = synth.to_f16_codes(np.clip(x, -6e4, 6e4))
+    buf = np.zeros((rows, ldx), dtype=codes.dtype)
+    buf[:, :cols] = codes
+    return buf, codes
+
+
+def run_quant(codes_buf, xt, rows, cols, ldx, yt, block, want_q=True, want_qt=True):
+    rb, cb = -(-rows // 128), -(-cols // 128)
+    lds = rb if block else rows
+    ldst = cb if block else cols
+    ldq, ldqt = cols + 5, rows + 3
+    q = empty(rows * ldq, fill=0xEE) if want_q else None
+    s = empty(cb * lds * 4, fill=0xEE) if want_q else None
+    qt = empty(cols * ldqt, fill=0xEE) if want_qt else None
+    st = empty(rb * ldst * 4, fill=0xEE) if want_qt else None
+    amp.amp_quantize_blockwise(dev(codes_buf), xt, rows, cols, ldx, yt, block, q, ldq, s, lds,
+                               qt, ldqt, st, ldst)
+    out = {}
+    if want_q:
+        out["q"] = host(q, np.uint8).reshape(rows, ldq)[:, :cols]
+        out["s"] = host(s, np.float32).reshape(cb, lds)
+    if want_qt:
+        out["qt"] = host(qt, np.uint8).reshape(cols, ldqt)[:, :rows]
+        out["st"] = host(st, np.float32).reshape(rb, ldst)
+    return out
+
+
+@pytest.mark.parametrize("xt", [amp.BF16, amp.F32, amp.F16])
+@pytest.mark.parametrize("yt", [amp.E4M3, amp.E5M2])
+@pytest.mark.parametrize("block", [0, 1])
+@pytest.mark.parametrize("pad", [8, 3])
+def test_quantize_blockwise_bit_exact(xt, yt, block, pad):
+    rows, cols = 300, 200
+    ldx = cols + pad                     # pad 8: 16-byte rows (vector loads); 3: scalar loads
+    buf, codes = bw_input(80 + xt + yt, rows, cols, xt, ldx)
+    got = run_quant(buf, xt, rows, cols, ldx, yt, block)
+    wq, ws = OB.quantize(codes, XF[xt], YF[yt], bool(block))
+    wqt, wst = OB.quantize(codes, XF[xt], YF[yt], bool(block), transpose=True)
+    assert np.array_equal(got["s"], ws.astype(np.float32))
+    assert np.array_equal(got["st"], wst.astype(np.float32))
+    bad = np.argwhere(got["q"] != wq)
+    assert bad.size == 0, (bad[:5], got["q"][tuple(bad[0])], wq[tuple(bad[0])])
+    bad = np.argwhere(got["qt"] != wqt)
+    assert bad.size == 0, (bad[:5], got["qt"][tuple(bad[0])], wqt[tuple(bad[0])])
+
+
+@pytest.mark.parametrize("block", [0, 1])
+@pytest.mark.parametrize("which", ["q", "qt"])
+def test_quantize_blockwise_single_output_full_tiles(block, which):
+    rows, cols = 256, 384
+    buf, codes = bw_input(90 + block, rows, cols, amp.BF16, cols)
+    got = run_quant(buf, amp.BF16, rows, cols, cols, amp.E4M3, block,
+                    want_q=which == "q", want_qt=which == "qt")
+    wq, ws = OB.quantize(codes, F.BF16, F.E4M3, bool(block), transpose=which == "qt")
+    key_s = "s" if which == "q" else "st"
+    assert np.array_equal(got[key_s], ws.astype(np.float32))
+    assert np.array_equal(got[which], wq)
+
+
+def bw_operand(seed, rows, k, fmt, block, std):
+    x = synth.student_t_f32(seed, (rows, k), 3.0, std)
+    return OB.quantize(synth.f32_bits(x), F.F32, fmt, block)
+
+
+def run_gemm(M, N, K, at, bt, a_block, b_block, ct, seed):
+    ca, sa = bw_operand(seed, M, K, YF[at], a_block, 1.0)
+    cb, sb = bw_operand(seed + 1, N, K, YF[bt], b_block, 0.02)
+    c = empty(M * N * 4)
+    amp.amp_gemm_blockwise(M, N, K, dev(ca), at, K, dev(sa.astype(np.float32)), sa.shape[1],
+                           a_block, dev(cb), bt, K, dev(sb.astype(np.float32)), sb.shape[1],
+                           b_block, c, ct, N)
+    cref, mag = OB.gemm(ca, sa, YF[at], bool(a_block), cb, sb, YF[bt], bool(b_block))
+    if ct == amp.F32:
+        got = host(c, np.float32)[:M * N].reshape(M, N)
+        ok = OG.check_f32(got, cref, mag)
+    else:
+        fmt = F.BF16 if ct == amp.BF16 else F.F16
+        got = host(c, np.uint16)[:M * N].reshape(M, N)
+        ok = OG.check_rounded(got, fmt, cref, mag)
+    bad = np.argwhere(~ok)
+    assert bad.size == 0, (bad[:5], got[tuple(bad[0])], cref[tuple(bad[0])], mag[tuple(bad[0])])
+
+
+@pytest.mark.parametrize("at", [amp.E4M3, amp.E5M2])
+@pytest.mark.parametrize("b_block", [0, 1])
+@pytest.mark.parametrize("ct", [amp.F32, amp.BF16])
+def test_gemm_blockwise_matrix_core_path(at, b_block, ct):
+    # full 256x128 tiles, 5 K-blocks: several tiles in both directions
+    run_gemm(512, 384, 640, at, amp.E4M3, 0, b_block, ct, seed=100 + at + 2 * b_block)
+
+
+@pytest.mark.parametrize("shape", [(300, 200, 333), (256, 128, 200), (64, 48, 128), (5, 7, 1)])
+@pytest.mark.parametrize("a_block", [0, 1])
+def test_gemm_blockwise_elementwise_path(shape, a_block):
+    M, N, K = shape
+    run_gemm(M, N, K, amp.E4M3, amp.E4M3, a_block, 1, amp.F32, seed=110 + a_block)
+
+
+def test_gemm_blockwise_e5m2_b_operand_and_f16_output():
+    run_gemm(256, 128, 256, amp.E5M2, amp.E5M2, 0, 0, amp.F16, seed=120)
+
+
+def test_gemm_blockwise_k_zero_writes_zeros():
+    M, N = 256, 128
+    c = empty(M * N * 4, fill=0x55)
+    amp.amp_gemm_blockwise(M, N, 0, None, amp.E4M3, 0, None, 0, 0, None, amp.E4M3, 0, None, 0, 1,
+                           c, amp.F32, N)
+    assert not host(c, np.float32)[:M * N].any()
+
+
+def test_ffn_up_projection_full_size_sampled():
+    """Fine-grained FP8 forward GEMM of the FFN up projection (8192 tokens,
+    hidden 4096, 28672 outputs): X in 1x128 tiles, W in 128x128 blocks, both
+    quantized on the GPU; sampled rows and 128-row weight blocks are
+    quantized by the oracle from the same inputs and compared bit for bit,
+    and sampled outputs against the oracle's GEMM."""
+    T, I, O = 8192, 4096, 28672
+    d = "cuda"
+    gen = torch.Generator(device=d).manual_seed(21)
+    x = torch.randn(T, I, generator=gen, device=d).to(torch.bfloat16)
+    w = (torch.randn(O, I, generator=gen, device=d) * 0.02).to(torch.bfloat16)
+    qx = torch.empty(T, I, dtype=torch.uint8, device=d)
+    sx = torch.empty(I // 128, T, dtype=torch.float32, device=d)
+    qw = torch.empty(O, I, dtype=torch.uint8, device=d)
+    sw = torch.empty(I // 128, O // 128, dtype=torch.float32, device=d)
+    amp.amp_quantize_blockwise(x, amp.BF16, T, I, I, amp.E4M3, 0, qx, I, sx, T)
+    amp.amp_quantize_blockwise(w, amp.BF16, O, I, I, amp.E4M3, 1, qw, I, sw, O // 128)
+    c = torch.empty(T, O, dtype=torch.bfloat16, device=d)
+    amp.amp_gemm_blockwise(T, O, I, qx, amp.E4M3, I, sx, T, 0, qw, amp.E4M3, I, sw, O // 128, 1,
+                           c, amp.BF16, O)
+    rng = np.random.default_rng(5)
+    rows = np.sort(rng.choice(T, 48, replace=False))
+    wblocks = np.sort(rng.choice(O // 128, 2, replace=False))
+    xs = x[torch.from_numpy(rows).to(d)].view(torch.int16).cpu().numpy().view(np.uint16)
+    wq_all, ws_all, cols = [], [], []
+    for b in wblocks:
+        wsl = w[b * 128:(b + 1) * 128].view(torch.int16).cpu().numpy().view(np.uint16)
+        wq, ws = OB.quantize(wsl, F.BF16, F.E4M3, block=True)
+        got_q = qw[b * 128:(b + 1) * 128].cpu().numpy()
+        assert np.array_equal(got_q, wq)
+        assert np.array_equal(sw[:, b].cpu().numpy(), ws[:, 0].astype(np.float32))
+        wq_all.append(wq); ws_all.append(ws); cols.append(np.arange(b * 128, b * 128 + 128))
+    xq, xsc = OB.quantize(xs, F.BF16, F.E4M3, block=False)
+    assert np.array_equal(qx[torch.from_numpy(rows).to(d)].cpu().numpy(), xq)
+    assert np.array_equal(sx[:, torch.from_numpy(rows).to(d)].cpu().numpy(), xsc.astype(np.float32))
+    cols = np.concatenate(cols)
+    wq = np.concatenate(wq_all)
+    ws = np.concatenate(ws_all, axis=1)          # [K-blocks, 2]
+    cref, mag = OB.gemm(xq, xsc, F.E4M3, False, wq, ws, F.E4M3, True)
+    out = c[torch.from_numpy(rows).to(d)][:, torch.from_numpy(cols).to(d)]
+    got = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert OG.check_rounded(got, F.BF16, cref, mag).all()

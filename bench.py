@@ -20,7 +20,10 @@ Also measured in the same run (reported under "components"):
   * the global-norm pass (2^31 FP16 gradients) and FP32 gradient
     accumulation;
   * MXFP4 and MXFP8 GEMMs of the FFN up projection on the block-scaled
-    matrix cores, with their quantizer.
+    matrix cores, with their quantizer;
+  * fine-grained FP8 (1x128 activation / gradient tiles, 128x128 weight
+    blocks): the three quantizer passes and the forward, dgrad and wgrad
+    GEMMs of the FFN up projection.
 The CPU oracle is timed on a bounded sample of the optimizer workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-components]
@@ -413,6 +416,65 @@ def mx_workload(torch, amp):
     return out
 
 
+def blockwise_workload(torch, amp):
+    """Fine-grained FP8 (1x128 activation / gradient tiles, 128x128 weight
+    blocks, E4M3 everywhere) through one FFN up projection (8192 tokens,
+    hidden 4096, 28672 outputs): quantize X, W and dY (each with its
+    transposed operand in the same pass), then the forward, dgrad and wgrad
+    GEMMs with per-128-K promotion."""
+    T, I, O = 8192, 4096, 28672
+    d = "cuda"
+    gen = torch.Generator(device=d).manual_seed(13)
+    X = torch.randn(T, I, device=d, generator=gen).to(torch.bfloat16)
+    W = (torch.randn(O, I, device=d, generator=gen) * 0.02).to(torch.bfloat16)
+    dY = (torch.randn(T, O, device=d, generator=gen) * 1e-3).to(torch.bfloat16)
+    u8, f32 = torch.uint8, torch.float32
+    qx, qxt = torch.empty(T, I, dtype=u8, device=d), torch.empty(I, T, dtype=u8, device=d)
+    sx, sxt = torch.empty(I // 128, T, dtype=f32, device=d), torch.empty(T // 128, I, dtype=f32, device=d)
+    qw, qwt = torch.empty(O, I, dtype=u8, device=d), torch.empty(I, O, dtype=u8, device=d)
+    sw, swt = (torch.empty(I // 128, O // 128, dtype=f32, device=d),
+               torch.empty(O // 128, I // 128, dtype=f32, device=d))
+    qd, qdt = torch.empty(T, O, dtype=u8, device=d), torch.empty(O, T, dtype=u8, device=d)
+    sd, sdt = torch.empty(O // 128, T, dtype=f32, device=d), torch.empty(T // 128, O, dtype=f32, device=d)
+    Y = torch.empty(T, O, dtype=torch.bfloat16, device=d)
+    dX = torch.empty(T, I, dtype=torch.bfloat16, device=d)
+    dW = torch.empty(O, I, dtype=f32, device=d)
+    E4 = amp.E4M3
+
+    def quant():
+        amp.amp_quantize_blockwise(X, amp.BF16, T, I, I, E4, 0, qx, I, sx, T, qxt, T, sxt, I)
+        amp.amp_quantize_blockwise(W, amp.BF16, O, I, I, E4, 1, qw, I, sw, O // 128, qwt, O, swt, I // 128)
+        amp.amp_quantize_blockwise(dY, amp.BF16, T, O, O, E4, 0, qd, O, sd, T, qdt, T, sdt, O)
+
+    def fprop():
+        amp.amp_gemm_blockwise(T, O, I, qx, E4, I, sx, T, 0, qw, E4, I, sw, O // 128, 1, Y, amp.BF16, O)
+
+    def dgrad():
+        amp.amp_gemm_blockwise(T, I, O, qd, E4, O, sd, T, 0, qwt, E4, O, swt, I // 128, 1, dX,
+                               amp.BF16, I)
+
+    def wgrad():
+        amp.amp_gemm_blockwise(O, I, T, qdt, E4, T, sdt, O, 0, qxt, E4, T, sxt, I, 0, dW, amp.F32, I)
+
+    q_ms = _timed(torch, quant, 5)
+    out = {"quantize_ms": round(q_ms, 4),
+           "quantize_gbs": round((T * I + O * I + T * O) * 4 / q_ms / 1e6, 1)}
+    flops = 2 * T * I * O
+    total = q_ms
+    for name, f in (("fprop", fprop), ("dgrad", dgrad), ("wgrad", wgrad)):
+        ms = _timed(torch, f, 10)
+        total += ms
+        tf = flops / ms / 1e9
+        out[name] = {"ms": round(ms, 4), "tflops": round(tf, 1),
+                     "frac_bf16_mfma": round(tf / BF16_PEAK_TFLOPS, 4)}
+    out["layer_ms"] = round(total, 4)
+    out["layer_tflops"] = round(3 * flops / total / 1e9, 1)
+    out["mfma"] = "bf16 (E4M3 widened exactly; per-128-K FP32 promotion)"
+    del X, W, dY, qx, qxt, qw, qwt, qd, qdt, Y, dX, dW
+    torch.cuda.empty_cache()
+    return out
+
+
 def measured_traffic():
     """HBM bytes per launch of the apply kernel, from the committed rocprofv3
     counter summary, or None when the kernel sources changed since then."""
@@ -496,6 +558,8 @@ def main():
         comps["nvfp4_wgrad"] = nvfp4_workload(torch, amp)
         log("components: MX GEMMs (block-scaled matrix cores)")
         comps["mx"] = mx_workload(torch, amp)
+        log("components: fine-grained FP8 (1x128 / 128x128 scales) FFN up projection")
+        comps["blockwise_fp8"] = blockwise_workload(torch, amp)
         log("components: delayed vs current scaling casts")
         comps["scaling"] = scaling_workload(torch, amp)
         log("components: gradient norm and accumulation")

@@ -79,6 +79,14 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *static_cast<const u32x4*>(p); }
 
+// The wave's index in its block.  It is the same for every lane, but the
+// compiler cannot tell from threadIdx; taken through readfirstlane it lives
+// in a scalar register, so buffer-load scalar offsets and LDS bases derived
+// from it need no per-lane (waterfall) loop.
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6));
+}
+
 // 8x8 transpose of 16-bit elements held as 8 rows of 4 words.
 __device__ __forceinline__ void transpose8x8_16(const u32x4 (&v)[8], u32x4 (&o)[8]) {
 #pragma unroll
@@ -306,7 +314,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma(GemmArgs g) {
   const int64_t m0 = tm * kBM, n0 = tn * kBN;
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = wave_id();
   const int wm = wave >> 1, wn = wave & 1;
 
   f32x16 acc[4][4];
@@ -442,7 +450,7 @@ typedef __attribute__((address_space(3))) void lds_void;
 // starts at the tile's first row; koff is the K-step's byte offset.
 __device__ __forceinline__ void d2l_stage(__amdgpu_buffer_rsrc_t rsrc, uint32_t ldb, uint32_t koff,
                                           uint8_t* stage) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = wave_id();
   const uint32_t vrow = static_cast<uint32_t>(w * 64 + lane / 8) * ldb;
   const uint32_t x = static_cast<uint32_t>(((lane & 7) ^ (lane >> 3)) & 7) << 4;
 #pragma unroll
@@ -459,7 +467,7 @@ __device__ __forceinline__ void d2l_stage(__amdgpu_buffer_rsrc_t rsrc, uint32_t 
 // physical chunk l%32 of row l/32.  rsrc starts at the step's first K-row.
 __device__ __forceinline__ void d2l_stage_mn(__amdgpu_buffer_rsrc_t rsrc, uint32_t ldb,
                                              uint8_t* stage) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = wave_id();
   const int hr = lane >> 5;
   const uint32_t v0 = static_cast<uint32_t>(hr) * ldb;
   // row%4 = 2*(i&1) + hr
@@ -558,7 +566,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
   const int64_t gsz = nbm - first_m < kGroup ? nbm - first_m : kGroup;
   const int64_t in_group = tile % (kGroup * nbn);
   const int64_t m0 = (first_m + in_group % gsz) * kBM, n0 = (in_group / gsz) * kBN;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int wm = wave >> 1, wn = wave & 1;
   f32x16 acc[4][4];
 #pragma unroll
@@ -888,7 +896,7 @@ __device__ __forceinline__ void d2l_rows(__amdgpu_buffer_rsrc_t rsrc, uint32_t l
                                          uint8_t* stage) {
   constexpr int RPW = ROWS / NW;
   static_assert(RPW % 8 == 0, "whole 8-row loads per wave");
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, w = wave_id();
   const uint32_t vrow = static_cast<uint32_t>(w * RPW + lane / 8) * ld;
   const uint32_t x = static_cast<uint32_t>((lane & 7) ^ (lane >> 3));
 #pragma unroll
@@ -916,7 +924,7 @@ __global__ __launch_bounds__(kBwThreads, 1) void gemm_bw_d2l(BwArgs g) {
   const int64_t gsz = nbm - first_m < kGroup ? nbm - first_m : kGroup;
   const int64_t in_group = tile % (kGroup * nbn);
   const int64_t m0 = (first_m + in_group % gsz) * kBwBM, n0 = (in_group / gsz) * kBwBN;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = wave_id();
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, h = lane >> 5;
   f32x16 acc[2][2], P[2][2];

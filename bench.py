@@ -324,7 +324,7 @@ def nvfp4_workload(torch, amp):
     return {"gemm_ms": round(g_ms, 4), "gemm_tflops": round(tf, 1),
             "peak_tflops_fp4": FP4_PEAK_TFLOPS, "frac_fp4": round(tf / FP4_PEAK_TFLOPS, 4),
             "frac_bf16_mfma": round(tf / BF16_PEAK_TFLOPS, 4),
-            "mfma": "bf16 (E2M1 x E4M3 decoded exactly to BF16)",
+            "mfma": "f16 (E2M1 x E4M3 decoded exactly to F16 per register fragment)",
             "quantize_ms": round(q_ms, 4), "quantize_gbs": round(qbytes / q_ms / 1e6, 1),
             "tflop_per_step": round(flops / 1e12, 3)}
 

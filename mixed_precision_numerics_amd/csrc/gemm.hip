@@ -7,9 +7,10 @@
 // sums, output cast); page "Mixed Precision Training/es" (marovi), section
 // "La receta de precisión mixta".  For NVFP4 operands (page "Pretraining
 // Large Language Models with NVFP4", section 2.1) each E2M1 element times its
-// E4M3 block scale is an exact BF16 value (at most 6 significant bits, range
-// 2^-10 .. 2688), so the operand is decoded exactly to BF16 and the tensor
-// scales are applied in the epilogue.
+// E4M3 block scale is exact in BF16 and in F16 (at most 6 significant bits,
+// magnitudes 2^-10 .. 2688), so the operand is decoded exactly (to F16 per
+// register fragment on the full-tile path, to BF16 on the way to LDS
+// otherwise) and the tensor scales are applied in the epilogue.
 //
 //   C = out_cast( fl32(alphaA * alphaB) * sum_k op(A)[m,k] op(B)[k,n] )
 //
@@ -21,10 +22,14 @@
 // swizzle (chunk ^ ((row ^ row >> 3) & 7)) so that both the MFMA fragment
 // reads (32 consecutive rows, one chunk) and the transposed stores (rows 8
 // apart) spread over the banks (measured: no bank conflicts).
-//  * gemm_mfma_d2l: both operands K-contiguous, full tiles.  The next K-step
-//    is fetched with direct-to-LDS loads (global_load_lds, 16 B per lane, no
-//    VGPR staging): lane l of each 1 KB load fetches the logical chunk that
-//    the swizzle places at LDS byte 16*l.
+//  * gemm_mfma_d2l: full tiles.  The next K-step is fetched with
+//    direct-to-LDS loads (buffer_load ... lds, 16 B per lane, no VGPR
+//    staging): lane l of each 1 KB load fetches the logical chunk that the
+//    swizzle places at LDS byte 16*l.  8-bit and 4-bit operands stay in their
+//    storage format in LDS and are widened per register fragment (FP8 ->
+//    BF16, NVFP4 -> F16 x block scale) or fed to the block-scaled
+//    instruction (MX); M/N-contiguous 16-bit operands are read with
+//    transposing LDS reads.
 //  * gemm_mfma: any layout and ragged edges.  The next K-step is staged in
 //    registers; operands whose contiguous dimension is M or N (dgrad's
 //    weight, both wgrad operands) are loaded as 8x8 blocks and transposed in
@@ -57,6 +62,7 @@ enum Path : int {
   kPFP4 = 3,      // NVFP4 operands decoded (x block scale) to BF16, BF16 MFMA, BK = 64
   kPMX8 = 4,      // MX, FP8 elements + UE8M0 scale per 32: block-scaled MFMA, BK = 128
   kPMX4 = 5,      // MX, E2M1 elements + UE8M0 scale per 32: block-scaled MFMA, BK = 256
+  kPFP4D = 6,     // NVFP4 codes in LDS, decoded per fragment to F16 x block scale, F16 MFMA, BK = 256
 };
 
 struct GemmArgs {
@@ -119,6 +125,21 @@ __device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w, float S) {
   const float lo = bitsf(p << 16) * S;
   const float hi = bitsf(p & 0xffff0000u) * S;
   return (fbits(lo) >> 16) | (fbits(hi) & 0xffff0000u);
+}
+
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// Eight E2M1 codes (one dword, lower k in the low nibble) times the E4M3
+// block scale held twice in S -> eight F16 values (four dwords).  E2M1 to F16
+// is exact (hardware conversion at scale 1) and so is the F16 product: at
+// most 6 significant bits, magnitudes 2^-10 .. 2688, all normal in F16.
+__device__ __forceinline__ u32x4 fp4x8_to_f16(uint32_t w, f16x2_t S) {
+  u32x4 o;
+  o[0] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0)) * S);
+  o[1] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1)) * S);
+  o[2] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2)) * S);
+  o[3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3)) * S);
+  return o;
 }
 
 // ---------------------------------------------------------------- loaders
@@ -551,8 +572,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
   __shared__ __align__(16) uint8_t smem[2][2][kOperandBytes];
   constexpr bool kF8 = PATH == kPF8Native || PATH == kPF8Exact || PATH == kPMX8;
   constexpr bool kMX = PATH == kPMX8 || PATH == kPMX4;
-  constexpr int BK = PATH == kPMX4 ? 256 : (kF8 ? 128 : 64);     // K elements per step
-  constexpr int EB = kF8 || PATH == kPMX4 ? 1 : 2;                // row stride unit (bytes for FP4)
+  constexpr bool kFP4 = PATH == kPMX4 || PATH == kPFP4D;
+  constexpr int BK = kFP4 ? 256 : (kF8 ? 128 : 64);               // K elements per step
+  constexpr int EB = kF8 || kFP4 ? 1 : 2;                         // row stride unit (bytes for FP4)
   // fragment reads per step: K-slices of 16 (16-bit), 64 (FP8 native, MX),
   // or pairs of 16-slices (FP8 widened to BF16 in registers)
   constexpr int NS = PATH == kPF8Native || PATH == kPMX8 ? 2 : 4;
@@ -643,6 +665,21 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
       }
     }
   };
+  // NVFP4: this lane's 16 E4M3 block scales of the step (one per 16 K) for
+  // its rows of A and B (16x16 blocks: row / 16)
+  u32x4 nvA[4], nvB[4], nnvA[4], nnvB[4];
+  auto load_nv = [&](int64_t kt, u32x4 (&a)[4], u32x4 (&b)[4]) {
+    if constexpr (PATH == kPFP4D) {
+      const int64_t kc = kt < nk ? kt : nk - 1;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int64_t ra_ = m0 + wm * 128 + mb * 32 + (lane & 31);
+        const int64_t rb_ = n0 + wn * 128 + mb * 32 + (lane & 31);
+        a[mb] = *reinterpret_cast<const u32x4*>(g.sA + (g.s2dA ? ra_ / 16 : ra_) * g.ldsA + kc * 16);
+        b[mb] = *reinterpret_cast<const u32x4*>(g.sB + (g.s2dB ? rb_ / 16 : rb_) * g.ldsB + kc * 16);
+      }
+    }
+  };
   Frag fa[2][4], fb[2][4];
   uint32_t tra[4], trb[4];
 #pragma unroll
@@ -699,12 +736,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
   load_part(0, 0);
   load_part(0, 1);
   load_scales(0, scA, scB);
+  load_nv(0, nvA, nvB);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   frag(smem[0][0], 0, fa[0], fb[0]);
   for (int64_t kt = 0; kt < nk; ++kt) {
     const uint8_t* st = smem[kt & 1][0];
     load_scales(kt + 1, nscA, nscB);
+    load_nv(kt + 1, nnvA, nnvB);
 #pragma unroll
     for (int ks = 0; ks < NS; ++ks) {
       const int cur = ks & 1;
@@ -725,7 +764,35 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
         __syncthreads();
         frag(smem[(kt + 1) & 1][0], 0, fa[cur ^ 1], fb[cur ^ 1]);
       }
-      if constexpr (PATH == kPF8Exact) {
+      if constexpr (PATH == kPFP4D) {
+        // 16 bytes = 32 E2M1 of K per lane (logical chunk c = 2ks + h, NVFP4
+        // blocks 2c and 2c+1 of the step); dword e holds the 8 K values this
+        // lane gives MFMA e, scaled by block 2c + e/2
+        f16x2_t sa2[4], sb2[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          sa2[i] = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(nvA[i][ks] >> (16 * h), 1.0f, false));
+          sb2[i] = __builtin_bit_cast(f16x2_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(nvB[i][ks] >> (16 * h), 1.0f, false));
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          u32x4 da[4], db[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const f16x2_t a2 = e < 2 ? f16x2_t{sa2[i][0], sa2[i][0]} : f16x2_t{sa2[i][1], sa2[i][1]};
+            const f16x2_t b2 = e < 2 ? f16x2_t{sb2[i][0], sb2[i][0]} : f16x2_t{sb2[i][1], sb2[i][1]};
+            da[i] = fp4x8_to_f16(fa[cur][i][e], a2);
+            db[i] = fp4x8_to_f16(fb[cur][i][e], b2);
+          }
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+              acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, da[mb]),
+                                                                   __builtin_bit_cast(f16x8_t, db[nb]),
+                                                                   acc[mb][nb], 0, 0, 0);
+        }
+      } else if constexpr (PATH == kPF8Exact) {
         // 16 FP8 bytes per lane = K 32p + 16h + 8e + j for e = 0, 1: two BF16
         // fragments (the same K order for A and B; products are exact)
         u32x4 da[2][4], db[2][4];
@@ -785,7 +852,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
       // 16 MFMA per slice with the next slice's fragment reads spread evenly
       // (8 reads; 16 for FP8; two per transposed fragment)
       constexpr int kReads = PATH == kPF8Native || PATH == kPMX8 ? 16 : (A_KC ? 4 : 8) + (B_KC ? 4 : 8);
-      if constexpr (PATH != kPF8Exact) {
+      if constexpr (PATH != kPF8Exact && PATH != kPFP4D) {
         if (kSplit && ks < 2) sched_slice<0, kReads, 8>();
         else sched_slice<0, kReads, 0>();
       }
@@ -798,6 +865,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
           scA[mb][w] = nscA[mb][w];
           scB[mb][w] = nscB[mb][w];
         }
+    }
+    if constexpr (PATH == kPFP4D) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        nvA[mb] = nnvA[mb];
+        nvB[mb] = nnvB[mb];
+      }
     }
   }
   const float alpha = (g.alphaA ? *g.alphaA : 1.0f) * (g.alphaB ? *g.alphaB : 1.0f);
@@ -1223,6 +1297,19 @@ hipError_t launch_gemm(int opA, int opB, int64_t M, int64_t N, int64_t K, const 
                       K % 64 == 0 && aligned(g.sA, 2) && aligned(g.sB, 2) && g.ldsA % 2 == 0 &&
                       g.ldsB % 2 == 0;
     if (!fast) return launch_generic<AMP_E2M1X2, AMP_E2M1X2>(g, true, true, ct, s);
+    // full tiles, whole 256-K steps and 16-byte scale rows: codes to LDS by
+    // direct loads, decoded per fragment
+    constexpr int64_t kLim = int64_t(1) << 31;
+    if (M % kBM == 0 && N % kBN == 0 && K % 256 == 0 && lda * kBM < kLim && ldb * kBN < kLim &&
+        aligned(g.sA, 16) && aligned(g.sB, 16) && g.ldsA % 16 == 0 && g.ldsB % 16 == 0) {
+      const dim3 grid(static_cast<unsigned>((M / kBM) * (N / kBN)));
+      switch (ct) {
+        case AMP_F32: gemm_mfma_d2l<AMP_E2M1X2, AMP_E2M1X2, true, true, kPFP4D, AMP_F32><<<grid, kThreads, 0, s>>>(g); break;
+        case AMP_BF16: gemm_mfma_d2l<AMP_E2M1X2, AMP_E2M1X2, true, true, kPFP4D, AMP_BF16><<<grid, kThreads, 0, s>>>(g); break;
+        default: gemm_mfma_d2l<AMP_E2M1X2, AMP_E2M1X2, true, true, kPFP4D, AMP_F16><<<grid, kThreads, 0, s>>>(g); break;
+      }
+      return hipGetLastError();
+    }
     return launch_mfma<AMP_E2M1X2, AMP_E2M1X2, true, true, kPFP4>(g, ct, s);
   }
   if (at == AMP_E4M3 || at == AMP_E5M2) {

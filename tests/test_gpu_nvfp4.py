@@ -88,6 +88,41 @@ def test_nvfp4_wgrad_gemm_parity():
     assert rel < 0.3
 
 
+@pytest.mark.parametrize("ct", [amp.F32, amp.BF16])
+@pytest.mark.parametrize("b2d", [False, True])
+def test_nvfp4_gemm_direct_to_lds_path(ct, b2d):
+    """Full 256x256 tiles, K a multiple of 256 and 16-byte scale rows: the
+    codes travel to LDS by direct loads and each fragment is decoded in
+    registers (E2M1 -> F16 times its E4M3 block scale); B with 16x16 weight
+    blocks or 1x16 blocks; subnormal, zero and maximal block scales; tensor
+    scales in the epilogue."""
+    M, N, K = 512, 256, 768                    # 2 x 1 tiles, 3 K-steps
+    qa, sa, enca = synth.nvfp4_operand(201, M, K)
+    qb, sb, encb = synth.nvfp4_operand(202, N, K)
+    sa[0, :4] = [0x01, 0x07, 0x7E, 0x00]        # 2^-9, 7*2^-9, 448, 0
+    sa[300, 40:44] = [0x08, 0x7E, 0x01, 0x3F]
+    if b2d:
+        sb = sb[: N // 16].copy()
+        sb[3, 10:12] = [0x7E, 0x02]
+    deca = np.float32(1.0) / np.float32(enca)
+    decb = np.float32(1.0) / np.float32(encb)
+    c = empty(M * N * 4)
+    sa_d, sb_d = dev(sa), dev(sb)
+    amp.amp_gemm(amp.OP_N, amp.OP_T, M, N, K, dev(qa), amp.E2M1X2, K // 2, dev(np.array([deca])),
+                 dev(qb), amp.E2M1X2, K // 2, dev(np.array([decb])), c, ct, N,
+                 amp.BlockScales(sa_d.data_ptr(), K // 16, 0, 0),
+                 amp.BlockScales(sb_d.data_ptr(), K // 16, int(b2d), 0))
+    A = ON.dequantize(qa, sa, 1.0) * float(deca)
+    B = ON.dequantize(qb, sb, 1.0, block2d=b2d) * float(decb)
+    cref, bound = OG.reference(A, B.T)
+    if ct == amp.F32:
+        ok = OG.check_f32(host(c, np.float32)[:M * N].reshape(M, N), cref, bound)
+    else:
+        ok = OG.check_rounded(host(c, np.uint16)[:M * N].reshape(M, N), F.BF16, cref, bound)
+    bad = np.argwhere(~ok)
+    assert bad.size == 0, bad[:5]
+
+
 def test_nvfp4_decode_every_code_and_scale_via_identity():
     """C = A @ I over all 16 E2M1 codes times many E4M3 block scales."""
     K = 256

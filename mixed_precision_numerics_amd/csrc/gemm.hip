@@ -57,7 +57,8 @@ constexpr int kOperandBytes = 256 * kRowBytes;       // one operand, one stage
 // How operands travel from HBM to the matrix cores.
 enum Path : int {
   kP16 = 0,       // F16/BF16 operands, BF16/F16 MFMA 32x32x16, BK = 64
-  kPF8Exact = 1,  // FP8 operands decoded to BF16 on the way to LDS, BF16 MFMA, BK = 64
+  kPF8Exact = 1,  // FP8 operands widened exactly to BF16 (gemm_mfma: on the way to LDS, BK = 64;
+                  // gemm_mfma_d2l: FP8 in LDS, per register fragment, BK = 128), BF16 MFMA
   kPF8Native = 2, // FP8 operands in LDS, FP8 MFMA 32x32x64, BK = 128
   kPFP4 = 3,      // NVFP4 operands decoded (x block scale) to BF16, BF16 MFMA, BK = 64
   kPMX8 = 4,      // MX, FP8 elements + UE8M0 scale per 32: block-scaled MFMA, BK = 128

@@ -70,3 +70,22 @@ def cast_values(x_f32_values, out_fmt: F.Fmt, scale: float | None = None):
     x = np.asarray(x_f32_values, dtype=np.float64)
     t = x if scale is None else F.f32(x * F.f32(np.float64(scale)))
     return F.round_to(t, out_fmt)
+
+
+def saturated_count(codes, in_fmt: F.Fmt, out_fmt: F.Fmt, scale: float | None = None) -> int:
+    """Number of elements the saturating cast clips.
+
+    Section 8(b) of the hot-path contract has FP8 saturation counted as data
+    (hwlabs "FP8이 어려운 이유": values beyond the format's range are clipped to
+    it).  Reading: an element is saturated when its scaled value
+    ``t = fl32(x * scale)`` has ``|t| > max_finite`` of the saturating output
+    format (E4M3, E5M2), infinities included; NaN is not a saturation; the
+    IEEE-mode 16-bit formats overflow to inf instead and count nothing."""
+    if not out_fmt.saturate:
+        return 0
+    bits = widen_to_f32_bits(codes, in_fmt)
+    x = F.decode(bits, F.F32)
+    t = x if scale is None else F.f32(x * F.f32(np.float64(scale)))
+    with np.errstate(invalid="ignore"):
+        return int(np.count_nonzero(np.abs(t) > out_fmt.max_finite))
+

@@ -160,3 +160,25 @@ def test_current_scaling_closed_forms():
     assert R.current_scale(0x7FC00000, R.E5M2_MAX) == (1.0, 1.0)
     sc, _ = R.current_scale(bits(100.0), R.E5M2_MAX, 2.0)
     assert sc == float(F.f32(57344.0 / 200.0))
+
+
+def test_saturation_count_closed_forms():
+    """hwlabs "FP8이 어려운 이유": values past the range are clipped; the count
+    is of |fl32(x*scale)| > max (448 for E4M3, 57344 for E5M2), inf included,
+    NaN and the maximum itself excluded."""
+    above = float(np.nextafter(np.float32(448.0), np.float32(1e9)))
+    x = np.array([447.0, 448.0, above, 500.0, np.inf, -np.inf, np.nan, -1000.0, 0.0],
+                 dtype=np.float32)
+    assert C.saturated_count(synth.f32_bits(x), F.F32, F.E4M3) == 5
+    # a power-of-two scale moves the threshold exactly: x * 2 > 448 <=> x > 224
+    y = np.array([224.0, 224.5, -225.0, 100.0], dtype=np.float32)
+    assert C.saturated_count(synth.f32_bits(y), F.F32, F.E4M3, 2.0) == 2
+    assert C.saturated_count(synth.f32_bits(y), F.F32, F.E4M3, 1.0) == 0
+    z = np.array([57344.0, 57345.0, 60000.0, -1e6, 448.0], dtype=np.float32)
+    assert C.saturated_count(synth.f32_bits(z), F.F32, F.E5M2) == 3
+    # 16-bit IEEE outputs overflow to inf instead of saturating
+    assert C.saturated_count(synth.f32_bits(z), F.F32, F.F16) == 0
+    # BF16 input widens exactly: 449.0 is not BF16-representable (448 < 450)
+    b = synth.to_bf16_codes(np.array([449.0, 450.0], dtype=np.float32))
+    assert C.saturated_count(b, F.BF16, F.E4M3) == 1
+

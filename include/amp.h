@@ -149,6 +149,18 @@ int amp_cast(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
              void* y, int yt, int64_t ldy, void* y_t, int64_t ldy_t,
              const float* d_scale, float* d_amax, void* stream);
 
+/* amp_cast_ex -- amp_cast that also counts FP8 saturation.
+ * Source: hwlabs "FP8이 어려운 이유" (values beyond the FP8 range are clipped to
+ * it).  d_sat_count: device unsigned 64-bit counter, add-accumulated (the
+ * caller zeroes it), or NULL: the number of elements whose scaled value
+ * fl32(x * scale) has |t| > 448 (E4M3) or > 57344 (E5M2), infinities
+ * included, NaN not.  FP16/BF16 outputs overflow to inf instead and count
+ * nothing.  Every other argument and rule as amp_cast. */
+int amp_cast_ex(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
+                void* y, int yt, int64_t ldy, void* y_t, int64_t ldy_t,
+                const float* d_scale, float* d_amax, unsigned long long* d_sat_count,
+                void* stream);
+
 /* amp_gemm -- C = out_cast( alpha_A * alpha_B * op(A) @ op(B) ), FP32 accumulate.
  * Sources: itwiki "FP32 누산과 연산별 정밀도"; hwlabs "GEMM 누적 정밀도 문제";
  * marovi "La receta de precisión mixta".

@@ -26,7 +26,7 @@ __all__ = [
     "amp_colsum_f16", "amp_grad_accumulate", "amp_grad_norm_init", "amp_grad_norm_accumulate",
     "amp_clip_coefficient", "amp_optimizer_step_ex", "NORM_STATE_BYTES", "NORM_PARTIALS",
     "amp_cast_current_scaling", "amp_mx_quantize", "GEMM_MX",
-    "amp_quantize_blockwise", "amp_gemm_blockwise",
+    "amp_quantize_blockwise", "amp_gemm_blockwise", "amp_cast_ex",
 ]
 
 F32, F16, BF16, E4M3, E5M2, E2M1X2 = 0, 1, 2, 3, 4, 5
@@ -84,6 +84,7 @@ _SIGS = {
     "amp_status_string": ([_I], ctypes.c_char_p),
     "amp_last_hip_error": ([], _I),
     "amp_cast": ([_P, _I, _I64, _I64, _I64, _P, _I, _I64, _P, _I64, _P, _P, _P], _I),
+    "amp_cast_ex": ([_P, _I, _I64, _I64, _I64, _P, _I, _I64, _P, _I64, _P, _P, _P, _P], _I),
     "amp_gemm": ([_I, _I, _I64, _I64, _I64, _P, _I, _I64, _P, _P, _I, _I64, _P, _P, _I, _I64,
                   _P, _P, _P], _I),
     "amp_gemm_ex": ([_I, _I, _I64, _I64, _I64, _P, _I, _I64, _P, _P, _I, _I64, _P, _P, _I, _I64,
@@ -181,6 +182,13 @@ def amp_cast(x, xt, rows, cols, ldx, y, yt, ldy, y_t=None, ldy_t=0, d_scale=None
     _check("amp_cast", load().amp_cast(_ptr(x), xt, rows, cols, ldx, _ptr(y), yt, ldy,
                                        _ptr(y_t), ldy_t, _ptr(d_scale), _ptr(d_amax),
                                        _stream(stream)))
+
+
+def amp_cast_ex(x, xt, rows, cols, ldx, y, yt, ldy, y_t=None, ldy_t=0, d_scale=None,
+                d_amax=None, d_sat_count=None, stream=None):
+    _check("amp_cast_ex", load().amp_cast_ex(_ptr(x), xt, rows, cols, ldx, _ptr(y), yt, ldy,
+                                             _ptr(y_t), ldy_t, _ptr(d_scale), _ptr(d_amax),
+                                             _ptr(d_sat_count), _stream(stream)))
 
 
 def amp_gemm(opA, opB, M, N, K, A, at, lda, d_alphaA, B, bt, ldb, d_alphaB, C, ct, ldc,

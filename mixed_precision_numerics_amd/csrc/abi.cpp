@@ -76,6 +76,13 @@ int amp_last_hip_error(void) { return g_last_hip_error; }
 int amp_cast(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx, void* y, int yt,
              int64_t ldy, void* y_t, int64_t ldy_t, const float* d_scale, float* d_amax,
              void* stream) {
+  return amp_cast_ex(x, xt, rows, cols, ldx, y, yt, ldy, y_t, ldy_t, d_scale, d_amax, nullptr,
+                     stream);
+}
+
+int amp_cast_ex(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx, void* y, int yt,
+                int64_t ldy, void* y_t, int64_t ldy_t, const float* d_scale, float* d_amax,
+                unsigned long long* d_sat_count, void* stream) {
   if (rows < 0 || cols < 0) return AMP_EINVAL;
   if (!is_cast_in(xt) || !is_cast_out(yt)) return AMP_EUNSUPPORTED;
   if (rows == 0 || cols == 0) return AMP_OK;
@@ -83,7 +90,7 @@ int amp_cast(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx, voi
   if (ldx < cols || (y && ldy < cols) || (y_t && ldy_t < rows)) return AMP_EINVAL;
   if (int st = check_device()) return st;
   return hip_status(amp::launch_cast(x, xt, rows, cols, ldx, y, yt, ldy, y_t, ldy_t, d_scale,
-                                     d_amax, static_cast<hipStream_t>(stream)));
+                                     d_amax, d_sat_count, static_cast<hipStream_t>(stream)));
 }
 
 int amp_cast_current_scaling(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,

@@ -88,15 +88,31 @@ __device__ __forceinline__ void store_one(void* y, int64_t i, uint32_t c) {
   static_cast<typename CodeT<YT>::type*>(y)[i] = static_cast<typename CodeT<YT>::type>(c);
 }
 
+// Saturating (FP8) outputs: elements whose scaled value lies beyond the
+// format's largest magnitude are clipped; the optional counter records them
+// (inf included, NaN not).
+template <int YT> struct SatMax { static constexpr bool on = false; static constexpr float v = 0.0f; };
+template <> struct SatMax<AMP_E4M3> { static constexpr bool on = true; static constexpr float v = 448.0f; };
+template <> struct SatMax<AMP_E5M2> { static constexpr bool on = true; static constexpr float v = 57344.0f; };
+
+// Wave sum of per-lane counts, one 64-bit atomic add per wave (all lanes call).
+__device__ __forceinline__ void add_sat(uint32_t n, unsigned long long* d_sat) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) n += static_cast<uint32_t>(__shfl_xor(static_cast<int>(n), off, kWave));
+  if ((threadIdx.x & (kWave - 1)) == 0 && n != 0) atomicAdd(d_sat, static_cast<unsigned long long>(n));
+}
+
 constexpr int kFlatThreads = 256;
 
-template <int XT, int YT, bool VEC>
+template <int XT, int YT, bool VEC, bool SAT>
 __global__ __launch_bounds__(kFlatThreads) void cast_flat(const void* __restrict__ x,
                                                           void* __restrict__ y, int64_t n,
                                                           const float* __restrict__ d_scale,
-                                                          float* __restrict__ d_amax) {
+                                                          float* __restrict__ d_amax,
+                                                          unsigned long long* __restrict__ d_sat) {
   __shared__ uint32_t red[kFlatThreads / kWave];
   const bool SCALE = d_scale != nullptr, AMAX = d_amax != nullptr;
+  uint32_t ns = 0;
   const float scale = SCALE ? *d_scale : 1.0f;
   uint32_t am = 0;
   const int64_t tid = static_cast<int64_t>(blockIdx.x) * kFlatThreads + threadIdx.x;
@@ -110,22 +126,29 @@ __global__ __launch_bounds__(kFlatThreads) void cast_flat(const void* __restrict
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         if (AMAX) { const uint32_t a = fbits(v[k]) & 0x7fffffffu; am = am > a ? am : a; }
-        c[k] = to_code<YT>(SCALE ? v[k] * scale : v[k]);
+        const float t = SCALE ? v[k] * scale : v[k];
+        if constexpr (SAT) ns += fabsf(t) > SatMax<YT>::v;
+        c[k] = to_code<YT>(t);
       }
       store8<YT>(y, j * 8, c);
     }
     for (int64_t i = nv * 8 + tid; i < n; i += nthr) {
       const float v = load_one<XT>(x, i);
       if (AMAX) { const uint32_t a = fbits(v) & 0x7fffffffu; am = am > a ? am : a; }
-      store_one<YT>(y, i, to_code<YT>(SCALE ? v * scale : v));
+      const float t = SCALE ? v * scale : v;
+      if constexpr (SAT) ns += fabsf(t) > SatMax<YT>::v;
+      store_one<YT>(y, i, to_code<YT>(t));
     }
   } else {
     for (int64_t i = tid; i < n; i += nthr) {
       const float v = load_one<XT>(x, i);
       if (AMAX) { const uint32_t a = fbits(v) & 0x7fffffffu; am = am > a ? am : a; }
-      store_one<YT>(y, i, to_code<YT>(SCALE ? v * scale : v));
+      const float t = SCALE ? v * scale : v;
+      if constexpr (SAT) ns += fabsf(t) > SatMax<YT>::v;
+      store_one<YT>(y, i, to_code<YT>(t));
     }
   }
+  if constexpr (SAT) add_sat(ns, d_sat);
   if (AMAX) {
     am = block_max_u32<kFlatThreads>(am, red);
     if (threadIdx.x == 0 && am != 0)
@@ -141,17 +164,19 @@ constexpr int kTileThreads = 256;
 // and every access is 16-byte aligned (checked on the host).
 __device__ __forceinline__ int swz8(int c) { return (2 * (c >> 4)) & 14; }
 
-template <int XT, int YT, bool WY, bool WYT, bool VEC>
+template <int XT, int YT, bool WY, bool WYT, bool VEC, bool SAT>
 __global__ __launch_bounds__(kTileThreads) void cast_tile(
     const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
     void* __restrict__ y, int64_t ldy, void* __restrict__ y_t, int64_t ldy_t,
-    const float* __restrict__ d_scale, float* __restrict__ d_amax) {
+    const float* __restrict__ d_scale, float* __restrict__ d_amax,
+    unsigned long long* __restrict__ d_sat) {
   using Code = typename CodeT<YT>::type;
   constexpr int kPitch = kTile + 16 / static_cast<int>(sizeof(Code));  // row pitch in codes
   __shared__ __align__(16) Code lds[WYT ? kTile * kPitch : 1];
   __shared__ uint32_t red[kTileThreads / kWave];
 
   const bool SCALE = d_scale != nullptr, AMAX = d_amax != nullptr;
+  uint32_t ns = 0;
   const float scale = SCALE ? *d_scale : 1.0f;
   const int64_t r_base = static_cast<int64_t>(blockIdx.y) * kTile;
   const int64_t c_base = static_cast<int64_t>(blockIdx.x) * kTile;
@@ -176,7 +201,10 @@ __global__ __launch_bounds__(kTileThreads) void cast_tile(
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (AMAX) { const uint32_t a = fbits(v[j]) & 0x7fffffffu; am = am > a ? am : a; }
-      code[i][j] = to_code<YT>(SCALE ? v[j] * scale : v[j]);
+      const float t = SCALE ? v[j] * scale : v[j];
+      // padding outside the tensor is 0 and never counts
+      if constexpr (SAT) ns += fabsf(t) > SatMax<YT>::v;
+      code[i][j] = to_code<YT>(t);
     }
     if constexpr (WY) {
       if (full) {
@@ -235,16 +263,17 @@ __global__ __launch_bounds__(kTileThreads) void cast_tile(
     }
   }
 
+  if constexpr (SAT) add_sat(ns, d_sat);
   if (AMAX) {
     am = block_max_u32<kTileThreads>(am, red);
     if (t == 0 && am != 0) atomicMax(reinterpret_cast<unsigned int*>(d_amax), canon_amax(am));
   }
 }
 
-template <int XT, int YT>
-hipError_t dispatch_layout(const void* x, int64_t rows, int64_t cols, int64_t ldx, void* y,
-                           int64_t ldy, void* y_t, int64_t ldy_t, const float* d_scale,
-                           float* d_amax, hipStream_t s) {
+template <int XT, int YT, bool SAT>
+hipError_t dispatch_layout_t(const void* x, int64_t rows, int64_t cols, int64_t ldx, void* y,
+                             int64_t ldy, void* y_t, int64_t ldy_t, const float* d_scale,
+                             float* d_amax, unsigned long long* d_sat, hipStream_t s) {
   const int xb = dtype_bytes(XT), yb = dtype_bytes(YT);
   if (y_t == nullptr && ldx == cols && ldy == cols) {
     const int64_t n = rows * cols;
@@ -253,11 +282,11 @@ hipError_t dispatch_layout(const void* x, int64_t rows, int64_t cols, int64_t ld
     if (blocks > 256 * 64) blocks = 256 * 64;
     if (blocks < 1) blocks = 1;
     if (vec)
-      cast_flat<XT, YT, true><<<dim3(static_cast<unsigned>(blocks)), kFlatThreads, 0, s>>>(
-          x, y, n, d_scale, d_amax);
+      cast_flat<XT, YT, true, SAT><<<dim3(static_cast<unsigned>(blocks)), kFlatThreads, 0, s>>>(
+          x, y, n, d_scale, d_amax, d_sat);
     else
-      cast_flat<XT, YT, false><<<dim3(static_cast<unsigned>(blocks)), kFlatThreads, 0, s>>>(
-          x, y, n, d_scale, d_amax);
+      cast_flat<XT, YT, false, SAT><<<dim3(static_cast<unsigned>(blocks)), kFlatThreads, 0, s>>>(
+          x, y, n, d_scale, d_amax, d_sat);
     return hipGetLastError();
   }
   // the vector path needs every row start 16-byte aligned for x and the outputs
@@ -267,8 +296,8 @@ hipError_t dispatch_layout(const void* x, int64_t rows, int64_t cols, int64_t ld
   const dim3 grid(static_cast<unsigned>((cols + kTile - 1) / kTile),
                   static_cast<unsigned>((rows + kTile - 1) / kTile));
 #define AMP_TILE(WY, WYT, V) \
-  cast_tile<XT, YT, WY, WYT, V><<<grid, kTileThreads, 0, s>>>( \
-      x, rows, cols, ldx, y, ldy, y_t, ldy_t, d_scale, d_amax)
+  cast_tile<XT, YT, WY, WYT, V, SAT><<<grid, kTileThreads, 0, s>>>( \
+      x, rows, cols, ldx, y, ldy, y_t, ldy_t, d_scale, d_amax, d_sat)
   if (y && y_t) { if (vec) AMP_TILE(true, true, true); else AMP_TILE(true, true, false); }
   else if (y)   { if (vec) AMP_TILE(true, false, true); else AMP_TILE(true, false, false); }
   else          { if (vec) AMP_TILE(false, true, true); else AMP_TILE(false, true, false); }
@@ -276,15 +305,30 @@ hipError_t dispatch_layout(const void* x, int64_t rows, int64_t cols, int64_t ld
   return hipGetLastError();
 }
 
+// The saturation counter is a separate instantiation (FP8 outputs only), so
+// the plain cast carries no counting code.
+template <int XT, int YT>
+hipError_t dispatch_layout(const void* x, int64_t rows, int64_t cols, int64_t ldx, void* y,
+                           int64_t ldy, void* y_t, int64_t ldy_t, const float* d_scale,
+                           float* d_amax, unsigned long long* d_sat, hipStream_t s) {
+  if constexpr (SatMax<YT>::on) {
+    if (d_sat)
+      return dispatch_layout_t<XT, YT, true>(x, rows, cols, ldx, y, ldy, y_t, ldy_t, d_scale,
+                                             d_amax, d_sat, s);
+  }
+  return dispatch_layout_t<XT, YT, false>(x, rows, cols, ldx, y, ldy, y_t, ldy_t, d_scale, d_amax,
+                                          nullptr, s);
+}
+
 template <int XT>
 hipError_t dispatch_out(int yt, const void* x, int64_t rows, int64_t cols, int64_t ldx, void* y,
                         int64_t ldy, void* y_t, int64_t ldy_t, const float* d_scale,
-                        float* d_amax, hipStream_t s) {
+                        float* d_amax, unsigned long long* d_sat, hipStream_t s) {
   switch (yt) {
-    case AMP_F16: return dispatch_layout<XT, AMP_F16>(x, rows, cols, ldx, y, ldy, y_t, ldy_t, d_scale, d_amax, s);
-    case AMP_BF16: return dispatch_layout<XT, AMP_BF16>(x, rows, cols, ldx, y, ldy, y_t, ldy_t, d_scale, d_amax, s);
-    case AMP_E4M3: return dispatch_layout<XT, AMP_E4M3>(x, rows, cols, ldx, y, ldy, y_t, ldy_t, d_scale, d_amax, s);
-    default: return dispatch_layout<XT, AMP_E5M2>(x, rows, cols, ldx, y, ldy, y_t, ldy_t, d_scale, d_amax, s);
+    case AMP_F16: return dispatch_layout<XT, AMP_F16>(x, rows, cols, ldx, y, ldy, y_t, ldy_t, d_scale, d_amax, d_sat, s);
+    case AMP_BF16: return dispatch_layout<XT, AMP_BF16>(x, rows, cols, ldx, y, ldy, y_t, ldy_t, d_scale, d_amax, d_sat, s);
+    case AMP_E4M3: return dispatch_layout<XT, AMP_E4M3>(x, rows, cols, ldx, y, ldy, y_t, ldy_t, d_scale, d_amax, d_sat, s);
+    default: return dispatch_layout<XT, AMP_E5M2>(x, rows, cols, ldx, y, ldy, y_t, ldy_t, d_scale, d_amax, d_sat, s);
   }
 }
 
@@ -554,11 +598,11 @@ hipError_t dispatch_bw_out(int yt, const void* x, int64_t rows, int64_t cols, in
 
 hipError_t launch_cast(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx, void* y,
                        int yt, int64_t ldy, void* y_t, int64_t ldy_t, const float* d_scale,
-                       float* d_amax, hipStream_t s) {
+                       float* d_amax, unsigned long long* d_sat, hipStream_t s) {
   switch (xt) {
-    case AMP_F32: return dispatch_out<AMP_F32>(yt, x, rows, cols, ldx, y, ldy, y_t, ldy_t, d_scale, d_amax, s);
-    case AMP_BF16: return dispatch_out<AMP_BF16>(yt, x, rows, cols, ldx, y, ldy, y_t, ldy_t, d_scale, d_amax, s);
-    default: return dispatch_out<AMP_F16>(yt, x, rows, cols, ldx, y, ldy, y_t, ldy_t, d_scale, d_amax, s);
+    case AMP_F32: return dispatch_out<AMP_F32>(yt, x, rows, cols, ldx, y, ldy, y_t, ldy_t, d_scale, d_amax, d_sat, s);
+    case AMP_BF16: return dispatch_out<AMP_BF16>(yt, x, rows, cols, ldx, y, ldy, y_t, ldy_t, d_scale, d_amax, d_sat, s);
+    default: return dispatch_out<AMP_F16>(yt, x, rows, cols, ldx, y, ldy, y_t, ldy_t, d_scale, d_amax, d_sat, s);
   }
 }
 
@@ -583,7 +627,7 @@ hipError_t launch_cast_current(const void* x, int xt, int64_t rows, int64_t cols
 #undef AMP_AMAX
   current_scale_kernel<<<1, 64, 0, s>>>(meta, fp8_max, margin);
   if (hipError_t e = hipGetLastError()) return e;
-  return launch_cast(x, xt, rows, cols, ldx, y, yt, ldy, y_t, ldy_t, &meta->scale, nullptr, s);
+  return launch_cast(x, xt, rows, cols, ldx, y, yt, ldy, y_t, ldy_t, &meta->scale, nullptr, nullptr, s);
 }
 
 hipError_t launch_quantize_blockwise(const void* x, int xt, int64_t rows, int64_t cols,

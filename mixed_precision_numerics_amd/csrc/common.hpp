@@ -59,7 +59,8 @@ inline bool aligned(const void* p, uintptr_t a) {
 // hipError_t of the launch.
 hipError_t launch_cast(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
                        void* y, int yt, int64_t ldy, void* y_t, int64_t ldy_t,
-                       const float* d_scale, float* d_amax, hipStream_t s);
+                       const float* d_scale, float* d_amax, unsigned long long* d_sat,
+                       hipStream_t s);
 hipError_t launch_cast_current(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
                                void* y, int yt, int64_t ldy, void* y_t, int64_t ldy_t,
                                float fp8_max, float margin, amp_fp8_meta* meta, hipStream_t s);

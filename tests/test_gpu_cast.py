@@ -195,3 +195,32 @@ def test_current_scaling_degenerate(fill):
     assert m["scale"] == 1.0 and m["scale_inv"] == 1.0
     want, _ = OC.cast(codes, F.BF16, F.E4M3, 1.0)
     assert np.array_equal(host(y, np.uint8)[:n], want)
+
+
+@pytest.mark.parametrize("yt", [amp.E4M3, amp.E5M2, amp.F16])
+@pytest.mark.parametrize("layout", ["flat", "tile", "tile_t"])
+def test_cast_saturation_count(yt, layout):
+    """amp_cast_ex counts the clipped elements (oracle.cast.saturated_count):
+    flat path, strided tile path, and tile path with the transposed copy."""
+    rows, cols = 300, 200
+    x = synth.student_t_f32(140 + yt, (rows, cols), 3.0, 150.0)
+    x[3, 5] = np.inf
+    x[4, 6] = np.nan
+    x[7, :] = 448.0
+    xc = synth.to_bf16_codes(x)
+    ldx = cols if layout == "flat" else cols + 8
+    buf = np.zeros((rows, ldx), np.uint16)
+    buf[:, :cols] = xc
+    scale = np.float32(1.5)
+    yb = 1 if yt != amp.F16 else 2
+    y = empty(rows * ldx * yb)
+    y_t = empty(rows * cols * yb) if layout == "tile_t" else None
+    sat = empty(8)
+    amp.amp_cast_ex(dev(buf), amp.BF16, rows, cols, ldx, y, yt, ldx, y_t, rows if y_t is not None else 0,
+                    dev(np.array([scale])), None, sat)
+    want = OC.saturated_count(xc, F.BF16, {amp.E4M3: F.E4M3, amp.E5M2: F.E5M2, amp.F16: F.F16}[yt],
+                              float(scale))
+    assert int(host(sat, np.uint64)[0]) == want
+    if yt == amp.E4M3:
+        assert want > 100
+

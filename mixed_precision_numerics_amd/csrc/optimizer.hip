@@ -317,12 +317,13 @@ __global__ __launch_bounds__(kThreads) void delayed_update_kernel(amp_fp8_meta* 
 
 template <int GT>
 __device__ __forceinline__ void widen8(const void* g, int64_t j, float (&x)[8]) {
+  // gradients are read once: non-temporal loads (as in the overflow sweep)
   if constexpr (GT == AMP_F32) {
-    const f32x4 a = reinterpret_cast<const f32x4*>(g)[2 * j];
-    const f32x4 b = reinterpret_cast<const f32x4*>(g)[2 * j + 1];
+    const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g) + 2 * j);
+    const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g) + 2 * j + 1);
     x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
   } else {
-    const u32x4 w = reinterpret_cast<const u32x4*>(g)[j];
+    const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(g) + j);
     const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int q = 0; q < 4; ++q) {

@@ -89,3 +89,25 @@ def saturated_count(codes, in_fmt: F.Fmt, out_fmt: F.Fmt, scale: float | None = 
     with np.errstate(invalid="ignore"):
         return int(np.count_nonzero(np.abs(t) > out_fmt.max_finite))
 
+
+def found_inf_from_amax(amax_bits_list, out_fmt: F.Fmt, scale: float | None = None) -> bool:
+    """Overflow flag of gradients that a scaled cast produced, from the amax
+    values that cast recorded (the hot-path contract's producer-flag option for
+    the unscale + check step; itwiki "손실 스케일링": a step with any inf/NaN
+    gradient is skipped).
+
+    Reading: rounding is monotone in |t|, so some output of the cast is
+    non-finite exactly when the largest input magnitude gives one: the flag is
+    set if an amax is NaN or inf, or, for the IEEE-mode 16-bit formats, if
+    ``round_fmt(fl32(amax * scale))`` is infinite.  Saturating formats (FP8)
+    clip finite values, so only a non-finite amax sets it there."""
+    for ab in amax_bits_list:
+        a = float(F.from_f32_bits(np.uint32(int(ab))))
+        if not np.isfinite(a):
+            return True
+        if not out_fmt.saturate:
+            t = a if scale is None else float(F.f32(a * float(F.f32(np.float64(scale)))))
+            if not np.isfinite(F.round_to(np.array([t]), out_fmt)[0]):
+                return True
+    return False
+

@@ -182,3 +182,28 @@ def test_saturation_count_closed_forms():
     b = synth.to_bf16_codes(np.array([449.0, 450.0], dtype=np.float32))
     assert C.saturated_count(b, F.BF16, F.E4M3) == 1
 
+
+def test_found_inf_from_amax_matches_the_cast_outputs():
+    """The flag derived from the recorded amax equals the check of the cast's
+    own outputs (oracle.adamw.found_inf), over tensors around the FP16 and
+    BF16 overflow thresholds, with and without a scale, with inf and NaN."""
+    from oracle import adamw as OA
+    rng = np.random.default_rng(7)
+    cases = 0
+    for peak in (1.0, 6.55e4, 65519.0, 65520.0, 7e4, 3.3e38, 3.4e38, np.inf, np.nan):
+        for scale in (None, 0.5, 2.0):
+            x = (rng.standard_normal(257) * 10).astype(np.float32)
+            x[17] = peak
+            for out in (F.F16, F.BF16):
+                codes, am = C.cast(synth.f32_bits(x), F.F32, out, scale)
+                want = OA.found_inf(codes, out)
+                assert C.found_inf_from_amax([am], out, scale) == want, (peak, scale, out.name)
+                cases += int(want)
+            codes8, am8 = C.cast(synth.f32_bits(x), F.F32, F.E4M3, scale)
+            assert C.found_inf_from_amax([am8], F.E4M3, scale) == (not np.isfinite(peak))
+    assert cases > 10
+    # closed forms at the FP16 threshold: 65519 rounds to 65504, 65520 to inf
+    assert not C.found_inf_from_amax([int(synth.f32_bits(np.array([65519.0], np.float32))[0])], F.F16)
+    assert C.found_inf_from_amax([int(synth.f32_bits(np.array([65520.0], np.float32))[0])], F.F16)
+    assert C.found_inf_from_amax([0, 0x7FC00000], F.F16)
+

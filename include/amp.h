@@ -248,6 +248,19 @@ int amp_optimizer_step(float* master, float* m, float* v, const void* grads, int
 int amp_check_overflow(const void* x, int xt, int64_t n, amp_scaler_state* d_state,
                        void* stream);
 
+/* amp_found_inf_from_amax -- the overflow flag taken from the producer of the
+ * gradients instead of a sweep over them (then amp_optimizer_step with
+ * AMP_OPT_SKIP_CHECK is a single 28 B/parameter pass).  Source: itwiki
+ * "손실 스케일링" (a step with any inf/NaN gradient is skipped).
+ * d_amax: n device floats, the amax values that amp_cast recorded while
+ * writing the gradients as yt in {F16, BF16, E4M3, E5M2} with the device
+ * scale d_scale (NULL: 1).  Sets d_state->found_inf = 1 if an amax is inf or
+ * NaN or, for F16/BF16, if round_yt(fl32(amax * scale)) is infinite --
+ * exactly when some output of that cast is non-finite, since rounding is
+ * monotone in |t|.  Never clears the flag. */
+int amp_found_inf_from_amax(const float* d_amax, int32_t n, int yt, const float* d_scale,
+                            amp_scaler_state* d_state, void* stream);
+
 /* amp_scaler_update -- on found_inf: scale *= backoff, tracker = 0; else
  * tracker += 1 and at growth_interval: scale *= growth, tracker = 0.  Then
  * found_inf = 0.  No floor on the scale.  p == NULL uses (2, 0.5, 2000). */

@@ -27,6 +27,7 @@ __all__ = [
     "amp_clip_coefficient", "amp_optimizer_step_ex", "NORM_STATE_BYTES", "NORM_PARTIALS",
     "amp_cast_current_scaling", "amp_mx_quantize", "GEMM_MX",
     "amp_quantize_blockwise", "amp_gemm_blockwise", "amp_cast_ex",
+    "amp_found_inf_from_amax",
 ]
 
 F32, F16, BF16, E4M3, E5M2, E2M1X2 = 0, 1, 2, 3, 4, 5
@@ -84,6 +85,7 @@ _SIGS = {
     "amp_status_string": ([_I], ctypes.c_char_p),
     "amp_last_hip_error": ([], _I),
     "amp_cast": ([_P, _I, _I64, _I64, _I64, _P, _I, _I64, _P, _I64, _P, _P, _P], _I),
+    "amp_found_inf_from_amax": ([_P, ctypes.c_int32, _I, _P, _P, _P], _I),
     "amp_cast_ex": ([_P, _I, _I64, _I64, _I64, _P, _I, _I64, _P, _I64, _P, _P, _P, _P], _I),
     "amp_gemm": ([_I, _I, _I64, _I64, _I64, _P, _I, _I64, _P, _P, _I, _I64, _P, _P, _I, _I64,
                   _P, _P, _P], _I),
@@ -182,6 +184,11 @@ def amp_cast(x, xt, rows, cols, ldx, y, yt, ldy, y_t=None, ldy_t=0, d_scale=None
     _check("amp_cast", load().amp_cast(_ptr(x), xt, rows, cols, ldx, _ptr(y), yt, ldy,
                                        _ptr(y_t), ldy_t, _ptr(d_scale), _ptr(d_amax),
                                        _stream(stream)))
+
+
+def amp_found_inf_from_amax(d_amax, n, yt, d_scale, d_state, stream=None):
+    _check("amp_found_inf_from_amax", load().amp_found_inf_from_amax(
+        _ptr(d_amax), n, yt, _ptr(d_scale), _ptr(d_state), _stream(stream)))
 
 
 def amp_cast_ex(x, xt, rows, cols, ldx, y, yt, ldy, y_t=None, ldy_t=0, d_scale=None,

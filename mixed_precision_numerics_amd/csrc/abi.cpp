@@ -180,6 +180,17 @@ int amp_check_overflow(const void* x, int xt, int64_t n, amp_scaler_state* d_sta
   return hip_status(amp::launch_check_overflow(x, xt, n, d_state, static_cast<hipStream_t>(stream)));
 }
 
+int amp_found_inf_from_amax(const float* d_amax, int32_t n, int yt, const float* d_scale,
+                            amp_scaler_state* d_state, void* stream) {
+  if (n < 0 || !d_state) return AMP_EINVAL;
+  if (yt != AMP_F16 && yt != AMP_BF16 && !is_fp8(yt)) return AMP_EUNSUPPORTED;
+  if (n == 0) return AMP_OK;
+  if (!d_amax) return AMP_EINVAL;
+  if (int e = check_device()) return e;
+  return hip_status(amp::launch_found_inf_from_amax(d_amax, n, yt, d_scale, d_state,
+                                                    static_cast<hipStream_t>(stream)));
+}
+
 int amp_optimizer_step_ex(float* master, float* m, float* v, const void* grads, int gt,
                           void* w16, int wt, int64_t n, const amp_adamw_hparams* hp,
                           amp_scaler_state* d_state, const float* d_grad_mult, int flags,

@@ -68,6 +68,8 @@ hipError_t launch_quantize_blockwise(const void* x, int xt, int64_t rows, int64_
                                      int64_t ldx, int yt, int block, uint8_t* q, int64_t ldq,
                                      float* s, int64_t lds, uint8_t* qt, int64_t ldqt, float* st,
                                      int64_t ldst, hipStream_t hs);
+hipError_t launch_found_inf_from_amax(const float* amax, int32_t n, int yt, const float* d_scale,
+                                      amp_scaler_state* st, hipStream_t s);
 hipError_t launch_check_overflow(const void* g, int gt, int64_t n, amp_scaler_state* st,
                                  hipStream_t s);
 hipError_t launch_optimizer_apply(float* master, float* m, float* v, const void* g, int gt,

@@ -505,7 +505,39 @@ hipError_t launch_apply_g(float* th, float* m, float* v, const void* g, void* w,
   return launch_apply_m<GT, false>(th, m, v, g, w, wt, n, hp, st, mult, s);
 }
 
+// Overflow flag from the amax values a producing cast recorded: one thread
+// per value.  Rounding is monotone in |t|, so the largest magnitude decides
+// whether any output of that cast is non-finite.
+template <int YT>
+__global__ void flag_from_amax_kernel(const float* __restrict__ amax, int32_t n,
+                                      const float* __restrict__ d_scale,
+                                      amp_scaler_state* __restrict__ st) {
+  const int i = static_cast<int>(blockIdx.x) * 64 + static_cast<int>(threadIdx.x);
+  if (i >= n) return;
+  const uint32_t b = fbits(amax[i]) & 0x7fffffffu;
+  bool bad = b >= 0x7f800000u;                    // an inf or NaN input
+  if constexpr (YT == AMP_F16 || YT == AMP_BF16) {
+    if (!bad) {
+      const float t = d_scale ? bitsf(b) * *d_scale : bitsf(b);
+      if constexpr (YT == AMP_F16) bad = (f32_to_f16(t) & 0x7c00u) == 0x7c00u;
+      else bad = (f32_to_bf16(t) & 0x7f80u) == 0x7f80u;
+    }
+  }
+  if (bad) st->found_inf = 1;
+}
+
 }  // namespace
+
+hipError_t launch_found_inf_from_amax(const float* amax, int32_t n, int yt, const float* d_scale,
+                                      amp_scaler_state* st, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>((n + 63) / 64));
+  switch (yt) {
+    case AMP_F16: flag_from_amax_kernel<AMP_F16><<<grid, 64, 0, s>>>(amax, n, d_scale, st); break;
+    case AMP_BF16: flag_from_amax_kernel<AMP_BF16><<<grid, 64, 0, s>>>(amax, n, d_scale, st); break;
+    default: flag_from_amax_kernel<AMP_E4M3><<<grid, 64, 0, s>>>(amax, n, d_scale, st); break;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_check_overflow(const void* g, int gt, int64_t n, amp_scaler_state* st,
                                  hipStream_t s) {

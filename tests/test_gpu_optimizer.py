@@ -158,3 +158,65 @@ def test_delayed_scaling_update(algo, hist_len):
     hist = host(hd, np.uint32).reshape(nm, hist_len)
     for i in range(nm):
         assert np.array_equal(hist[i], om[i].history_bits)
+
+
+@pytest.mark.parametrize("yt", [amp.F16, amp.BF16, amp.E4M3])
+@pytest.mark.parametrize("scale", [None, 0.5, 2.0])
+def test_found_inf_from_amax_matches_the_cast_outputs(yt, scale):
+    """amp_found_inf_from_amax on the amax values amp_cast recorded equals the
+    oracle's check of the oracle's cast outputs of the same inputs."""
+    yf = {amp.F16: F.F16, amp.BF16: F.BF16, amp.E4M3: F.E4M3}[yt]
+    from oracle import cast as OC
+    for peak in (1.0, 65519.0, 65520.0, 7e4, 3.4e38, np.inf, np.nan):
+        tensors = [synth.normal_f32(300 + k, 4099, 10.0) for k in range(3)]
+        tensors[1] = tensors[1].copy()
+        tensors[1][77] = peak
+        amax = empty(4 * len(tensors))
+        amax.zero_()
+        st_d = empty(40)
+        amp.amp_scaler_init(st_d, 1.0)
+        want = False
+        for k, x in enumerate(tensors):
+            y = empty(x.size * 2)
+            amp.amp_cast(dev(x), amp.F32, 1, x.size, x.size, y, yt, x.size, None, 0,
+                         None if scale is None else dev(np.array([scale], np.float32)),
+                         amax[4 * k:4 * k + 4])
+            codes, _ = OC.cast(synth.f32_bits(x), F.F32, yf, scale)
+            want |= OA.found_inf(codes, yf) if yt != amp.E4M3 else not np.all(np.isfinite(x))
+        amp.amp_found_inf_from_amax(amax, len(tensors), yt,
+                                    None if scale is None else dev(np.array([scale], np.float32)), st_d)
+        assert bool(scaler_state(st_d)["found_inf"]) == want, (peak, scale)
+
+
+@pytest.mark.parametrize("overflow", [False, True])
+def test_single_pass_step_with_the_producer_flag(overflow):
+    """FP32 gradients cast to FP16 by amp_cast (recording amax), the flag from
+    that amax, and one optimizer pass with SKIP_CHECK: the same state as the
+    oracle's checked step on the oracle's cast of the same gradients."""
+    from oracle import cast as OC
+    n = (1 << 18) + 3
+    S = 1024.0
+    hp_o = OA.AdamWHParams(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1)
+    hp = amp.AdamWHParams(hp_o.lr, hp_o.beta1, hp_o.beta2, hp_o.eps, hp_o.weight_decay)
+    theta0 = synth.normal_f32(11, n, 0.02)
+    g32 = (synth.normal_f32(12, n, 1e-3) * np.float32(S)).astype(np.float32)
+    if overflow:
+        g32[n // 2] = 7e4                      # finite in FP32, inf in FP16
+    th_d = dev(theta0); m_d = dev(np.zeros(n, np.float32)); v_d = dev(np.zeros(n, np.float32))
+    w_d = empty(2 * n); g16_d = empty(2 * n); amax = empty(4); amax.zero_()
+    st_d = empty(40)
+    amp.amp_scaler_init(st_d, S)
+    amp.amp_cast(dev(g32), amp.F32, 1, n, n, g16_d, amp.F16, n, None, 0, None, amax)
+    amp.amp_found_inf_from_amax(amax, 1, amp.F16, None, st_d)
+    amp.amp_optimizer_step(th_d, m_d, v_d, g16_d, amp.F16, w_d, amp.F16, n, hp, st_d,
+                           flags=amp.OPT_SKIP_CHECK)
+    codes, _ = OC.cast(synth.f32_bits(g32), F.F32, F.F16, None)
+    th, m, v, w, applied = OA.apply(theta0.astype(np.float64), np.zeros(n), np.zeros(n), codes,
+                                    F.F16, hp_o, OA.AdamCounters(), S)
+    assert applied == (not overflow)
+    assert bool(scaler_state(st_d)["found_inf"]) == overflow
+    assert np.array_equal(host(th_d, np.float32).astype(np.float64), th)
+    assert np.array_equal(host(m_d, np.float32).astype(np.float64), m)
+    assert np.array_equal(host(v_d, np.float32).astype(np.float64), v)
+    if applied:
+        assert np.array_equal(host(w_d, np.uint16), w)

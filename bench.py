@@ -284,6 +284,28 @@ def _timed(torch, f, reps):
     return s.elapsed_time(e) / reps
 
 
+def _timed_rot(torch, fns, reps):
+    """Mean time of one call when the calls rotate over the given closures
+    (distinct buffers totalling more than the 256 MB Infinity Cache, so that
+    every call reads from HBM)."""
+    for f in fns:
+        f()
+    torch.cuda.synchronize()
+    s = torch.cuda.Event(enable_timing=True)
+    e = torch.cuda.Event(enable_timing=True)
+    s.record()
+    for i in range(reps):
+        fns[i % len(fns)]()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / reps
+
+
+def _copies(need_bytes, each_bytes, lo=4):
+    """Number of buffer sets needed for a working set above 1 GiB."""
+    return max(lo, -(-need_bytes // each_bytes))
+
+
 def cast_t_workload(torch, amp):
     """BF16 -> E5M2 of an FFN output gradient [8192 x 28672] with its
     transposed copy (the dgrad and wgrad operands) and amax: 4 B/elem."""
@@ -364,21 +386,26 @@ def scaling_workload(torch, amp):
     gen = torch.Generator(device="cuda").manual_seed(9)
     for name, R, C, yt, fmax in (("x_e4m3", 8192, 4096, amp.E4M3, 448.0),
                                  ("dy_e5m2", 8192, 28672, amp.E5M2, 57344.0)):
-        x = torch.randn(R, C, device="cuda", generator=gen).to(torch.bfloat16)
-        y = torch.empty(R * C, device="cuda", dtype=torch.uint8)
-        y_t = torch.empty(R * C, device="cuda", dtype=torch.uint8)
+        # rotate over enough input/output sets to exceed 1 GiB
+        k = _copies(1 << 30, 4 * R * C)
+        xs = [torch.randn(R, C, device="cuda", generator=gen).to(torch.bfloat16) for _ in range(k)]
+        ys = [torch.empty(R * C, device="cuda", dtype=torch.uint8) for _ in range(k)]
+        yts = [torch.empty(R * C, device="cuda", dtype=torch.uint8) for _ in range(k)]
         meta = torch.empty(16, device="cuda", dtype=torch.uint8)
         hist = torch.empty(4 * 1024, device="cuda", dtype=torch.uint8)
         amp.amp_fp8_meta_init(meta, hist, 1, 1024)
         r = amp.DelayedRecipe(fmax, 1.0, 1024, amp.AMAX_MAX)
         mp = meta.data_ptr()
-        d_ms = _timed(torch, lambda: amp.amp_cast(x, amp.BF16, R, C, C, y, yt, C, y_t, R, mp + 4, mp),
-                      10)
-        c_ms = _timed(torch, lambda: amp.amp_cast_current_scaling(x, amp.BF16, R, C, C, y, yt, C,
-                                                                  y_t, R, r, meta), 10)
+        dl = [lambda i=i: amp.amp_cast(xs[i], amp.BF16, R, C, C, ys[i], yt, C, yts[i], R, mp + 4, mp)
+              for i in range(k)]
+        cl = [lambda i=i: amp.amp_cast_current_scaling(xs[i], amp.BF16, R, C, C, ys[i], yt, C, yts[i],
+                                                       R, r, meta) for i in range(k)]
+        d_ms = _timed_rot(torch, dl, 4 * k)
+        c_ms = _timed_rot(torch, cl, 4 * k)
         out[name] = {"delayed_ms": round(d_ms, 4), "current_ms": round(c_ms, 4),
-                     "current_over_delayed": round(c_ms / d_ms, 3)}
-        del x, y, y_t
+                     "current_over_delayed": round(c_ms / d_ms, 3),
+                     "working_set_gib": round(k * 4 * R * C / 2**30, 2)}
+        del xs, ys, yts
     torch.cuda.empty_cache()
     return out
 
@@ -423,7 +450,13 @@ def mx_workload(torch, amp):
         qw = torch.empty(O * I // div, device="cuda", dtype=torch.uint8)
         sx = torch.empty(T * I // 32, device="cuda", dtype=torch.uint8)
         sw = torch.empty(O * I // 32, device="cuda", dtype=torch.uint8)
-        q_ms = _timed(torch, lambda: amp.amp_mx_quantize(X, amp.BF16, T, I, I, 0, yt, qx, sx), 5)
+        k = _copies(1 << 30, T * I * 2)
+        Xs = [X] + [X.clone() for _ in range(k - 1)]
+        qs = [qx] + [torch.empty_like(qx) for _ in range(k - 1)]
+        ss = [sx] + [torch.empty_like(sx) for _ in range(k - 1)]
+        q_ms = _timed_rot(torch, [lambda i=i: amp.amp_mx_quantize(Xs[i], amp.BF16, T, I, I, 0, yt, qs[i],
+                                                                   ss[i]) for i in range(k)], 4 * k)
+        del Xs[1:], qs[1:], ss[1:]
         amp.amp_mx_quantize(W, amp.BF16, O, I, I, 0, yt, qw, sw)
         Y = torch.empty(T, O, device="cuda", dtype=torch.bfloat16)
         bsx = amp.BlockScales(sx.data_ptr(), I // 32, 0, 0)

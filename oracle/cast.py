@@ -75,9 +75,9 @@ def cast_values(x_f32_values, out_fmt: F.Fmt, scale: float | None = None):
 def saturated_count(codes, in_fmt: F.Fmt, out_fmt: F.Fmt, scale: float | None = None) -> int:
     """Number of elements the saturating cast clips.
 
-    Section 8(b) of the hot-path contract has FP8 saturation counted as data
-    (hwlabs "FP8이 어려운 이유": values beyond the format's range are clipped to
-    it).  Reading: an element is saturated when its scaled value
+    Saturation is data, not an error (hwlabs "FP8이 어려운 이유": values
+    beyond the format's range are clipped to it).  Reading: an element is
+    saturated when its scaled value
     ``t = fl32(x * scale)`` has ``|t| > max_finite`` of the saturating output
     format (E4M3, E5M2), infinities included; NaN is not a saturation; the
     IEEE-mode 16-bit formats overflow to inf instead and count nothing."""
@@ -92,9 +92,8 @@ def saturated_count(codes, in_fmt: F.Fmt, out_fmt: F.Fmt, scale: float | None = 
 
 def found_inf_from_amax(amax_bits_list, out_fmt: F.Fmt, scale: float | None = None) -> bool:
     """Overflow flag of gradients that a scaled cast produced, from the amax
-    values that cast recorded (the hot-path contract's producer-flag option for
-    the unscale + check step; itwiki "손실 스케일링": a step with any inf/NaN
-    gradient is skipped).
+    values that cast recorded, so that the optimizer needs no sweep of its own
+    (itwiki "손실 스케일링": a step with any inf/NaN gradient is skipped).
 
     Reading: rounding is monotone in |t|, so some output of the cast is
     non-finite exactly when the largest input magnitude gives one: the flag is

@@ -3,10 +3,11 @@
  *
  * Three parts, as the pages describe mixed-precision training:
  *   1. scaled down-casts to FP16 / BF16 / FP8 (E4M3 forward, E5M2 backward)
- *      with amax capture and a delayed-scaling history, plus the NVFP4
- *      two-level quantizer;
+ *      with amax capture, delayed and current scaling, plus the NVFP4,
+ *      MX and fine-grained (tile / block) FP8 quantizers;
  *   2. low-precision GEMM with FP32 accumulation (forward, dgrad, wgrad);
- *   3. the fused FP32-master AdamW step with dynamic loss scaling.
+ *   3. the fused FP32-master AdamW step with dynamic loss scaling, with
+ *      gradient accumulation and global-norm clipping.
  *
  * Conventions for every call
  * --------------------------
@@ -21,6 +22,10 @@
  *    is launched and a negative amp_status is returned.  AMP_EHIP reports a
  *    failed launch; amp_last_hip_error() gives the hipError_t of the calling
  *    thread's last failure.  No C++ exception crosses this boundary.
+ *  - Device pointers to state structs and scalars (amp_scaler_state,
+ *    amp_grad_norm_state: 8 bytes; amp_fp8_meta, FP32 scalars and arrays:
+ *    4 bytes; the 64-bit saturation counter: 8 bytes) must be naturally
+ *    aligned, else AMP_EINVAL.
  *  - Numerical events (inf/NaN, saturation) are data, not errors.
  *  - Scalar state (loss scale, overflow flag, Adam step, FP8 scales) lives in
  *    device memory so that no step needs a host round trip.

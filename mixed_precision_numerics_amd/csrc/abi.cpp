@@ -54,6 +54,11 @@ bool is_cast_out(int t) { return t == AMP_F16 || t == AMP_BF16 || t == AMP_E4M3 
 bool is_grad(int t) { return t == AMP_F32 || t == AMP_F16 || t == AMP_BF16; }
 bool is_fp8(int t) { return t == AMP_E4M3 || t == AMP_E5M2; }
 
+// Device state and scalar pointers must be naturally aligned (they are read
+// as wide words and updated by atomics); a misaligned one is an argument
+// error, not a memory fault.  NULL passes (optional arguments).
+bool al(const void* p, uintptr_t a) { return p == nullptr || amp::aligned(p, a); }
+
 }  // namespace
 
 extern "C" {
@@ -83,6 +88,7 @@ int amp_cast(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx, voi
 int amp_cast_ex(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx, void* y, int yt,
                 int64_t ldy, void* y_t, int64_t ldy_t, const float* d_scale, float* d_amax,
                 unsigned long long* d_sat_count, void* stream) {
+  if (!al(d_scale, 4) || !al(d_amax, 4) || !al(d_sat_count, 8)) return AMP_EINVAL;
   if (rows < 0 || cols < 0) return AMP_EINVAL;
   if (!is_cast_in(xt) || !is_cast_out(yt)) return AMP_EUNSUPPORTED;
   if (rows == 0 || cols == 0) return AMP_OK;
@@ -96,6 +102,7 @@ int amp_cast_ex(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx, 
 int amp_cast_current_scaling(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
                              void* y, int yt, int64_t ldy, void* y_t, int64_t ldy_t,
                              const amp_delayed_recipe* r, amp_fp8_meta* d_meta, void* stream) {
+  if (!al(d_meta, alignof(amp_fp8_meta))) return AMP_EINVAL;
   if (rows < 0 || cols < 0 || !r || !d_meta) return AMP_EINVAL;
   if (!(r->fp8_max > 0.0f) || !(r->margin > 0.0f)) return AMP_EINVAL;
   if (!is_cast_in(xt) || !is_cast_out(yt)) return AMP_EUNSUPPORTED;
@@ -121,6 +128,7 @@ int amp_gemm_ex(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A
                 const float* d_alphaB, void* C, int ct, int64_t ldc,
                 const amp_block_scales* bsA, const amp_block_scales* bsB, int flags,
                 void* stream) {
+  if (!al(d_alphaA, 4) || !al(d_alphaB, 4)) return AMP_EINVAL;
   if (flags & ~(AMP_GEMM_FP8_NATIVE | AMP_GEMM_MX)) return AMP_EINVAL;
   if (M < 0 || N < 0 || K < 0) return AMP_EINVAL;
   if ((opA != AMP_OP_N && opA != AMP_OP_T) || (opB != AMP_OP_N && opB != AMP_OP_T))
@@ -165,6 +173,7 @@ int amp_gemm_ex(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A
 }
 
 int amp_scaler_init(amp_scaler_state* d_state, float init_scale, void* stream) {
+  if (!al(d_state, 8)) return AMP_EINVAL;
   if (!d_state || !(init_scale > 0.0f)) return AMP_EINVAL;
   if (int st = check_device()) return st;
   return hip_status(amp::launch_scaler_init(d_state, init_scale, static_cast<hipStream_t>(stream)));
@@ -172,6 +181,7 @@ int amp_scaler_init(amp_scaler_state* d_state, float init_scale, void* stream) {
 
 int amp_check_overflow(const void* x, int xt, int64_t n, amp_scaler_state* d_state,
                        void* stream) {
+  if (!al(d_state, 8)) return AMP_EINVAL;
   if (n < 0 || !d_state) return AMP_EINVAL;
   if (!is_grad(xt)) return AMP_EUNSUPPORTED;
   if (n == 0) return AMP_OK;
@@ -182,6 +192,7 @@ int amp_check_overflow(const void* x, int xt, int64_t n, amp_scaler_state* d_sta
 
 int amp_found_inf_from_amax(const float* d_amax, int32_t n, int yt, const float* d_scale,
                             amp_scaler_state* d_state, void* stream) {
+  if (!al(d_amax, 4) || !al(d_scale, 4) || !al(d_state, 8)) return AMP_EINVAL;
   if (n < 0 || !d_state) return AMP_EINVAL;
   if (yt != AMP_F16 && yt != AMP_BF16 && !is_fp8(yt)) return AMP_EUNSUPPORTED;
   if (n == 0) return AMP_OK;
@@ -195,6 +206,7 @@ int amp_optimizer_step_ex(float* master, float* m, float* v, const void* grads, 
                           void* w16, int wt, int64_t n, const amp_adamw_hparams* hp,
                           amp_scaler_state* d_state, const float* d_grad_mult, int flags,
                           void* stream) {
+  if (!al(master, 4) || !al(m, 4) || !al(v, 4) || !al(d_state, 8) || !al(d_grad_mult, 4)) return AMP_EINVAL;
   if (n < 0 || !hp || !d_state) return AMP_EINVAL;
   if (!is_grad(gt)) return AMP_EUNSUPPORTED;
   if (w16 && wt != AMP_F16 && wt != AMP_BF16) return AMP_EUNSUPPORTED;
@@ -239,6 +251,7 @@ int amp_mx_quantize(const void* x, int xt, int64_t rows, int64_t cols, int64_t l
 int amp_quantize_blockwise(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
                            int yt, int block, uint8_t* q, int64_t ldq, float* s, int64_t lds,
                            uint8_t* qt, int64_t ldqt, float* st, int64_t ldst, void* stream) {
+  if (!al(s, 4) || !al(st, 4)) return AMP_EINVAL;
   if (rows < 0 || cols < 0 || ldx < cols || (block != 0 && block != 1)) return AMP_EINVAL;
   if (!is_cast_in(xt)) return AMP_EUNSUPPORTED;
   if (!is_fp8(yt)) return AMP_EUNSUPPORTED;
@@ -257,6 +270,7 @@ int amp_gemm_blockwise(int64_t M, int64_t N, int64_t K, const void* A, int at, i
                        const float* sA, int64_t ldsA, int a_block, const void* B, int bt,
                        int64_t ldb, const float* sB, int64_t ldsB, int b_block, void* C, int ct,
                        int64_t ldc, void* stream) {
+  if (!al(sA, 4) || !al(sB, 4)) return AMP_EINVAL;
   if (M < 0 || N < 0 || K < 0) return AMP_EINVAL;
   if ((a_block != 0 && a_block != 1) || (b_block != 0 && b_block != 1)) return AMP_EINVAL;
   if (!is_fp8(at) || !is_fp8(bt)) return AMP_EUNSUPPORTED;
@@ -276,6 +290,7 @@ int amp_gemm_blockwise(int64_t M, int64_t N, int64_t K, const void* A, int at, i
 
 int amp_grad_accumulate(float* acc, const void* grads, int gt, int64_t n, int first,
                         void* stream) {
+  if (!al(acc, 4)) return AMP_EINVAL;
   if (n < 0) return AMP_EINVAL;
   if (!is_grad(gt)) return AMP_EUNSUPPORTED;
   if (n == 0) return AMP_OK;
@@ -286,6 +301,7 @@ int amp_grad_accumulate(float* acc, const void* grads, int gt, int64_t n, int fi
 }
 
 int amp_grad_norm_init(amp_grad_norm_state* d_norm, void* stream) {
+  if (!al(d_norm, 8)) return AMP_EINVAL;
   if (!d_norm) return AMP_EINVAL;
   if (int st = check_device()) return st;
   return hip_status(amp::launch_grad_norm_init(d_norm, static_cast<hipStream_t>(stream)));
@@ -293,6 +309,7 @@ int amp_grad_norm_init(amp_grad_norm_state* d_norm, void* stream) {
 
 int amp_grad_norm_accumulate(const void* grads, int gt, int64_t n, amp_scaler_state* d_state,
                              amp_grad_norm_state* d_norm, void* stream) {
+  if (!al(d_state, 8) || !al(d_norm, 8)) return AMP_EINVAL;
   if (n < 0 || !d_state || !d_norm) return AMP_EINVAL;
   if (!is_grad(gt)) return AMP_EUNSUPPORTED;
   if (n == 0) return AMP_OK;
@@ -304,6 +321,7 @@ int amp_grad_norm_accumulate(const void* grads, int gt, int64_t n, amp_scaler_st
 
 int amp_clip_coefficient(const amp_grad_norm_state* d_norm, float max_norm,
                          const amp_scaler_state* d_state, float* d_out, void* stream) {
+  if (!al(d_norm, 8) || !al(d_state, 8) || !al(d_out, 4)) return AMP_EINVAL;
   if (!d_norm || !d_state || !d_out || !(max_norm > 0.0f) || !(max_norm < 3.0e38f))
     return AMP_EINVAL;
   if (int st = check_device()) return st;
@@ -312,6 +330,7 @@ int amp_clip_coefficient(const amp_grad_norm_state* d_norm, float max_norm,
 }
 
 int amp_scaler_update(amp_scaler_state* d_state, const amp_scaler_params* p, void* stream) {
+  if (!al(d_state, 8)) return AMP_EINVAL;
   if (!d_state) return AMP_EINVAL;
   amp_scaler_params q{2.0f, 0.5f, 2000};
   if (p) q = *p;
@@ -322,6 +341,7 @@ int amp_scaler_update(amp_scaler_state* d_state, const amp_scaler_params* p, voi
 
 int amp_fp8_meta_init(amp_fp8_meta* d_metas, float* d_history, int32_t n, int32_t history_len,
                       void* stream) {
+  if (!al(d_metas, alignof(amp_fp8_meta)) || !al(d_history, 4)) return AMP_EINVAL;
   if (n < 0 || history_len <= 0) return AMP_EINVAL;
   if (n == 0) return AMP_OK;
   if (!d_metas || !d_history) return AMP_EINVAL;
@@ -332,6 +352,7 @@ int amp_fp8_meta_init(amp_fp8_meta* d_metas, float* d_history, int32_t n, int32_
 
 int amp_delayed_scaling_update(amp_fp8_meta* d_metas, float* d_history, int32_t n,
                                const amp_delayed_recipe* r, void* stream) {
+  if (!al(d_metas, alignof(amp_fp8_meta)) || !al(d_history, 4)) return AMP_EINVAL;
   if (n < 0 || !r || r->history_len <= 0) return AMP_EINVAL;
   if (r->algo != AMP_AMAX_MAX && r->algo != AMP_AMAX_MOST_RECENT) return AMP_EINVAL;
   if (!(r->fp8_max > 0.0f) || !(r->margin > 0.0f)) return AMP_EINVAL;
@@ -346,6 +367,7 @@ int amp_nvfp4_quantize(const void* x, int xt, int64_t rows, int64_t cols, int64_
                        int transpose, int block2d, int rht, uint64_t rht_seed, int rnd,
                        uint64_t sr_seed, uint8_t* q, uint8_t* scales, float* d_tensor,
                        void* stream) {
+  if (!al(d_tensor, 4)) return AMP_EINVAL;
   if (rows < 0 || cols < 0 || ldx < cols) return AMP_EINVAL;
   if (xt != AMP_BF16 && xt != AMP_F32) return AMP_EUNSUPPORTED;
   if (rnd != AMP_ROUND_RNE && rnd != AMP_ROUND_SR) return AMP_EINVAL;
@@ -361,6 +383,7 @@ int amp_nvfp4_quantize(const void* x, int xt, int64_t rows, int64_t cols, int64_
 
 int amp_bias_gelu_f16(const float* acc, int64_t rows, int64_t cols, const void* b16, void* z16,
                       void* a16, void* stream) {
+  if (!al(acc, 4)) return AMP_EINVAL;
   if (rows < 0 || cols < 0) return AMP_EINVAL;
   if (rows == 0 || cols == 0) return AMP_OK;
   if (!acc || !z16) return AMP_EINVAL;
@@ -372,6 +395,7 @@ int amp_bias_gelu_f16(const float* acc, int64_t rows, int64_t cols, const void* 
 int amp_softmax_xent_f16(const void* logits16, const int32_t* labels, int64_t rows, int64_t cols,
                          const amp_scaler_state* d_state, float* d_loss, void* dlogits16,
                          void* stream) {
+  if (!al(labels, 4) || !al(d_state, 8) || !al(d_loss, 4)) return AMP_EINVAL;
   if (rows < 0 || cols <= 0 || rows > 65536) return AMP_EINVAL;
   if (rows == 0) return AMP_OK;
   if (!logits16 || !labels) return AMP_EINVAL;

@@ -66,6 +66,10 @@ def test_invalid_arguments_rejected_before_any_device_work():
                                   None) == -2
     assert lib.amp_gemm_blockwise(4, 4, 4, 8, 3, 4, 8, 3, 0, 8, 3, 4, 8, 4, 0, 8, 0, 4,
                                   None) == -1
+    # misaligned state / scalar pointers are argument errors, not faults
+    assert lib.amp_scaler_init(12, 1024.0, None) == -1
+    assert lib.amp_cast_ex(8, 2, 4, 4, 4, 8, 3, 4, None, 0, None, None, 12, None) == -1
+    assert lib.amp_found_inf_from_amax(6, 1, 1, None, 8, None) == -1
     # empty work is a successful no-op
     assert lib.amp_cast(None, 0, 0, 4, 4, None, 1, 4, None, 0, None, None, None) == 0
     assert lib.amp_gemm_blockwise(0, 4, 4, None, 3, 4, None, 0, 0, None, 3, 4, None, 0, 0, None,

@@ -15,7 +15,9 @@ under "components".
 Also measured in the same run (reported under "components"):
   * the BF16 and FP8 (delayed-scaling, E4M3 fwd / E5M2 bwd) GEMMs of one
     transformer block's linear layers at hidden 4096, FFN 14336, 8192 tokens
-    (fwd, dgrad, wgrad of QKV, O, up/gate, down: 10.72 TFLOP per block step);
+    (fwd, dgrad, wgrad of QKV, O, up/gate, down: 10.72 TFLOP per block step),
+    the FP8 step both on the exact BF16 route and on the native FP8
+    instruction;
   * the NVFP4 weight-gradient GEMM 20480 x 5120 x 16384 and its two
     quantizer calls (RHT on both operands, stochastic rounding on dY);
   * the scaled casts (BF16 -> E4M3 flat 2^31, BF16 -> E5M2 [8192 x 28672]
@@ -160,10 +162,13 @@ def optimizer_workload(torch, amp, n, steps, warmup, calibrate_copy):
     return wall * 1e3 / steps, apply_ms, wall1 * 1e3 / steps
 
 
-def gemm_block_workload(torch, amp, fp8: bool, reps: int = 3):
+def gemm_block_workload(torch, amp, fp8: bool, reps: int = 3, native: bool = False):
     """12 GEMMs of one transformer block (fwd, dgrad, wgrad of 4 linears).
     FP8: E4M3 activations/weights, E5M2 output gradients, delayed-scaling
-    casts (row-major + transposed FP8 copies) before the GEMMs."""
+    casts (row-major + transposed FP8 copies) before the GEMMs.  native: the
+    FP8 GEMMs on the FP8 matrix-core instruction (AMP_GEMM_FP8_NATIVE, its
+    reduced-precision 64-term sums) instead of the exact BF16 route."""
+    gflags = amp.GEMM_FP8_NATIVE if native else 0
     T = 8192
     layers = [("qkv", 4096, 6144), ("o", 4096, 4096), ("up", 4096, 28672), ("down", 14336, 4096)]
     dev = "cuda"
@@ -212,14 +217,17 @@ def gemm_block_workload(torch, amp, fp8: bool, reps: int = 3):
                              mp(ix, 4), mp(ix, 0))
                 amp.amp_cast(d["W"], amp.BF16, dout, din, din, d["W8"], amp.E4M3, din, d["W8t"],
                              dout, mp(iw, 4), mp(iw, 0))
-                amp.amp_gemm(amp.OP_N, amp.OP_T, T, dout, din, d["X8"], amp.E4M3, din, mp(ix, 8),
-                             d["W8"], amp.E4M3, din, mp(iw, 8), d["Y"], amp.BF16, dout)
+                amp.amp_gemm_ex(amp.OP_N, amp.OP_T, T, dout, din, d["X8"], amp.E4M3, din, mp(ix, 8),
+                                d["W8"], amp.E4M3, din, mp(iw, 8), d["Y"], amp.BF16, dout,
+                                flags=gflags)
                 amp.amp_cast(d["dY"], amp.BF16, T, dout, dout, d["G8"], amp.E5M2, dout, d["G8t"],
                              T, mp(ig, 4), mp(ig, 0))
-                amp.amp_gemm(amp.OP_N, amp.OP_T, T, din, dout, d["G8"], amp.E5M2, dout, mp(ig, 8),
-                             d["W8t"], amp.E4M3, dout, mp(iw, 8), d["dX"], amp.BF16, din)
-                amp.amp_gemm(amp.OP_N, amp.OP_T, dout, din, T, d["G8t"], amp.E5M2, T, mp(ig, 8),
-                             d["X8t"], amp.E4M3, T, mp(ix, 8), d["dW"], amp.BF16, din)
+                amp.amp_gemm_ex(amp.OP_N, amp.OP_T, T, din, dout, d["G8"], amp.E5M2, dout, mp(ig, 8),
+                                d["W8t"], amp.E4M3, dout, mp(iw, 8), d["dX"], amp.BF16, din,
+                                flags=gflags)
+                amp.amp_gemm_ex(amp.OP_N, amp.OP_T, dout, din, T, d["G8t"], amp.E5M2, T, mp(ig, 8),
+                                d["X8t"], amp.E4M3, T, mp(ix, 8), d["dW"], amp.BF16, din,
+                                flags=gflags)
         if fp8:
             # E4M3 metas (X, W) and E5M2 metas (dY) are updated by role
             for li in range(len(layers)):
@@ -244,7 +252,8 @@ def gemm_block_workload(torch, amp, fp8: bool, reps: int = 3):
     tf = flops / ms / 1e9
     return {"ms": round(ms, 4), "tflops": round(tf, 1), "peak_tflops": peak,
             "frac": round(tf / peak, 4), "tflop_per_step": round(flops / 1e12, 3),
-            "includes": "casts+delayed-scaling updates" if fp8 else "gemms only"}
+            "includes": "casts+delayed-scaling updates" if fp8 else "gemms only",
+            **({"fp8_instruction": "native (reduced-precision 64-term sums)"} if native else {})}
 
 
 def cast_workload(torch, amp):
@@ -612,6 +621,8 @@ def main():
         comps["gemm_bf16_block"] = gemm_block_workload(torch, amp, fp8=False)
         log("components: FP8 delayed-scaling block")
         comps["gemm_fp8_block"] = gemm_block_workload(torch, amp, fp8=True)
+        log("components: FP8 block on the native FP8 instruction")
+        comps["gemm_fp8_native_block"] = gemm_block_workload(torch, amp, fp8=True, native=True)
         log("components: cast")
         comps["cast"] = cast_workload(torch, amp)
         log("components: cast with transposed copy")

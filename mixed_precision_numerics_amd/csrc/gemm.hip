@@ -465,11 +465,32 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma(GemmArgs g) {
 // ------------------------------------------------------- direct-to-LDS NT
 typedef __attribute__((address_space(3))) void lds_void;
 
+// One 16-byte-per-lane direct-to-LDS load (64 lanes fill 1 KB at dst).  With
+// ASM set it is written as inline assembly: the compiler then does not track
+// it as a pending LDS write.  It has to be kept from tracking it where the
+// transposing LDS reads follow: those reads carry no alias information, so
+// the compiler would make the first of them wait for every load in flight,
+// exposing the whole global-load latency in each K-step.  Every caller makes
+// the loads land before their destination is read (s_waitcnt vmcnt(0), then
+// a block barrier), which is the ordering the compiler would otherwise add.
+template <bool ASM>
+__device__ __forceinline__ void d2l16(__amdgpu_buffer_rsrc_t rsrc, uint8_t* dst, uint32_t voff,
+                                      uint32_t soff) {
+  if constexpr (ASM) {
+    const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_void*)dst));
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds" ::"v"(voff), "s"(rsrc), "s"(soff), "{m0}"(m0)
+                 : "memory");
+  } else {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, voff, soff, 0, 0);
+  }
+}
+
 // Wave w fills rows w*64 .. w*64+63 of a 256-row operand stage, 8 rows (1 KB)
 // per buffer load; lane l writes LDS bytes 16*l of those 8 rows, i.e.
 // physical chunk l%8 of row l/8, so it fetches the logical chunk that the
 // swizzle maps there: p ^ (l/8) ^ i for the i-th load.  The buffer resource
 // starts at the tile's first row; koff is the K-step's byte offset.
+template <bool ASM = false>
 __device__ __forceinline__ void d2l_stage(__amdgpu_buffer_rsrc_t rsrc, uint32_t ldb, uint32_t koff,
                                           uint8_t* stage) {
   const int lane = threadIdx.x & 63, w = wave_id();
@@ -477,9 +498,8 @@ __device__ __forceinline__ void d2l_stage(__amdgpu_buffer_rsrc_t rsrc, uint32_t 
   const uint32_t x = static_cast<uint32_t>(((lane & 7) ^ (lane >> 3)) & 7) << 4;
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(stage + (w * 64 + i * 8) * kRowBytes),
-                                             16, vrow + (x ^ static_cast<uint32_t>(i << 4)),
-                                             koff + static_cast<uint32_t>(8 * i) * ldb, 0, 0);
+    d2l16<ASM>(rsrc, stage + (w * 64 + i * 8) * kRowBytes, vrow + (x ^ static_cast<uint32_t>(i << 4)),
+               koff + static_cast<uint32_t>(8 * i) * ldb);
 }
 
 // M/N-contiguous 16-bit operand (rows of the global matrix are K): an LDS
@@ -487,6 +507,7 @@ __device__ __forceinline__ void d2l_stage(__amdgpu_buffer_rsrc_t rsrc, uint32_t 
 // row, with 16-byte chunk c of K-row k stored at chunk c ^ 4*(k%4).  Wave w
 // loads K-rows 16w .. 16w+15, two rows (1 KB) per buffer load: lane l writes
 // physical chunk l%32 of row l/32.  rsrc starts at the step's first K-row.
+// Always followed by transposing reads, so always the assembly form.
 __device__ __forceinline__ void d2l_stage_mn(__amdgpu_buffer_rsrc_t rsrc, uint32_t ldb,
                                              uint8_t* stage) {
   const int lane = threadIdx.x & 63, w = wave_id();
@@ -497,9 +518,8 @@ __device__ __forceinline__ void d2l_stage_mn(__amdgpu_buffer_rsrc_t rsrc, uint32
   const uint32_t vo = v0 + (static_cast<uint32_t>((lane & 31) ^ (4 * (2 + hr))) << 4);
 #pragma unroll
   for (int i = 0; i < 8; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(stage + (w * 16 + 2 * i) * 512), 16,
-                                             (i & 1) ? vo : ve,
-                                             static_cast<uint32_t>(w * 16 + 2 * i) * ldb, 0, 0);
+    d2l16<true>(rsrc, stage + (w * 16 + 2 * i) * 512, (i & 1) ? vo : ve,
+                static_cast<uint32_t>(w * 16 + 2 * i) * ldb);
 }
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
@@ -614,7 +634,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
     const uint32_t koff = static_cast<uint32_t>(kc * kRowBytes);
     if (which == 0) {
       if constexpr (A_KC) {
-        d2l_stage(ra, lda_b, koff, smem[kt & 1][0]);
+        d2l_stage<!B_KC>(ra, lda_b, koff, smem[kt & 1][0]);
       } else {
         // M-contiguous: the step's 64 K-rows, columns m0 .. m0+255
         const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
@@ -623,7 +643,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
       }
     } else {
       if constexpr (B_KC) {
-        d2l_stage(rb, ldb_b, koff, smem[kt & 1][1]);
+        d2l_stage<!A_KC>(rb, ldb_b, koff, smem[kt & 1][1]);
       } else {
         const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint8_t*>(gB + (kc * BK * g.ldb + n0) * EB), 0, static_cast<int>(BK * ldb_b), 0x00020000);

@@ -765,12 +765,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
     const uint8_t* st = smem[kt & 1][0];
     load_scales(kt + 1, nscA, nscB);
     load_nv(kt + 1, nnvA, nnvB);
+    // The next step's scales are consumed only after the closing barrier;
+    // left to itself the scheduler sinks their loads to just before that
+    // barrier's vmcnt(0), exposing their latency once per step.
+    if constexpr (kMX || PATH == kPFP4D) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < NS; ++ks) {
       const int cur = ks & 1;
       // K-contiguous operands: A's loads in slice 0 and B's in slice 1, spread
-      // among the MFMAs; with transposed operands both at the start of the step
-      constexpr bool kSplit = A_KC && B_KC;
+      // among the MFMAs; with transposed operands both at the start of the
+      // step, and with only two slices per step both in slice 0 (B's loads
+      // in the last slice would meet the barrier's wait at once)
+      constexpr bool kSplit = A_KC && B_KC && NS > 2;
       if (kSplit && ks < 2) load_part(kt + 1, ks);
       if (!kSplit && ks == 0) {
         load_part(kt + 1, 0);
@@ -875,9 +881,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
       constexpr int kReads = PATH == kPF8Native || PATH == kPMX8 ? 16 : (A_KC ? 4 : 8) + (B_KC ? 4 : 8);
       if constexpr (PATH != kPF8Exact && PATH != kPFP4D) {
         if (kSplit && ks < 2) sched_slice<0, kReads, 8>();
+        else if (!kSplit && A_KC && B_KC && ks == 0) sched_slice<0, kReads, 16>();
         else sched_slice<0, kReads, 0>();
       }
     }
+    // and the register copies stay after the barrier (whose vmcnt(0) they
+    // then need not add to)
+    if constexpr (kMX || PATH == kPFP4D) __builtin_amdgcn_sched_barrier(0);
     if constexpr (kMX) {
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)

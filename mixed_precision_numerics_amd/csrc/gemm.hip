@@ -602,7 +602,10 @@ __device__ __forceinline__ void sched_half() {
 template <int AT, int BT, bool A_KC, bool B_KC, int PATH, int CT>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
   static_assert((A_KC && B_KC) || PATH == kP16, "M/N-contiguous operands are 16-bit");
-  __shared__ __align__(16) uint8_t smem[2][2][kOperandBytes];
+  // the two stages are separate objects, so that the compiler can tell the
+  // loads into one from the fragment reads of the other
+  __shared__ __align__(16) uint8_t smem0[2][kOperandBytes];
+  __shared__ __align__(16) uint8_t smem1[2][kOperandBytes];
   constexpr bool kF8 = PATH == kPF8Native || PATH == kPF8Exact || PATH == kPMX8;
   constexpr bool kMX = PATH == kPMX8 || PATH == kPMX4;
   constexpr bool kFP4 = PATH == kPMX4 || PATH == kPFP4D;
@@ -641,25 +644,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
       const_cast<uint8_t*>(gB + n0 * g.ldb * EB), 0, static_cast<int>(kBN * ldb_b), 0x00020000);
   // past the end a step reloads the last one into the idle stage (never
   // read); operand 0 (A) and 1 (B) are fetched in different K-slices
-  auto load_part = [&](int64_t kt, int which) {
+  auto load_part = [&](int64_t kt, int which, uint8_t* dst) {
     const int64_t kc = kt < nk ? kt : nk - 1;
     const uint32_t koff = static_cast<uint32_t>(kc * kRowBytes);
     if (which == 0) {
       if constexpr (A_KC) {
-        d2l_stage<!B_KC>(ra, lda_b, koff, smem[kt & 1][0]);
+        d2l_stage<!B_KC>(ra, lda_b, koff, dst);
       } else {
         // M-contiguous: the step's 64 K-rows, columns m0 .. m0+255
         const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint8_t*>(gA + (kc * BK * g.lda + m0) * EB), 0, static_cast<int>(BK * lda_b), 0x00020000);
-        d2l_stage_mn(r, lda_b, smem[kt & 1][0]);
+        d2l_stage_mn(r, lda_b, dst);
       }
     } else {
       if constexpr (B_KC) {
-        d2l_stage<!A_KC>(rb, ldb_b, koff, smem[kt & 1][1]);
+        d2l_stage<!A_KC>(rb, ldb_b, koff, dst + kOperandBytes);
       } else {
         const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint8_t*>(gB + (kc * BK * g.ldb + n0) * EB), 0, static_cast<int>(BK * ldb_b), 0x00020000);
-        d2l_stage_mn(r, ldb_b, smem[kt & 1][1]);
+        d2l_stage_mn(r, ldb_b, dst + kOperandBytes);
       }
     }
   };
@@ -766,15 +769,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
       }
     }
   };
-  load_part(0, 0);
-  load_part(0, 1);
+  load_part(0, 0, smem0[0]);
+  load_part(0, 1, smem0[0]);
   load_scales(0, scA, scB);
   load_nv(0, nvA, nvB);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  frag(smem[0][0], 0, fa[0], fb[0]);
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    const uint8_t* st = smem[kt & 1][0];
+  frag(smem0[0], 0, fa[0], fb[0]);
+  auto step = [&](int64_t kt, const uint8_t* st, uint8_t* nst) __attribute__((always_inline)) {
     load_scales(kt + 1, nscA, nscB);
     load_nv(kt + 1, nnvA, nnvB);
     // The next step's scales are consumed only after the closing barrier;
@@ -789,10 +791,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
       // step, and with only two slices per step both in slice 0 (B's loads
       // in the last slice would meet the barrier's wait at once)
       constexpr bool kSplit = A_KC && B_KC && NS > 2;
-      if (kSplit && ks < 2) load_part(kt + 1, ks);
+      if (kSplit && ks < 2) load_part(kt + 1, ks, nst);
       if (!kSplit && ks == 0) {
-        load_part(kt + 1, 0);
-        load_part(kt + 1, 1);
+        load_part(kt + 1, 0, nst);
+        load_part(kt + 1, 1, nst);
       }
       // With two slices per step (FP8 elements, 64 K per MFMA) the barrier
       // moves to the middle of the last slice: the loads of the first slice
@@ -803,7 +805,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
       auto next_step = [&]() __attribute__((always_inline)) {
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
         __syncthreads();
-        frag(smem[(kt + 1) & 1][0], 0, fa[cur ^ 1], fb[cur ^ 1]);
+        frag(nst, 0, fa[cur ^ 1], fb[cur ^ 1]);
       };
       if (ks + 1 < NS) {
         frag(st, ks + 1, fa[cur ^ 1], fb[cur ^ 1]);
@@ -935,6 +937,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
         nvB[mb] = nnvB[mb];
       }
     }
+  };
+  if constexpr (PATH == kPF8Exact || PATH == kPFP4D) {
+    // long step bodies without scheduling hints: one step per iteration,
+    // stages chosen at run time (measured faster for these two)
+    for (int64_t kt = 0; kt < nk; ++kt)
+      step(kt, (kt & 1) ? smem1[0] : smem0[0], (kt & 1) ? smem0[0] : smem1[0]);
+  } else {
+    // two steps per iteration, each naming its stages statically
+    int64_t kt = 0;
+    for (; kt + 1 < nk; kt += 2) {
+      step(kt, smem0[0], smem1[0]);
+      step(kt + 1, smem1[0], smem0[0]);
+    }
+    if (kt < nk) step(kt, smem0[0], smem1[0]);
   }
   const float alpha = (g.alphaA ? *g.alphaA : 1.0f) * (g.alphaB ? *g.alphaB : 1.0f);
 #pragma unroll

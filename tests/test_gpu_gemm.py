@@ -127,10 +127,11 @@ def test_fp8_decode_every_code_via_identity(fmt):
     assert np.array_equal(out.view(np.float32).astype(np.float64), F.decode(a, FMT[fmt]))
 
 
-def test_gemm_fp8_native_precision_report():
+@pytest.mark.parametrize("K", [4096, 384])          # an even and an odd number of K-steps
+def test_gemm_fp8_native_precision_report(K):
     """The FP8 matrix-core path: report its error against the bound (its
     64-term partial sums have reduced internal precision); require 2^-10."""
-    M, N, K = 512, 512, 4096
+    M, N = 512, 512
     a, b, ia, ib = fp8_operands(7, M, N, K, amp.E4M3, amp.E4M3)
     out = run_gemm(amp.OP_N, amp.OP_T, M, N, K, a, amp.E4M3, K, b, amp.E4M3, K, amp.F32,
                    flags=amp.GEMM_FP8_NATIVE)

@@ -184,7 +184,12 @@ __global__ __launch_bounds__(kTileThreads) void cast_tile(
   const int c0 = 8 * (t % 16), r0 = 8 * (t / 16);
   const bool full = VEC && (r_base + kTile <= rows) && (c_base + kTile <= cols);
   uint32_t am = 0;
-  uint32_t code[8][8];
+  // 16-bit codes are kept one per register; 8-bit ones four per register
+  // (row i's codes 4q .. 4q+3 in pk[i][q]), which cuts the live registers
+  // from 64 to 16 and lets more blocks share a CU
+  constexpr bool kPack = sizeof(Code) == 1;
+  uint32_t code[kPack ? 1 : 8][8];
+  uint32_t pk[kPack ? 8 : 1][2];
 
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
@@ -198,21 +203,29 @@ __global__ __launch_bounds__(kTileThreads) void cast_tile(
       for (int j = 0; j < 8; ++j)
         v[j] = (r < rows && c + j < cols) ? load_one<XT>(x, r * ldx + c + j) : 0.0f;
     }
+    uint32_t c8[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (AMAX) { const uint32_t a = fbits(v[j]) & 0x7fffffffu; am = am > a ? am : a; }
       const float t = SCALE ? v[j] * scale : v[j];
       // padding outside the tensor is 0 and never counts
       if constexpr (SAT) ns += fabsf(t) > SatMax<YT>::v;
-      code[i][j] = to_code<YT>(t);
+      c8[j] = to_code<YT>(t);
+    }
+    if constexpr (kPack) {
+      pk[i][0] = c8[0] | (c8[1] << 8) | (c8[2] << 16) | (c8[3] << 24);
+      pk[i][1] = c8[4] | (c8[5] << 8) | (c8[6] << 16) | (c8[7] << 24);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) code[i][j] = c8[j];
     }
     if constexpr (WY) {
       if (full) {
-        store8<YT>(y, r * ldy + c, code[i]);
+        store8<YT>(y, r * ldy + c, c8);
       } else {
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-          if (r < rows && c + j < cols) store_one<YT>(y, r * ldy + c + j, code[i][j]);
+          if (r < rows && c + j < cols) store_one<YT>(y, r * ldy + c + j, c8[j]);
       }
     }
   }
@@ -225,11 +238,20 @@ __global__ __launch_bounds__(kTileThreads) void cast_tile(
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       Code* dst = lds + (c0 + j) * kPitch + r0;
-      if constexpr (sizeof(Code) == 1) {
+      if constexpr (kPack) {
         dst = lds + (c0 + j) * kPitch + 8 * ((r0 / 8) ^ swz8(c0 + j));
+        // column j = byte j%4 of pk[i][j/4] for rows i = 0..7, gathered with
+        // byte permutes (selector s < 4: byte s of the second operand, 4..7:
+        // byte s-4 of the first, 12: zero)
+        const int q = j >> 2;
+        const uint32_t sel = static_cast<uint32_t>(j & 3) | (static_cast<uint32_t>((j & 3) + 4) << 8) | 0x0c0c0000u;
+        const uint32_t t01 = __builtin_amdgcn_perm(pk[1][q], pk[0][q], sel);
+        const uint32_t t23 = __builtin_amdgcn_perm(pk[3][q], pk[2][q], sel);
+        const uint32_t t45 = __builtin_amdgcn_perm(pk[5][q], pk[4][q], sel);
+        const uint32_t t67 = __builtin_amdgcn_perm(pk[7][q], pk[6][q], sel);
         uint2 w;
-        w.x = code[0][j] | (code[1][j] << 8) | (code[2][j] << 16) | (code[3][j] << 24);
-        w.y = code[4][j] | (code[5][j] << 8) | (code[6][j] << 16) | (code[7][j] << 24);
+        w.x = __builtin_amdgcn_perm(t23, t01, 0x05040100u);
+        w.y = __builtin_amdgcn_perm(t67, t45, 0x05040100u);
         *reinterpret_cast<uint2*>(dst) = w;
       } else {
         uint4 w;

@@ -1065,7 +1065,10 @@ __global__ __launch_bounds__(kBwThreads, 1) void gemm_bw_d2l(BwArgs g) {
   constexpr int kOffB = kBwBM * kRowBytes;                  // B rows after A's
   constexpr int kOffS = kOffB + kBwBN * kRowBytes;          // then A's 256 scales
   constexpr int kStage = kOffS + kBwBM * 4;
-  __shared__ __align__(16) uint8_t smem[2][kStage];
+  // two stage objects, named statically two K-blocks at a time, so that the
+  // compiler can tell one stage's loads from the other's fragment reads
+  __shared__ __align__(16) uint8_t smem0[kStage];
+  __shared__ __align__(16) uint8_t smem1[kStage];
   const int64_t nbm = g.M / kBwBM, nbn = g.N / kBwBN;
   const int64_t total = nbm * nbn;
   int64_t tile = blockIdx.x;
@@ -1097,9 +1100,8 @@ __global__ __launch_bounds__(kBwThreads, 1) void gemm_bw_d2l(BwArgs g) {
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(g.sA + m0), 0, static_cast<int>(((nk - 1) * g.ldsA + kBwBM) * 4), 0x00020000);
   // past the end a step reloads the last one into the idle stage (never read)
-  auto load_part = [&](int64_t kt, int which) {
+  auto load_part = [&](int64_t kt, int which, uint8_t* st) {
     const int64_t kc = kt < nk ? kt : nk - 1;
-    uint8_t* st = smem[kt & 1];
     if (which == 0) {
       d2l_rows<kBwBM, 8>(ra, lda, static_cast<uint32_t>(kc * 128), st);
       if (wave == 0)
@@ -1137,20 +1139,19 @@ __global__ __launch_bounds__(kBwThreads, 1) void gemm_bw_d2l(BwArgs g) {
       b[i] = *reinterpret_cast<const u32x4*>(st + bbase + i * 32 * kRowBytes + ((y ^ c) << 4));
     }
   };
-  load_part(0, 0);
-  load_part(0, 1);
+  load_part(0, 0, smem0);
+  load_part(0, 1, smem0);
   load_sb(0, sb);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  frag(smem[0], 0, fa[0], fb[0]);
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    const uint8_t* st = smem[kt & 1];
+  frag(smem0, 0, fa[0], fb[0]);
+  auto step = [&](int64_t kt, const uint8_t* st, uint8_t* nst) __attribute__((always_inline)) {
     load_sb(kt + 1, nsb);
     f32x4 sav[2][4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const int cur = ks & 1;
-      if (ks < 2) load_part(kt + 1, ks);
+      if (ks < 2) load_part(kt + 1, ks, nst);
       if (ks < 3) {
         frag(st, ks + 1, fa[cur ^ 1], fb[cur ^ 1]);
       } else {
@@ -1162,7 +1163,7 @@ __global__ __launch_bounds__(kBwThreads, 1) void gemm_bw_d2l(BwArgs g) {
             sav[mb][q4] = *reinterpret_cast<const f32x4*>(st + kOffS + (wm * 64 + mb * 32 + 8 * q4 + 4 * h) * 4);
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
         __syncthreads();
-        frag(smem[(kt + 1) & 1], 0, fa[cur ^ 1], fb[cur ^ 1]);
+        frag(nst, 0, fa[cur ^ 1], fb[cur ^ 1]);
       }
       u32x4 da[2][2], db[2][2];
 #pragma unroll
@@ -1196,7 +1197,13 @@ __global__ __launch_bounds__(kBwThreads, 1) void gemm_bw_d2l(BwArgs g) {
         }
     sb[0] = nsb[0];
     sb[1] = nsb[1];
+  };
+  int64_t kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    step(kt, smem0, smem1);
+    step(kt + 1, smem1, smem0);
   }
+  if (kt < nk) step(kt, smem0, smem1);
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll

@@ -119,9 +119,7 @@ __global__ __launch_bounds__(kFlatThreads) void cast_flat(const void* __restrict
   const int64_t nthr = static_cast<int64_t>(gridDim.x) * kFlatThreads;
   if constexpr (VEC) {
     const int64_t nv = n / 8;
-    for (int64_t j = tid; j < nv; j += nthr) {
-      float v[8];
-      load8<XT>(x, j * 8, v);
+    auto encode8 = [&](int64_t j, const float (&v)[8]) __attribute__((always_inline)) {
       uint32_t c[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
@@ -131,6 +129,21 @@ __global__ __launch_bounds__(kFlatThreads) void cast_flat(const void* __restrict
         c[k] = to_code<YT>(t);
       }
       store8<YT>(y, j * 8, c);
+    };
+    // four 16-byte loads in flight per thread, then one at a time
+    constexpr int kU = 4;
+    int64_t j = tid;
+    for (; j + (kU - 1) * nthr < nv; j += kU * nthr) {
+      float v[kU][8];
+#pragma unroll
+      for (int u = 0; u < kU; ++u) load8<XT>(x, (j + u * nthr) * 8, v[u]);
+#pragma unroll
+      for (int u = 0; u < kU; ++u) encode8(j + u * nthr, v[u]);
+    }
+    for (; j < nv; j += nthr) {
+      float v[8];
+      load8<XT>(x, j * 8, v);
+      encode8(j, v);
     }
     for (int64_t i = nv * 8 + tid; i < n; i += nthr) {
       const float v = load_one<XT>(x, i);

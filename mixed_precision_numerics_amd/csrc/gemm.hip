@@ -29,7 +29,11 @@
 //    storage format in LDS and are widened per register fragment (FP8 ->
 //    BF16, NVFP4 -> F16 x block scale) or fed to the block-scaled
 //    instruction (MX); M/N-contiguous 16-bit operands are read with
-//    transposing LDS reads.
+//    transposing LDS reads.  The two stages are separate LDS objects that
+//    the K loop names statically, two steps at a time, so the compiler sees
+//    that one stage's loads and the other's fragment reads are independent;
+//    kernels with transposing reads issue their loads as inline assembly
+//    (see d2l16).
 //  * gemm_mfma: any layout and ragged edges.  The next K-step is staged in
 //    registers; operands whose contiguous dimension is M or N (dgrad's
 //    weight, both wgrad operands) are loaded as 8x8 blocks and transposed in

@@ -59,10 +59,13 @@ class AdamCounters:
 
 
 def nonfinite_16(codes, fmt: F.Fmt) -> np.ndarray:
-    """True where a 16-bit (or FP32) gradient code is inf or NaN."""
-    c = np.asarray(codes).astype(np.int64)
-    ef = (c >> fmt.mbits) & ((1 << fmt.ebits) - 1)
-    return ef == (1 << fmt.ebits) - 1
+    """True where a 16-bit (or FP32) gradient code is inf or NaN: its exponent
+    field is all ones.  Integer codes are tested in their own width."""
+    c = np.asarray(codes)
+    if c.dtype.kind not in "ui":
+        c = c.astype(np.int64)
+    ef_mask = ((1 << fmt.ebits) - 1) << fmt.mbits
+    return (c & ef_mask) == ef_mask
 
 
 def found_inf(codes, fmt: F.Fmt) -> bool:

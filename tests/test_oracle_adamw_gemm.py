@@ -45,6 +45,20 @@ def test_overflow_detection():
     assert A.found_inf(c, F.BF16)
 
 
+def test_nonfinite_mask_over_every_16bit_code():
+    """The per-code test flags exactly the codes NumPy / PyTorch read as inf
+    or NaN (FP16 through NumPy's float16, BF16 through PyTorch's bfloat16),
+    in any integer width the codes arrive in."""
+    import torch
+    c = np.arange(1 << 16, dtype=np.uint16)
+    f16 = ~np.isfinite(c.view(np.float16).astype(np.float64))
+    bf = ~torch.isfinite(torch.from_numpy(c.view(np.int16)).view(torch.bfloat16).float()).numpy()
+    for codes in (c, c.view(np.int16), c.astype(np.int64)):
+        assert np.array_equal(A.nonfinite_16(codes, F.F16), f16)
+        assert np.array_equal(A.nonfinite_16(codes, F.BF16), bf)
+    assert f16.sum() == 2 * 1024 and bf.sum() == 2 * 128
+
+
 def test_first_step_closed_form():
     hp = A.AdamWHParams(lr=1e-3, weight_decay=0.0, eps=0.0)
     ctr = A.AdamCounters()

@@ -43,11 +43,16 @@ E2M1_MAG = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
 TENSOR_NUM = 2688.0
 
 
-def _tensor_enc(z) -> float:
-    a = float(np.max(np.abs(z))) if z.size else 0.0
+def tensor_enc(amax: float) -> float:
+    """Reading 3: ``enc = fl32(2688 / A)`` for a finite A > 0, else 1."""
+    a = float(amax)
     if np.isfinite(a) and a > 0.0:
         return float(F.f32(TENSOR_NUM / a))
     return 1.0
+
+
+def _tensor_enc(z) -> float:
+    return tensor_enc(float(np.max(np.abs(z))) if z.size else 0.0)
 
 
 def _sr_e2m1(y, u):
@@ -66,12 +71,17 @@ def _sr_e2m1(y, u):
 
 def quantize(x, transpose: bool = False, block2d: bool = False,
              rht: bool = False, rht_seed: int = 0, sr: bool = False,
-             sr_seed: int = 0):
+             sr_seed: int = 0, tensor_amax: float | None = None, row_ids=None):
     """Quantize a 2-D float64 array (FP32/BF16-representable values).
 
     Returns ``(q_packed uint8 [rows, K/2], scale_codes uint8, enc float)``;
     ``scale_codes`` is ``[rows, K/16]`` (1x16 blocks) or ``[rows/16, K/16]``
     (16x16 blocks).
+
+    To quantize some rows of a larger operand: ``tensor_amax`` is the whole
+    (transformed) operand's ``max |z|`` (reading 3 takes the tensor's amax,
+    not the slice's) and ``row_ids`` the rows' indices in it (the stochastic
+    rounding index of reading 6 is ``row * K + k`` in the whole operand).
     """
     op = np.asarray(x, dtype=np.float64)
     if transpose:
@@ -80,7 +90,7 @@ def quantize(x, transpose: bool = False, block2d: bool = False,
     if K % 16 or (block2d and rows % 16):
         raise ValueError("dimensions must be multiples of 16")
     z = hadamard.rht16(op, hadamard.sign_vector(rht_seed)) if rht else op.copy()
-    enc = _tensor_enc(z)
+    enc = _tensor_enc(z) if tensor_amax is None else tensor_enc(tensor_amax)
     az = np.abs(z)
     if block2d:
         b = az.reshape(rows // 16, 16, K // 16, 16).max(axis=(1, 3))
@@ -94,7 +104,9 @@ def quantize(x, transpose: bool = False, block2d: bool = False,
         mult = np.where(S_el > 0, F.f32(enc / np.where(S_el > 0, S_el, 1.0)), 0.0)
     y = F.f32(z * mult)
     if sr:
-        idx = np.arange(rows * K, dtype=np.uint64)
+        r = (np.arange(rows, dtype=np.uint64) if row_ids is None
+             else np.asarray(row_ids, dtype=np.uint64))
+        idx = (r[:, None] * np.uint64(K) + np.arange(K, dtype=np.uint64)[None, :]).ravel()
         w = stream_words(sr_seed, idx).reshape(rows, K).astype(np.float64)
         u = np.floor(w / 256.0) * 2.0 ** -24
         yq = _sr_e2m1(y, u)

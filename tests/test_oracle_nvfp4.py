@@ -167,3 +167,24 @@ def test_zero_block_and_specials():
     assert s[0, 0] == 0 and np.all(Q.unpack(q)[:, :16] == 0)
     q, s, enc = Q.quantize(np.zeros((16, 16)))
     assert enc == 1.0 and np.all(q == 0)
+
+
+@pytest.mark.parametrize("sr", [False, True])
+def test_row_slice_with_tensor_amax_equals_whole_operand_rows(sr):
+    """Quantizing some rows of an operand with the whole operand's amax and
+    the rows' global indices gives exactly those rows of the whole
+    quantization (codes, block scales, tensor scale) -- the tensor scale is
+    the whole tensor's and the stochastic-rounding index is global."""
+    x = synth.outlier_bf16_codes(12, (96, 80))
+    xv = F.decode(x, F.BF16)
+    q, s, enc = Q.quantize(xv, transpose=True, rht=True, rht_seed=5, sr=sr, sr_seed=21)
+    A = float(np.max(np.abs(H.rht16(xv.T, H.sign_vector(5)))))
+    rows = np.array([3, 17, 40, 79])
+    q2, s2, enc2 = Q.quantize(xv[:, rows], transpose=True, rht=True, rht_seed=5, sr=sr,
+                              sr_seed=21, tensor_amax=A, row_ids=rows)
+    assert enc2 == enc
+    assert np.array_equal(q2, q[rows]) and np.array_equal(s2, s[rows])
+    # the slice's own amax differs from the tensor's, so without it the codes move
+    q3, _, enc3 = Q.quantize(xv[:, rows], transpose=True, rht=True, rht_seed=5, sr=sr,
+                             sr_seed=21, row_ids=rows)
+    assert enc3 != enc

@@ -388,7 +388,11 @@ int amp_bias_gelu_f16(const float* acc, int64_t rows, int64_t cols, const void* 
  * labels in [0, cols): *d_loss = mean over rows, in FP32 (NULL: not written);
  * dlogits16 = round16(S * (softmax - onehot) / rows) with S read from
  * d_state->scale (d_state NULL: S = 1; dlogits16 NULL: not written).
- * Runs as one work-group (meant for classifier heads, rows <= 65536). */
+ * Runs as one work-group (meant for classifier heads, rows <= 65536).
+ * labels are device int32 in 0..cols-1; a row whose label lies outside that
+ * range adds NaN to the loss and gets an all-zero dlogits row (the kernel
+ * reads no logit for it), so a bad label shows up as a NaN loss rather than
+ * as a memory fault. */
 int amp_softmax_xent_f16(const void* logits16, const int32_t* labels, int64_t rows,
                          int64_t cols, const amp_scaler_state* d_state, float* d_loss,
                          void* dlogits16, void* stream);
@@ -462,6 +466,16 @@ int amp_optimizer_step_ex(float* master, float* m, float* v, const void* grads, 
                           void* w16, int wt, int64_t n, const amp_adamw_hparams* hp,
                           amp_scaler_state* d_state, const float* d_grad_mult, int flags,
                           void* stream);
+
+/* amp_stream_copy -- a plain device copy dst[0..bytes) = src[0..bytes), the
+ * reference for the HBM roofline of the element-wise kernels (not a step of
+ * the training path).  The optimizer pass reads as many bytes as it writes, so
+ * the rate of a copy with the same access shape (16-byte loads and stores,
+ * several in flight per thread, 64 work-groups per CU) is its practical
+ * ceiling on a given part.  src and dst: device memory, 16-byte aligned, not
+ * overlapping; bytes == 0 is a no-op; misaligned or NULL pointers give
+ * AMP_EINVAL. */
+int amp_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -27,7 +27,7 @@ __all__ = [
     "amp_clip_coefficient", "amp_optimizer_step_ex", "NORM_STATE_BYTES", "NORM_PARTIALS",
     "amp_cast_current_scaling", "amp_mx_quantize", "GEMM_MX",
     "amp_quantize_blockwise", "amp_gemm_blockwise", "amp_cast_ex",
-    "amp_found_inf_from_amax",
+    "amp_found_inf_from_amax", "amp_stream_copy",
 ]
 
 F32, F16, BF16, E4M3, E5M2, E2M1X2 = 0, 1, 2, 3, 4, 5
@@ -95,6 +95,7 @@ _SIGS = {
     "amp_optimizer_step": ([_P, _P, _P, _P, _I, _P, _I, _I64, _P, _P, _I, _P], _I),
     "amp_check_overflow": ([_P, _I, _I64, _P, _P], _I),
     "amp_optimizer_step_ex": ([_P, _P, _P, _P, _I, _P, _I, _I64, _P, _P, _P, _I, _P], _I),
+    "amp_stream_copy": ([_P, _P, _I64, _P], _I),
     "amp_grad_accumulate": ([_P, _P, _I, _I64, _I, _P], _I),
     "amp_mx_quantize": ([_P, _I, _I64, _I64, _I64, _I, _I, _P, _P, _P], _I),
     "amp_quantize_blockwise": ([_P, _I, _I64, _I64, _I64, _I, _I, _P, _I64, _P, _I64, _P, _I64,
@@ -324,3 +325,7 @@ def amp_gelu_backward_f16(dA16, z16, n, dz16, stream=None):
 def amp_colsum_f16(x16, rows, cols, out16, stream=None):
     _check("amp_colsum_f16", load().amp_colsum_f16(_ptr(x16), rows, cols, _ptr(out16),
                                                    _stream(stream)))
+
+
+def amp_stream_copy(src, dst, nbytes, stream=None):
+    _check("amp_stream_copy", load().amp_stream_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))

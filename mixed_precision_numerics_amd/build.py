@@ -44,8 +44,17 @@ def hipcc() -> str:
     return shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
 
 
-def _compile(src: str) -> str:
+def _headers_mtime() -> float:
+    hs = glob.glob(os.path.join(CSRC, "*.hpp")) + glob.glob(os.path.join(ROOT, "include", "*.h"))
+    return max((os.path.getmtime(h) for h in hs), default=0.0)
+
+
+def _compile(src: str, incremental: bool = False) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+    if incremental and os.path.exists(obj):
+        newest = max(os.path.getmtime(src), _headers_mtime(), os.path.getmtime(__file__))
+        if os.path.getmtime(obj) > newest:
+            return obj
     extra = PER_FILE.get(os.path.basename(src), [])
     cmd = [hipcc(), "-c", src, "-o", obj] + COMMON + DEVICE + extra
     if src.endswith(".cpp"):
@@ -56,12 +65,14 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
+def build(verbose: bool = False, jobs: int | None = None, incremental: bool = False) -> str:
+    """Compile every source (``incremental``: reuse objects newer than their
+    source, the headers and this script) and link the library."""
     os.makedirs(BUILD, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")) + glob.glob(os.path.join(CSRC, "*.cpp")))
     jobs = jobs or min(8, max(1, len(srcs)))
     with cf.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(_compile, srcs))
+        objs = list(ex.map(lambda src: _compile(src, incremental), srcs))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "-shared", "-o", tmp] + objs + ["--offload-arch=" + ARCH, "-fPIC"]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -74,4 +85,4 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    build(verbose=True, incremental="--incremental" in sys.argv)

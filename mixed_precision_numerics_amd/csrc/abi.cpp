@@ -420,4 +420,12 @@ int amp_colsum_f16(const void* x16, int64_t rows, int64_t cols, void* out16, voi
   return hip_status(amp::launch_colsum(x16, rows, cols, out16, static_cast<hipStream_t>(stream)));
 }
 
+int amp_stream_copy(const void* src, void* dst, int64_t bytes, void* stream) {
+  if (bytes < 0) return AMP_EINVAL;
+  if (bytes == 0) return AMP_OK;
+  if (!src || !dst || !amp::aligned(src, 16) || !amp::aligned(dst, 16)) return AMP_EINVAL;
+  if (int st = check_device()) return st;
+  return hip_status(amp::launch_stream_copy(src, dst, bytes, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

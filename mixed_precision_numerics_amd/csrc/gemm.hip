@@ -1016,6 +1016,15 @@ __global__ __launch_bounds__(256) void gemm_generic(GemmArgs g, int a_kc, int b_
   store_c<CT>(g.C, row * g.ldc + col, acc * alpha);
 }
 
+// An empty sum (K == 0): C = +0 everywhere; neither operand nor scale is read.
+template <int CT>
+__global__ __launch_bounds__(256) void gemm_zero(GemmArgs g) {
+  const int64_t col = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x & 15);
+  const int64_t row = static_cast<int64_t>(blockIdx.y) * 16 + (threadIdx.x >> 4);
+  if (row >= g.M || col >= g.N) return;
+  store_c<CT>(g.C, row * g.ldc + col, 0.0f);
+}
+
 
 // ------------------------------------------- fine-grained FP8 (blockwise)
 // Page itwiki, section "FP8 혼합 정밀도": DeepSeek-V3's operands carry one
@@ -1379,6 +1388,16 @@ hipError_t launch_gemm(int opA, int opB, int64_t M, int64_t N, int64_t K, const 
              bsA ? bsA->scales : nullptr, bsB ? bsB->scales : nullptr,
              bsA ? bsA->ld : 0, bsB ? bsB->ld : 0, bsA ? bsA->block2d : 0,
              bsB ? bsB->block2d : 0, mx ? 1 : 0};
+  if (K == 0) {
+    // every kernel below assumes at least one K-step
+    const dim3 grid(static_cast<unsigned>((N + 15) / 16), static_cast<unsigned>((M + 15) / 16));
+    switch (ct) {
+      case AMP_F32: gemm_zero<AMP_F32><<<grid, 256, 0, s>>>(g); break;
+      case AMP_BF16: gemm_zero<AMP_BF16><<<grid, 256, 0, s>>>(g); break;
+      default: gemm_zero<AMP_F16><<<grid, 256, 0, s>>>(g); break;
+    }
+    return hipGetLastError();
+  }
   if (mx) return launch_mx(g, at, bt, ct, s);
   const bool a_kc = opA == AMP_OP_N, b_kc = opB == AMP_OP_T;
   if (at == AMP_E2M1X2) {

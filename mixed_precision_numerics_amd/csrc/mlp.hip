@@ -63,6 +63,14 @@ __global__ __launch_bounds__(256) void softmax_xent_kernel(
     for (int64_t c = 0; c < cols; ++c) s += expf(h2f(l[c]) - m);
     const float lse = m + logf(s);
     const int32_t y = labels[r];
+    if (y < 0 || y >= cols) {
+      // a label outside 0..cols-1 has no loss term: the row adds NaN to the
+      // loss and contributes a zero gradient (nothing out of range is read)
+      acc += __builtin_nanf("");
+      if (dlog)
+        for (int64_t c = 0; c < cols; ++c) dlog[r * cols + c] = 0;
+      continue;
+    }
     acc += lse - h2f(l[y]);
     if (dlog) {
       const float inv_s = 1.0f / s;

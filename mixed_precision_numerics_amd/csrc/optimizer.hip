@@ -45,8 +45,13 @@ __device__ __forceinline__ uint32_t nonfinite_word(uint32_t w) {
 template <int GT, bool VEC>
 __global__ __launch_bounds__(kThreads) void check_kernel(const void* __restrict__ g, int64_t n,
                                                          amp_scaler_state* __restrict__ st) {
-  // a block that starts after the flag is already set has nothing to add
-  if (__hip_atomic_load(&st->found_inf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) return;
+  // a block that starts after the flag is already set has nothing to add;
+  // one thread reads the flag so that the whole block leaves together
+  __shared__ int done;
+  if (threadIdx.x == 0)
+    done = __hip_atomic_load(&st->found_inf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  if (done) return;
   const int eb = GT == AMP_F32 ? 4 : 2;
   const int64_t nvec = VEC ? n * eb / 16 : 0;
   const u32x4* gv = static_cast<const u32x4*>(g);

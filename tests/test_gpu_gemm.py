@@ -92,6 +92,24 @@ def test_gemm_k_zero_and_padded_ldc():
     assert np.all(out.view(np.float32) == 0.0)
 
 
+@pytest.mark.parametrize("kind", ["bf16", "f16", "fp8", "fp8_native", "nvfp4", "mx4", "mx8"])
+@pytest.mark.parametrize("ct", [amp.F32, amp.BF16])
+def test_gemm_k_zero_full_tiles(kind, ct):
+    """K == 0 on whole 256x256 tiles (the shapes that reach the direct-to-LDS
+    kernels otherwise): C is zero and no operand or scale is read (all the
+    operand pointers given are one-byte buffers and lda = ldb = 0 is valid)."""
+    M, N = 512, 256
+    at = {"bf16": amp.BF16, "f16": amp.F16, "fp8": amp.E4M3, "fp8_native": amp.E4M3,
+          "nvfp4": amp.E2M1X2, "mx4": amp.E2M1X2, "mx8": amp.E5M2}[kind]
+    flags = {"fp8_native": amp.GEMM_FP8_NATIVE, "mx4": amp.GEMM_MX, "mx8": amp.GEMM_MX}.get(kind, 0)
+    one = empty(16)
+    bs = amp.BlockScales(one.data_ptr(), 0, 0) if kind in ("nvfp4", "mx4", "mx8") else None
+    c = empty(M * N * CT[ct][2], fill=0x7F)
+    amp.amp_gemm_ex(amp.OP_N, amp.OP_T, M, N, 0, one, at, 0, None, one, at, 0, None, c, ct, N,
+                    bsA=bs, bsB=bs, flags=flags)
+    assert np.all(host(c, CT[ct][1]) == 0)
+
+
 def fp8_operands(seed, M, N, K, fa, fb):
     x = synth.student_t_f32(seed, (M, K), scale=3.0)
     w = synth.normal_f32(seed + 1, (N, K), 0.02)

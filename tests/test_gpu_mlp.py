@@ -116,11 +116,7 @@ def test_mlp_ops_match_oracle_step_by_step():
         dlog = out16(B * DO)
         amp.amp_softmax_xent_f16(dev16(fb["logits"]), dev(y.astype(np.int32)), B, DO, st, loss, dlog)
         assert abs(float(host(loss, np.float32)[0]) - fb["loss"]) <= 1e-5 * abs(fb["loss"]), t
-        lg = fb["logits"] - fb["logits"].max(axis=1, keepdims=True)
-        prob = np.exp(lg) / np.exp(lg).sum(axis=1, keepdims=True)
-        onehot = np.zeros_like(prob)
-        onehot[np.arange(B), y] = 1.0
-        assert within_one_ulp16(h16(dlog), (S * (prob - onehot) / B).ravel()).all(), t
+        assert within_one_ulp16(h16(dlog), fb["dlog"].ravel()).all(), t
 
         # backward GEMMs and glue, each from the oracle's tensors
         dlogd = dev16(fb["dlog"])
@@ -245,3 +241,27 @@ def test_mlp_amp_ten_steps_free_running():
     rel = np.abs(gl - rl) / np.abs(rl)
     print("losses gpu", np.round(gl, 5), "max rel diff vs oracle", rel.max())
     assert rel.max() < 1e-3
+
+
+def test_softmax_xent_labels_out_of_range():
+    """Labels outside 0..cols-1 read nothing: their rows add NaN to the loss
+    and get zero gradients; the other rows are what they are with valid
+    labels (the cross-entropy itself is checked against the oracle above)."""
+    rows, cols = 8, DO
+    rng = synth.rng(77)
+    lg = F.round_to(rng.standard_normal((rows, cols)), F.F16)
+    y = rng.integers(0, cols, size=rows).astype(np.int32)
+    loss = torch.empty(1, device="cuda")
+    dlog = out16(rows * cols)
+    amp.amp_softmax_xent_f16(dev16(lg), dev(y), rows, cols, None, loss, dlog)
+    assert np.isfinite(host(loss, np.float32)[0])
+    good = h16(dlog, (rows, cols)).copy()
+    bad_y = y.copy()
+    bad_y[2], bad_y[5] = -1, cols
+    dlog.fill_(0x3c00)
+    amp.amp_softmax_xent_f16(dev16(lg), dev(bad_y), rows, cols, None, loss, dlog)
+    assert np.isnan(host(loss, np.float32)[0])
+    got = h16(dlog, (rows, cols))
+    assert np.all(got[[2, 5]] == 0)
+    keep = [r for r in range(rows) if r not in (2, 5)]
+    assert np.array_equal(got[keep], good[keep])

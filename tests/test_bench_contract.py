@@ -20,9 +20,13 @@ def test_more_than_one_gpu_exits_with_a_message():
 
 
 def test_cpu_baseline_record():
-    rec = bench.cpu_baseline(sample=4096, steps=2)
-    assert rec["kind"] == "oracle" and rec["unit"] == "GB/s" and rec["cores"] == 1
-    assert rec["value"] > 0 and "4096 params x 2" in rec["sample"]
+    rec = bench.cpu_baseline(sample=4096, steps=2, gemm_mnk=(64, 48, 32))
+    cores = min(16, len(os.sched_getaffinity(0)))
+    assert rec["kind"] == "oracle" and rec["unit"] == "GB/s" and rec["cores"] == cores
+    assert rec["value"] > 0 and f"{cores} processes x 4096 params x 2" in rec["sample"]
+    assert rec["host"]["os_cpu_count"] == os.cpu_count()
+    assert rec["host"]["affinity"] == len(os.sched_getaffinity(0))
+    assert rec["gemm"]["shape"] == [64, 48, 32] and rec["gemm"]["gflops"] > 0
 
 
 def test_traffic_lookup_follows_the_source_hash(tmp_path, monkeypatch):

@@ -453,6 +453,20 @@ int amp_grad_norm_init(amp_grad_norm_state* d_norm, void* stream);
 int amp_grad_norm_accumulate(const void* grads, int gt, int64_t n, amp_scaler_state* d_state,
                              amp_grad_norm_state* d_norm, void* stream);
 
+/* amp_grad_norm_accumulate_noalloc -- amp_grad_norm_accumulate for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same kernels and the
+ * same result bit for bit, but the running sum is one caller float64
+ * (*d_sumsq += ..., the caller zeroes it) and the per-work-group partials
+ * live in a file-scope device array of the library (1024 float64 = 8 KiB per
+ * GPU, kept until the process ends; the pass never uses more work-groups, so
+ * every n fits).  The call allocates nothing.  All calls on one GPU share
+ * that array: calls that overlap on one GPU (other streams, other threads)
+ * race and must be serialised by the caller.  d_sumsq: device, 8-byte
+ * aligned. */
+int amp_grad_norm_accumulate_noalloc(const void* grads, int gt, int64_t n,
+                                     amp_scaler_state* d_state, double* d_sumsq, void* stream);
+
 /* d_out[0] = coef = min(1, fl32(max_norm / fl32(norm + 1e-6))) and d_out[1] =
  * norm, with norm = fl32(sqrt(sumsq)) (float64 square root); if found_inf is
  * set: d_out = {1, +inf} (the step will be skipped).  max_norm > 0. */

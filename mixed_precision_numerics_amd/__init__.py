@@ -27,7 +27,7 @@ __all__ = [
     "amp_clip_coefficient", "amp_optimizer_step_ex", "NORM_STATE_BYTES", "NORM_PARTIALS",
     "amp_cast_current_scaling", "amp_mx_quantize", "GEMM_MX",
     "amp_quantize_blockwise", "amp_gemm_blockwise", "amp_cast_ex",
-    "amp_found_inf_from_amax", "amp_stream_copy",
+    "amp_found_inf_from_amax", "amp_stream_copy", "amp_grad_norm_accumulate_noalloc",
 ]
 
 F32, F16, BF16, E4M3, E5M2, E2M1X2 = 0, 1, 2, 3, 4, 5
@@ -96,6 +96,7 @@ _SIGS = {
     "amp_check_overflow": ([_P, _I, _I64, _P, _P], _I),
     "amp_optimizer_step_ex": ([_P, _P, _P, _P, _I, _P, _I, _I64, _P, _P, _P, _I, _P], _I),
     "amp_stream_copy": ([_P, _P, _I64, _P], _I),
+    "amp_grad_norm_accumulate_noalloc": ([_P, _I, _I64, _P, _P, _P], _I),
     "amp_grad_accumulate": ([_P, _P, _I, _I64, _I, _P], _I),
     "amp_mx_quantize": ([_P, _I, _I64, _I64, _I64, _I, _I, _P, _P, _P], _I),
     "amp_quantize_blockwise": ([_P, _I, _I64, _I64, _I64, _I, _I, _P, _I64, _P, _I64, _P, _I64,
@@ -272,6 +273,11 @@ def amp_grad_norm_init(d_norm, stream=None):
 def amp_grad_norm_accumulate(grads, gt, n, d_state, d_norm, stream=None):
     _check("amp_grad_norm_accumulate", load().amp_grad_norm_accumulate(
         _ptr(grads), gt, n, _ptr(d_state), _ptr(d_norm), _stream(stream)))
+
+
+def amp_grad_norm_accumulate_noalloc(grads, gt, n, d_state, d_sumsq, stream=None):
+    _check("amp_grad_norm_accumulate_noalloc", load().amp_grad_norm_accumulate_noalloc(
+        _ptr(grads), gt, n, _ptr(d_state), _ptr(d_sumsq), _stream(stream)))
 
 
 def amp_clip_coefficient(d_norm, max_norm, d_state, d_out, stream=None):

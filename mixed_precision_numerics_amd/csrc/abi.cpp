@@ -319,6 +319,18 @@ int amp_grad_norm_accumulate(const void* grads, int gt, int64_t n, amp_scaler_st
                                           static_cast<hipStream_t>(stream)));
 }
 
+int amp_grad_norm_accumulate_noalloc(const void* grads, int gt, int64_t n,
+                                     amp_scaler_state* d_state, double* d_sumsq, void* stream) {
+  if (!al(d_state, 8) || !al(d_sumsq, 8)) return AMP_EINVAL;
+  if (n < 0 || !d_state || !d_sumsq) return AMP_EINVAL;
+  if (!is_grad(gt)) return AMP_EUNSUPPORTED;
+  if (n == 0) return AMP_OK;
+  if (!grads) return AMP_EINVAL;
+  if (int st = check_device()) return st;
+  return hip_status(amp::launch_grad_norm_noalloc(grads, gt, n, d_state, d_sumsq,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
 int amp_clip_coefficient(const amp_grad_norm_state* d_norm, float max_norm,
                          const amp_scaler_state* d_state, float* d_out, void* stream) {
   if (!al(d_norm, 8) || !al(d_state, 8) || !al(d_out, 4)) return AMP_EINVAL;

@@ -78,6 +78,8 @@ hipError_t launch_optimizer_apply(float* master, float* m, float* v, const void*
 hipError_t launch_grad_accumulate(float* acc, const void* g, int gt, int64_t n, int first,
                                   hipStream_t s);
 hipError_t launch_grad_norm_init(amp_grad_norm_state* ns, hipStream_t s);
+hipError_t launch_grad_norm_noalloc(const void* g, int gt, int64_t n, amp_scaler_state* st,
+                                    double* sumsq, hipStream_t s);
 hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
 hipError_t launch_grad_norm(const void* g, int gt, int64_t n, amp_scaler_state* st,
                             amp_grad_norm_state* ns, hipStream_t s);

@@ -21,6 +21,8 @@
 // The per-element arithmetic is FP32 without contraction (-ffp-contract=off):
 //   g = f32(g16)*invS; m = b1*m + c1*g; v = b2*v + c2*(g*g);
 //   d = sqrt(v)*rbc2 + eps; theta = theta*decay - step*(m/d); w16 = rne(theta).
+#include <mutex>
+
 #include "common.hpp"
 #include "formats.hpp"
 
@@ -444,12 +446,13 @@ __global__ __launch_bounds__(kNormThreads) void norm_kernel(const void* __restri
 }
 
 // sumsq += (partials in order) * (1/S)^2 -- exact scaling by a power of two.
-__global__ void norm_finalize(amp_grad_norm_state* ns, int nb, const amp_scaler_state* st) {
+__global__ void norm_finalize(const double* __restrict__ partial, double* __restrict__ sumsq,
+                              int nb, const amp_scaler_state* st) {
   if (threadIdx.x != 0) return;
   double t = 0.0;
-  for (int b = 0; b < nb; ++b) t += ns->partial[b];
+  for (int b = 0; b < nb; ++b) t += partial[b];
   const double inv = static_cast<double>(1.0f / st->scale);
-  ns->sumsq += t * inv * inv;
+  *sumsq += t * inv * inv;
 }
 
 __global__ void norm_init_kernel(amp_grad_norm_state* ns) {
@@ -593,24 +596,79 @@ hipError_t launch_grad_norm_init(amp_grad_norm_state* ns, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_grad_norm(const void* g, int gt, int64_t n, amp_scaler_state* st,
-                            amp_grad_norm_state* ns, hipStream_t s) {
-  const bool vec = aligned(g, 16);
+namespace {
+
+// Work-groups of one norm pass: one float64 partial each, at most
+// AMP_NORM_PARTIALS whatever n is (grid-stride loop).
+int64_t norm_blocks(int64_t n) {
   int64_t nb = (n + 8 * kNormThreads - 1) / (8 * kNormThreads);
   if (nb > AMP_NORM_PARTIALS) nb = AMP_NORM_PARTIALS;
-  if (nb < 1) nb = 1;
+  return nb < 1 ? 1 : nb;
+}
+
+hipError_t launch_norm_pass(const void* g, int gt, int64_t n, amp_scaler_state* st,
+                            double* partial, double* sumsq, int64_t nb, hipStream_t s) {
+  const bool vec = aligned(g, 16);
   const dim3 grid(static_cast<unsigned>(nb));
 #define AMP_NORM(T)                                                                        \
-  if (vec) norm_kernel<T, true><<<grid, kNormThreads, 0, s>>>(g, n, st, ns->partial);       \
-  else norm_kernel<T, false><<<grid, kNormThreads, 0, s>>>(g, n, st, ns->partial);
+  if (vec) norm_kernel<T, true><<<grid, kNormThreads, 0, s>>>(g, n, st, partial);           \
+  else norm_kernel<T, false><<<grid, kNormThreads, 0, s>>>(g, n, st, partial);
   switch (gt) {
     case AMP_F32: AMP_NORM(AMP_F32) break;
     case AMP_BF16: AMP_NORM(AMP_BF16) break;
     default: AMP_NORM(AMP_F16) break;
   }
 #undef AMP_NORM
-  norm_finalize<<<1, 64, 0, s>>>(ns, static_cast<int>(nb), st);
+  norm_finalize<<<1, 64, 0, s>>>(partial, sumsq, static_cast<int>(nb), st);
   return hipGetLastError();
+}
+
+}  // namespace
+
+// Scratch of the no-allocation norm entry point: the per-work-group float64
+// partials that amp_grad_norm_accumulate keeps in the caller's state struct.
+// One copy per GPU, held until the process ends (8 KiB); every pass writes the
+// slots it reads, so nothing needs clearing between calls.
+constexpr int kNormScratchPartials = AMP_NORM_PARTIALS;   // 1024 float64 = 8 KiB
+constexpr int kMaxScratchDevices = 64;
+static __device__ __align__(256) double scratch[kNormScratchPartials];
+
+namespace {
+
+// Device address of `scratch` on the current GPU, looked up once per device
+// with that device current (the array's name is only a host-side stand-in).
+hipError_t scratch_on_current_device(double** out) {
+  static std::mutex mu;
+  static double* ptr[kMaxScratchDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptr[dev] = static_cast<double*>(p);
+  }
+  *out = ptr[dev];
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_grad_norm(const void* g, int gt, int64_t n, amp_scaler_state* st,
+                            amp_grad_norm_state* ns, hipStream_t s) {
+  return launch_norm_pass(g, gt, n, st, ns->partial, &ns->sumsq, norm_blocks(n), s);
+}
+
+hipError_t launch_grad_norm_noalloc(const void* g, int gt, int64_t n, amp_scaler_state* st,
+                                    double* sumsq, hipStream_t s) {
+  const int64_t nb = norm_blocks(n);
+  if (nb > kNormScratchPartials) return hipErrorInvalidValue;   // never: the grid is capped
+  double* partial = nullptr;
+  if (hipError_t e = scratch_on_current_device(&partial)) return e;
+  return launch_norm_pass(g, gt, n, st, partial, sumsq, nb, s);
 }
 
 hipError_t launch_clip_coefficient(const amp_grad_norm_state* ns, float max_norm,

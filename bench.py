@@ -516,7 +516,9 @@ def mx_workload(torch, amp):
     W = (torch.randn(O, I, device="cuda", generator=gen) * 0.02).to(torch.bfloat16)
     out = {}
     flops = 2 * T * O * I
-    for name, yt, peak in (("mxfp4", amp.E2M1X2, FP4_PEAK_TFLOPS), ("mxfp8", amp.E4M3, FP8_PEAK_TFLOPS)):
+    for name, yt, peak in (("mxfp4", amp.E2M1X2, FP4_PEAK_TFLOPS), ("mxfp8", amp.E4M3, FP8_PEAK_TFLOPS),
+                           ("mxfp8_native", amp.E4M3, FP8_PEAK_TFLOPS)):
+        gflags = amp.GEMM_MX | (amp.GEMM_FP8_NATIVE if name == "mxfp8_native" else 0)
         div = 2 if yt == amp.E2M1X2 else 1
         qx = torch.empty(T * I // div, device="cuda", dtype=torch.uint8)
         qw = torch.empty(O * I // div, device="cuda", dtype=torch.uint8)
@@ -535,12 +537,17 @@ def mx_workload(torch, amp):
         bsw = amp.BlockScales(sw.data_ptr(), I // 32, 0, 0)
         g_ms = _timed(torch, lambda: amp.amp_gemm_ex(amp.OP_N, amp.OP_T, T, O, I, qx, yt, I // div,
                                                      None, qw, yt, I // div, None, Y, amp.BF16, O,
-                                                     bsx, bsw, flags=amp.GEMM_MX), 10)
+                                                     bsx, bsw, flags=gflags), 10)
         tf = flops / g_ms / 1e9
         qbytes = T * I * (2 + 1.0 / div + 1.0 / 32)
         out[name] = {"gemm_ms": round(g_ms, 4), "gemm_tflops": round(tf, 1), "peak_tflops": peak,
                      "frac": round(tf / peak, 4), "quantize_ms": round(q_ms, 4),
                      "quantize_gbs": round(qbytes / q_ms / 1e6, 1)}
+        if name == "mxfp8":
+            out[name]["mfma"] = "bf16 (FP8 x UE8M0 block scale widened exactly; FP32 sums)"
+            out[name]["frac_bf16_mfma"] = round(tf / BF16_PEAK_TFLOPS, 4)
+        if name == "mxfp8_native":
+            out[name]["mfma"] = "block-scaled FP8 (reduced-precision 64-term sums)"
         del qx, qw, sx, sw, Y
     del X, W
     torch.cuda.empty_cache()

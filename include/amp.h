@@ -197,20 +197,28 @@ int amp_gemm(int opA, int opB, int64_t M, int64_t N, int64_t K,
  *   with a reduced-precision internal sum (measured: errors near 2^-12 of the
  *   largest product in each 64-term group), the kind of limited FP8
  *   partial-sum precision hwlabs "GEMM 누적 정밀도 문제" describes for other
- *   hardware; the results between groups are accumulated in FP32.  Without
- *   the flag (the default) FP8 operands are widened exactly to BF16 in
- *   registers before the BF16 matrix cores and every product is summed in
- *   FP32.
+ *   hardware; the results between groups are accumulated in FP32.  (Every
+ *   FP8 matrix-core instruction of gfx950 -- 32x32x16 and 16x16x32, and the
+ *   block-scaled 32x32x64 and 16x16x128 -- measured the same way: see
+ *   amp_fp8_mfma_probe.)  Without the flag (the default) FP8 operands are
+ *   widened exactly to BF16 in registers before the BF16 matrix cores and
+ *   every product is summed in FP32.
  * AMP_GEMM_MX: both operands are MX blocks from amp_mx_quantize (opA = N,
  *   opB = T; at = bt = AMP_E2M1X2, or at, bt in {E4M3, E5M2}); bsA / bsB hold
  *   the UE8M0 scale codes [rows, K/32] (block2d = 0, ld in bytes) and
  *   C = out_cast(alphaA * alphaB * sum_k a[m,k] 2^(sa-127) b[n,k] 2^(sb-127)).
  *   Full 256x256 tiles with K a multiple of 128 (FP8) or 256 (E2M1) run on
- *   the CDNA4 block-scaled matrix cores, which take the scales per 32
- *   elements directly (FP8 elements there have the reduced-precision
- *   internal sum described above; E2M1 products are short enough to sum
- *   exactly); other shapes use an element-wise FP32 kernel.
- * Other flags must be 0. */
+ *   the matrix cores, other shapes on an element-wise FP32 kernel.  FP8
+ *   elements: each element times its block scale is formed exactly in BF16
+ *   by the scaled conversion and summed on the BF16 matrix cores in FP32
+ *   (exact products whenever the scaled elements are BF16 values: scale
+ *   codes 3..246 for E4M3, 10..239 for E5M2, which amp_mx_quantize produces
+ *   for every block whose maximum is at least 2^-116 / 2^-102); with
+ *   AMP_GEMM_FP8_NATIVE as well they go to the block-scaled FP8 instruction
+ *   instead (its reduced-precision internal sum).  E2M1 elements always use
+ *   the block-scaled instruction, whose few product bits it sums exactly.
+ * Other flags must be 0 (AMP_GEMM_FP8_NATIVE with E2M1 MX operands is
+ * AMP_EINVAL). */
 #define AMP_GEMM_FP8_NATIVE 1
 #define AMP_GEMM_MX 2
 int amp_gemm_ex(int opA, int opB, int64_t M, int64_t N, int64_t K,
@@ -490,6 +498,28 @@ int amp_optimizer_step_ex(float* master, float* m, float* v, const void* grads, 
  * overlapping; bytes == 0 is a no-op; misaligned or NULL pointers give
  * AMP_EINVAL. */
 int amp_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);
+
+/* amp_fp8_mfma_probe -- one FP8 matrix-core instruction per wave on given
+ * operand bytes, C_in = 0: the measurement behind AMP_GEMM_FP8_NATIVE's
+ * precision note (hwlabs "GEMM 누적 정밀도 문제": FP8 matrix units may keep
+ * limited precision in their partial sums); not a step of the training path.
+ * shape: 0 = 32x32x16 FP8, 1 = 16x16x32 FP8, 2 = block-scaled 32x32x64
+ * f8f6f4, 3 = block-scaled 16x16x128 f8f6f4 (neutral scales, 2^0).
+ * at: format of A, AMP_E4M3 or AMP_E5M2; B is E4M3.
+ * Layout, per tile t (tiles of them) and lane l = 0..63, with D = 32 (shapes
+ * 0, 2) or 16 (1, 3), P = 8 (shapes 0, 1) or 32 (2, 3) bytes per lane and
+ * R = 16 (32x32) or 4 (16x16) outputs per lane:
+ *   a[(t*64 + l)*P + j], b[(t*64 + l)*P + j]: lane l holds row l % D of A
+ *   and column l % D of B; A's byte j of lane l meets B's byte j of every
+ *   lane with the same l / D (the same K index on both sides), so
+ *   C[i][n] = sum over groups q < 64/D and bytes j of
+ *             a[q*D + i][j] * b[q*D + n][j];
+ *   c[(t*64 + l)*R + r] = C[row][l % D] with row = 8*(r/4) + 4*(l/32) + r%4
+ *   (32x32) or 4*(l/16) + r (16x16).
+ * a, b: device, 8-byte (shapes 0, 1) or 32-byte (2, 3) aligned; c: device,
+ * 4-byte aligned.  tiles == 0 is a no-op. */
+int amp_fp8_mfma_probe(int shape, int at, const void* a, const void* b, float* c,
+                       int64_t tiles, void* stream);
 
 #ifdef __cplusplus
 }

@@ -28,6 +28,7 @@ __all__ = [
     "amp_cast_current_scaling", "amp_mx_quantize", "GEMM_MX",
     "amp_quantize_blockwise", "amp_gemm_blockwise", "amp_cast_ex",
     "amp_found_inf_from_amax", "amp_stream_copy", "amp_grad_norm_accumulate_noalloc",
+    "amp_fp8_mfma_probe",
 ]
 
 F32, F16, BF16, E4M3, E5M2, E2M1X2 = 0, 1, 2, 3, 4, 5
@@ -96,6 +97,7 @@ _SIGS = {
     "amp_check_overflow": ([_P, _I, _I64, _P, _P], _I),
     "amp_optimizer_step_ex": ([_P, _P, _P, _P, _I, _P, _I, _I64, _P, _P, _P, _I, _P], _I),
     "amp_stream_copy": ([_P, _P, _I64, _P], _I),
+    "amp_fp8_mfma_probe": ([_I, _I, _P, _P, _P, _I64, _P], _I),
     "amp_grad_norm_accumulate_noalloc": ([_P, _I, _I64, _P, _P, _P], _I),
     "amp_grad_accumulate": ([_P, _P, _I, _I64, _I, _P], _I),
     "amp_mx_quantize": ([_P, _I, _I64, _I64, _I64, _I, _I, _P, _P, _P], _I),
@@ -335,3 +337,8 @@ def amp_colsum_f16(x16, rows, cols, out16, stream=None):
 
 def amp_stream_copy(src, dst, nbytes, stream=None):
     _check("amp_stream_copy", load().amp_stream_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
+
+
+def amp_fp8_mfma_probe(shape, at, a, b, c, tiles, stream=None):
+    _check("amp_fp8_mfma_probe", load().amp_fp8_mfma_probe(shape, at, _ptr(a), _ptr(b), _ptr(c),
+                                                           tiles, _stream(stream)))

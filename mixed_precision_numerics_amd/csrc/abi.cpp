@@ -139,7 +139,8 @@ int amp_gemm_ex(int opA, int opB, int64_t M, int64_t N, int64_t K, const void* A
   if (mx) {
     const bool fp4 = at == AMP_E2M1X2 && bt == AMP_E2M1X2;
     if (!fp4 && !(is_fp8(at) && is_fp8(bt))) return AMP_EUNSUPPORTED;
-    if (opA != AMP_OP_N || opB != AMP_OP_T || (flags & AMP_GEMM_FP8_NATIVE)) return AMP_EINVAL;
+    if (opA != AMP_OP_N || opB != AMP_OP_T || (fp4 && (flags & AMP_GEMM_FP8_NATIVE)))
+      return AMP_EINVAL;
     if (!bsA || !bsB || !bsA->scales || !bsB->scales || bsA->block2d || bsB->block2d)
       return AMP_EINVAL;
     if (K % 32 != 0) return AMP_EINVAL;
@@ -438,6 +439,19 @@ int amp_stream_copy(const void* src, void* dst, int64_t bytes, void* stream) {
   if (!src || !dst || !amp::aligned(src, 16) || !amp::aligned(dst, 16)) return AMP_EINVAL;
   if (int st = check_device()) return st;
   return hip_status(amp::launch_stream_copy(src, dst, bytes, static_cast<hipStream_t>(stream)));
+}
+
+int amp_fp8_mfma_probe(int shape, int at, const void* a, const void* b, float* c, int64_t tiles,
+                       void* stream) {
+  if (shape < 0 || shape > 3 || tiles < 0) return AMP_EINVAL;
+  if (at != AMP_E4M3 && at != AMP_E5M2) return AMP_EUNSUPPORTED;
+  if (tiles == 0) return AMP_OK;
+  const uintptr_t al_ab = shape <= 1 ? 8 : 32;
+  if (!a || !b || !c || !amp::aligned(a, al_ab) || !amp::aligned(b, al_ab) || !amp::aligned(c, 4))
+    return AMP_EINVAL;
+  if (int st = check_device()) return st;
+  return hip_status(amp::launch_fp8_mfma_probe(shape, at, a, b, c, tiles,
+                                               static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

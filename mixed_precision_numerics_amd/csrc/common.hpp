@@ -81,6 +81,8 @@ hipError_t launch_grad_norm_init(amp_grad_norm_state* ns, hipStream_t s);
 hipError_t launch_grad_norm_noalloc(const void* g, int gt, int64_t n, amp_scaler_state* st,
                                     double* sumsq, hipStream_t s);
 hipError_t launch_stream_copy(const void* src, void* dst, int64_t bytes, hipStream_t s);
+hipError_t launch_fp8_mfma_probe(int shape, int at, const void* a, const void* b, float* c,
+                                 int64_t tiles, hipStream_t s);
 hipError_t launch_grad_norm(const void* g, int gt, int64_t n, amp_scaler_state* st,
                             amp_grad_norm_state* ns, hipStream_t s);
 hipError_t launch_clip_coefficient(const amp_grad_norm_state* ns, float max_norm,

@@ -68,6 +68,8 @@ enum Path : int {
   kPMX8 = 4,      // MX, FP8 elements + UE8M0 scale per 32: block-scaled MFMA, BK = 128
   kPMX4 = 5,      // MX, E2M1 elements + UE8M0 scale per 32: block-scaled MFMA, BK = 256
   kPFP4D = 6,     // NVFP4 codes in LDS, decoded per fragment to F16 x block scale, F16 MFMA, BK = 256
+  kPMX8E = 7,     // MX, FP8 elements in LDS, widened per fragment to BF16 times the UE8M0 block
+                  // scale (exact for scaled elements within BF16's range), BF16 MFMA, BK = 128
 };
 
 struct GemmArgs {
@@ -112,11 +114,18 @@ __device__ __forceinline__ void transpose8x8_16(const u32x4 (&v)[8], u32x4 (&o)[
 
 // FP8 (E4M3 or E5M2) -> BF16, exact: 2 values per conversion instruction.
 template <int FMT, bool HI>
-__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w, float scale = 1.0f) {
   if constexpr (FMT == AMP_E4M3)
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, scale, HI));
   else
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, 1.0f, HI));
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_bf8(w, scale, HI));
+}
+
+// A UE8M0 block scale 2^(c - 127) as the FP32 operand of the scaled
+// conversions: code 0 is 2^-127 (an FP32 subnormal), 0xFF is NaN; both the
+// value and its exponent field read as the same power of two.
+__device__ __forceinline__ float e8m0_scale(uint32_t c) {
+  return bitsf(c == 0u ? 0x00400000u : (c == 255u ? 0x7fc00000u : c << 23));
 }
 
 // Two E2M1 codes (byte SEL of w) times the block scale S -> two BF16.  The
@@ -610,8 +619,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
   // loads into one from the fragment reads of the other
   __shared__ __align__(16) uint8_t smem0[2][kOperandBytes];
   __shared__ __align__(16) uint8_t smem1[2][kOperandBytes];
-  constexpr bool kF8 = PATH == kPF8Native || PATH == kPF8Exact || PATH == kPMX8;
-  constexpr bool kMX = PATH == kPMX8 || PATH == kPMX4;
+  constexpr bool kF8 = PATH == kPF8Native || PATH == kPF8Exact || PATH == kPMX8 || PATH == kPMX8E;
+  constexpr bool kMX = PATH == kPMX8 || PATH == kPMX4 || PATH == kPMX8E;
   constexpr bool kFP4 = PATH == kPMX4 || PATH == kPFP4D;
   constexpr int BK = kFP4 ? 256 : (kF8 ? 128 : 64);               // K elements per step
   constexpr int EB = kF8 || kFP4 ? 1 : 2;                         // row stride unit (bytes for FP4)
@@ -844,18 +853,25 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
                                                                    __builtin_bit_cast(f16x8_t, db[nb]),
                                                                    acc[mb][nb], 0, 0, 0);
         }
-      } else if constexpr (PATH == kPF8Exact) {
+      } else if constexpr (PATH == kPF8Exact || PATH == kPMX8E) {
         // 16 FP8 bytes per lane = K 32p + 16h + 8e + j for e = 0, 1: two BF16
-        // fragments (the same K order for A and B; products are exact)
+        // fragments (the same K order for A and B; products are exact).  MX:
+        // slice ks is MX block ks of the step for both lane halves, and the
+        // conversion multiplies by that block's power-of-two scale
         u32x4 da[2][4], db[2][4];
 #pragma unroll
         for (int mb = 0; mb < 4; ++mb) {
+          float sa = 1.0f, sb = 1.0f;
+          if constexpr (PATH == kPMX8E) {
+            sa = e8m0_scale((scA[mb][0] >> (8 * ks)) & 0xffu);
+            sb = e8m0_scale((scB[mb][0] >> (8 * ks)) & 0xffu);
+          }
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
-            da[e][mb] = u32x4{fp8x2_to_bf16x2<AT, false>(fa[cur][mb][2 * e]), fp8x2_to_bf16x2<AT, true>(fa[cur][mb][2 * e]),
-                              fp8x2_to_bf16x2<AT, false>(fa[cur][mb][2 * e + 1]), fp8x2_to_bf16x2<AT, true>(fa[cur][mb][2 * e + 1])};
-            db[e][mb] = u32x4{fp8x2_to_bf16x2<BT, false>(fb[cur][mb][2 * e]), fp8x2_to_bf16x2<BT, true>(fb[cur][mb][2 * e]),
-                              fp8x2_to_bf16x2<BT, false>(fb[cur][mb][2 * e + 1]), fp8x2_to_bf16x2<BT, true>(fb[cur][mb][2 * e + 1])};
+            da[e][mb] = u32x4{fp8x2_to_bf16x2<AT, false>(fa[cur][mb][2 * e], sa), fp8x2_to_bf16x2<AT, true>(fa[cur][mb][2 * e], sa),
+                              fp8x2_to_bf16x2<AT, false>(fa[cur][mb][2 * e + 1], sa), fp8x2_to_bf16x2<AT, true>(fa[cur][mb][2 * e + 1], sa)};
+            db[e][mb] = u32x4{fp8x2_to_bf16x2<BT, false>(fb[cur][mb][2 * e], sb), fp8x2_to_bf16x2<BT, true>(fb[cur][mb][2 * e], sb),
+                              fp8x2_to_bf16x2<BT, false>(fb[cur][mb][2 * e + 1], sb), fp8x2_to_bf16x2<BT, true>(fb[cur][mb][2 * e + 1], sb)};
           }
         }
 #pragma unroll
@@ -915,7 +931,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
       // 16 MFMA per slice with the next slice's fragment reads spread evenly
       // (8 reads; 16 for FP8; two per transposed fragment)
       constexpr int kReads = PATH == kPF8Native || PATH == kPMX8 ? 16 : (A_KC ? 4 : 8) + (B_KC ? 4 : 8);
-      if constexpr (PATH != kPF8Exact && PATH != kPFP4D) {
+      if constexpr (PATH != kPF8Exact && PATH != kPFP4D && PATH != kPMX8E) {
         if (kSplit && ks < 2) sched_slice<0, kReads, 8>();
         else if (!kSplit && A_KC && B_KC && ks == 0) sched_slice<0, kReads, 16>();
         else if (kMid && ks + 1 == NS) sched_half<0, kReads>();
@@ -942,9 +958,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
       }
     }
   };
-  if constexpr (PATH == kPF8Exact || PATH == kPFP4D) {
+  if constexpr (PATH == kPF8Exact || PATH == kPFP4D || PATH == kPMX8E) {
     // long step bodies without scheduling hints: one step per iteration,
-    // stages chosen at run time (measured faster for these two)
+    // stages chosen at run time (measured faster for the first two)
     for (int64_t kt = 0; kt < nk; ++kt)
       step(kt, (kt & 1) ? smem1[0] : smem0[0], (kt & 1) ? smem0[0] : smem1[0]);
   } else {
@@ -1365,12 +1381,22 @@ hipError_t launch_mx_t(const GemmArgs& g, int ct, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_mx(const GemmArgs& g, int at, int bt, int ct, hipStream_t s) {
+// FP8 elements: widened exactly to BF16 times the block scale by default;
+// `native` takes the block-scaled FP8 instruction (its reduced-precision
+// internal sums).  E2M1 elements: the block-scaled instruction (exact enough:
+// few product bits).
+template <int PATH>
+hipError_t launch_mx8(const GemmArgs& g, int at, int bt, int ct, hipStream_t s) {
+  if (at == AMP_E4M3 && bt == AMP_E4M3) return launch_mx_t<AMP_E4M3, AMP_E4M3, PATH>(g, ct, s);
+  if (at == AMP_E4M3) return launch_mx_t<AMP_E4M3, AMP_E5M2, PATH>(g, ct, s);
+  if (bt == AMP_E4M3) return launch_mx_t<AMP_E5M2, AMP_E4M3, PATH>(g, ct, s);
+  return launch_mx_t<AMP_E5M2, AMP_E5M2, PATH>(g, ct, s);
+}
+
+hipError_t launch_mx(const GemmArgs& g, int at, int bt, int ct, bool native, hipStream_t s) {
   if (at == AMP_E2M1X2) return launch_mx_t<AMP_E2M1X2, AMP_E2M1X2, kPMX4>(g, ct, s);
-  if (at == AMP_E4M3 && bt == AMP_E4M3) return launch_mx_t<AMP_E4M3, AMP_E4M3, kPMX8>(g, ct, s);
-  if (at == AMP_E4M3) return launch_mx_t<AMP_E4M3, AMP_E5M2, kPMX8>(g, ct, s);
-  if (bt == AMP_E4M3) return launch_mx_t<AMP_E5M2, AMP_E4M3, kPMX8>(g, ct, s);
-  return launch_mx_t<AMP_E5M2, AMP_E5M2, kPMX8>(g, ct, s);
+  if (native) return launch_mx8<kPMX8>(g, at, bt, ct, s);
+  return launch_mx8<kPMX8E>(g, at, bt, ct, s);
 }
 
 }  // namespace
@@ -1398,7 +1424,7 @@ hipError_t launch_gemm(int opA, int opB, int64_t M, int64_t N, int64_t K, const 
     }
     return hipGetLastError();
   }
-  if (mx) return launch_mx(g, at, bt, ct, s);
+  if (mx) return launch_mx(g, at, bt, ct, fp8_native, s);
   const bool a_kc = opA == AMP_OP_N, b_kc = opB == AMP_OP_T;
   if (at == AMP_E2M1X2) {
     const bool fast = aligned(A, 16) && aligned(B, 16) && lda % 16 == 0 && ldb % 16 == 0 &&

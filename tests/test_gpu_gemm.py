@@ -220,3 +220,52 @@ def test_gemm_fp8_exact_interior(fa, fb):
     alpha = float(np.float32(np.float32(ia) * np.float32(ib)))
     cref, bound = OG.reference(A, B, alpha=alpha)
     check(out, amp.F32, cref, bound, "fp8 exact interior")
+
+
+# lanes hold rows (A) / columns (B) l % D; P bytes per lane; R outputs per lane
+PROBE = {0: (32, 8, 16, "32x32x16 FP8"), 1: (16, 8, 4, "16x16x32 FP8"),
+         2: (32, 32, 16, "block-scaled 32x32x64 f8f6f4"),
+         3: (16, 32, 4, "block-scaled 16x16x128 f8f6f4")}
+
+
+def _probe_codes(seed, n, fmt, kind):
+    if kind == "all-codes":
+        c = synth.rng(seed).integers(0, 256, size=n, dtype=np.uint8)
+        return np.where(np.isfinite(F.decode(c, fmt)), c, 0x38).astype(np.uint8)
+    x = synth.student_t_f32(seed, n, scale=1.0)
+    return OC.cast(synth.f32_bits(x), F.F32, fmt, float(fmt.max_finite) / float(np.abs(x).max()))[0]
+
+
+@pytest.mark.parametrize("at", [amp.E4M3, amp.E5M2])
+@pytest.mark.parametrize("shape", [0, 1, 2, 3])
+def test_fp8_instruction_precision_report(shape, at):
+    """Each FP8 matrix-core instruction of gfx950 on random operands (every
+    finite code; Student-t activations scaled to the format's range) against
+    the exact sums: report the largest |err| / sum|ab| and the share of
+    outputs within 1e-5 * sum|ab|; assert the documented reduced-precision
+    bound (2^-10) and that the lane layout is the documented one (no gross
+    errors)."""
+    D, P, R, name = PROBE[shape]
+    G, tiles = 64 // D, 1024
+    lanes, r = np.arange(64), np.arange(R)
+    if D == 32:
+        row = 8 * (r // 4)[None, :] + 4 * (lanes // 32)[:, None] + (r % 4)[None, :]
+    else:
+        row = 4 * (lanes // 16)[:, None] + r[None, :]
+    col = np.broadcast_to((lanes % D)[:, None], row.shape)
+    for kind in ("all-codes", "activations"):
+        a = _probe_codes(100 + shape, tiles * 64 * P, FMT[at], kind)
+        b = _probe_codes(200 + shape, tiles * 64 * P, F.E4M3, kind)
+        c = empty(tiles * 64 * R * 4)
+        amp.amp_fp8_mfma_probe(shape, at, dev(a), dev(b), c, tiles)
+        got = host(c, np.float32).reshape(tiles, 64, R).astype(np.float64)
+        # byte j of lane q*D + i meets byte j of lane q*D + n: K index (q, j)
+        Av = F.decode(a, FMT[at]).reshape(tiles, G, D, P).transpose(0, 2, 1, 3).reshape(tiles, D, G * P)
+        Bv = F.decode(b, F.E4M3).reshape(tiles, G, D, P).transpose(0, 2, 1, 3).reshape(tiles, D, G * P)
+        cref, bound = OG.reference(Av, Bv.transpose(0, 2, 1))
+        want, bd = cref[:, row, col], bound[:, row, col]
+        rel = np.abs(got - want) / np.maximum(bd, 1e-300)
+        within = float(np.mean(rel <= OG.RTOL))
+        print(f"{name} {'E5M2' if at == amp.E5M2 else 'E4M3'}xE4M3 {kind}: "
+              f"max |err|/sum|ab| = {rel.max():.3g}, within 1e-5: {within:.4f}")
+        assert rel.max() <= 2.0 ** -10, (name, kind)

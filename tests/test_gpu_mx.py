@@ -1,6 +1,8 @@
 """MX block formats on the GPU: amp_mx_quantize bit-exact against oracle/mx.py
-and the MX GEMM on CDNA4's block-scaled matrix cores against the float64
-product of the dequantized operands."""
+and the MX GEMM (E2M1 on CDNA4's block-scaled matrix cores, FP8 elements
+widened exactly to BF16 times their block scale, or on the block-scaled FP8
+instruction on request) against the float64 product of the dequantized
+operands."""
 import numpy as np
 import pytest
 
@@ -65,16 +67,24 @@ def mx_operand(seed, rows, k, yt):
     return q, codes.astype(np.uint8), sc
 
 
-def run_mx_gemm(M, N, K, at, bt, ct=amp.F32, seed=0):
+def run_mx_gemm(M, N, K, at, bt, ct=amp.F32, seed=0, native=False, scales=None, edit=None):
     qa, ca, sa = mx_operand(seed + 1, M, K, at)
     qb, cb, sb = mx_operand(seed + 2, N, K, bt)
+    if scales is not None:                  # ((A lo, A hi), (B lo, B hi)) inclusive code ranges
+        g = synth.rng(seed + 3)
+        (alo, ahi), (blo, bhi) = scales
+        sa = g.integers(alo, ahi + 1, size=sa.shape, dtype=np.uint8)
+        sb = g.integers(blo, bhi + 1, size=sb.shape, dtype=np.uint8)
+    if edit is not None:
+        edit(sa, sb)
     lda = K // 2 if at == amp.E2M1X2 else K
     ldb = K // 2 if bt == amp.E2M1X2 else K
     c = empty(M * N * 4)
     sa_d, sb_d = dev(sa), dev(sb)
     amp.amp_gemm_ex(amp.OP_N, amp.OP_T, M, N, K, dev(qa), at, lda, None, dev(qb), bt, ldb, None,
                     c, ct, N, amp.BlockScales(sa_d.data_ptr(), K // 32, 0, 0),
-                    amp.BlockScales(sb_d.data_ptr(), K // 32, 0, 0), flags=amp.GEMM_MX)
+                    amp.BlockScales(sb_d.data_ptr(), K // 32, 0, 0),
+                    flags=amp.GEMM_MX | (amp.GEMM_FP8_NATIVE if native else 0))
     A = OM.dequantize(ca, sa, YF[at])
     B = OM.dequantize(cb, sb, YF[bt])
     cref, bound = OG.reference(A, B.T)
@@ -93,12 +103,55 @@ def test_mxfp4_gemm_within_fp32_accumulation_bound(M, N, K):
 
 
 @pytest.mark.parametrize("K", [1024, 384])          # an even and an odd number of K-steps
-@pytest.mark.parametrize("at,bt", [(amp.E4M3, amp.E4M3), (amp.E5M2, amp.E4M3)])
-def test_mxfp8_gemm_precision_report(at, bt, K):
-    """FP8 elements on the block-scaled matrix cores: the 64-term sums have the
-    reduced internal precision of the FP8 instruction (documented); assert
-    the measured bound and report how many outputs meet 1e-5 * sum|ab|."""
+@pytest.mark.parametrize("at,bt", [(amp.E4M3, amp.E4M3), (amp.E5M2, amp.E4M3),
+                                   (amp.E4M3, amp.E5M2), (amp.E5M2, amp.E5M2)])
+def test_mxfp8_gemm_within_fp32_accumulation_bound(at, bt, K):
+    """FP8 elements widened to BF16 times their block scale (exact) on the
+    BF16 matrix cores: every output within 1e-5 * sum|ab|."""
     out, cref, bound = run_mx_gemm(512, 512, K, at, bt, seed=5)
+    ok = OG.check_f32(out, cref, bound)
+    assert ok.all(), (np.argwhere(~ok)[:5], np.max(np.abs(out - cref) / np.maximum(bound, 1e-300)))
+
+
+@pytest.mark.parametrize("at,bt,scales", [
+    (amp.E4M3, amp.E4M3, ((3, 40), (210, 246))),       # E4M3 exact range: codes 3..246
+    (amp.E5M2, amp.E4M3, ((200, 239), (15, 54))),      # E5M2 exact range: codes 10..239
+    (amp.E5M2, amp.E5M2, ((10, 50), (200, 239)))])
+def test_mxfp8_gemm_extreme_block_scales(at, bt, scales):
+    """Block scales at both ends of the widened route's exact range (every
+    scaled element still a BF16 value), paired so that the products stay in
+    FP32's range: within the FP32-accumulation bound."""
+    out, cref, bound = run_mx_gemm(256, 256, 256, at, bt, seed=11, scales=scales)
+    ok = OG.check_f32(out, cref, bound)
+    fin = (bound < 2.0 ** 120) & (bound > 2.0 ** -100)
+    assert fin.mean() > 0.99
+    assert ok[fin].all(), (np.argwhere(~ok & fin)[:5])
+
+
+def test_mxfp8_gemm_nan_block_scale():
+    """A UE8M0 scale of 0xFF makes its block NaN, and every output that block
+    reaches NaN; the others are unaffected."""
+    def edit(sa, sb):
+        sa[3, 1] = 0xFF          # row 3 of A, K block 1
+        sb[7, 0] = 0xFF          # column 7 of B, K block 0
+    out, cref, bound = run_mx_gemm(256, 256, 256, amp.E4M3, amp.E4M3, seed=13, edit=edit)
+    nan = np.isnan(out)
+    assert nan[3, :].all() and nan[:, 7].all()
+    keep = np.ones_like(nan)
+    keep[3, :] = False
+    keep[:, 7] = False
+    assert not nan[keep].any()
+    assert OG.check_f32(out[keep], cref[keep], bound[keep]).all()
+
+
+@pytest.mark.parametrize("K", [1024, 384])
+@pytest.mark.parametrize("at,bt", [(amp.E4M3, amp.E4M3), (amp.E5M2, amp.E4M3)])
+def test_mxfp8_native_instruction_precision_report(at, bt, K):
+    """FP8 elements on the block-scaled FP8 matrix cores (AMP_GEMM_FP8_NATIVE):
+    the 64-term sums have the reduced internal precision of the FP8
+    instruction (documented); assert the measured bound and report how many
+    outputs meet 1e-5 * sum|ab|."""
+    out, cref, bound = run_mx_gemm(512, 512, K, at, bt, seed=5, native=True)
     rel = np.abs(out - cref) / np.maximum(bound, 1e-300)
     frac = float(np.mean(rel <= OG.RTOL))
     print(f"MXFP8 {at}x{bt}: max |err|/sum|ab| = {rel.max():.3g}, within 1e-5: {frac:.4f}")

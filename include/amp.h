@@ -492,9 +492,10 @@ int amp_optimizer_step_ex(float* master, float* m, float* v, const void* grads, 
 /* amp_stream_copy -- a plain device copy dst[0..bytes) = src[0..bytes), the
  * reference for the HBM roofline of the element-wise kernels (not a step of
  * the training path).  The optimizer pass reads as many bytes as it writes, so
- * the rate of a copy with the same access shape (16-byte loads and stores,
- * several in flight per thread, 64 work-groups per CU) is its practical
- * ceiling on a given part.  src and dst: device memory, 16-byte aligned, not
+ * the rate of a plain copy (16-byte non-temporal loads and stores, four in
+ * flight per thread, one contiguous 256 KiB range per work-group: the fastest
+ * copy form measured on this part) is its practical ceiling on a given part.
+ * src and dst: device memory, 16-byte aligned, not
  * overlapping; bytes == 0 is a no-op; misaligned or NULL pointers give
  * AMP_EINVAL. */
 int amp_stream_copy(const void* src, void* dst, int64_t bytes, void* stream);

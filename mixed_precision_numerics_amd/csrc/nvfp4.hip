@@ -489,17 +489,19 @@ hipError_t run_vec(const void* x, int64_t ldx, int64_t R, int64_t K, uint64_t rs
   using Gm = VecGeom<XT, TRANS>;
   const int64_t tiles_r = (R + Gm::kTileR - 1) / Gm::kTileR;
   const int64_t tiles_k = (K + Gm::kTileK - 1) / Gm::kTileK;
-  const int64_t waves = tiles_r * tiles_k;
-  int64_t blocks = (waves + kT / kWave - 1) / (kT / kWave);
-  if (blocks > 2048) blocks = 2048;
+  const int64_t ntiles = tiles_r * tiles_k;
+  auto* amax_pass = nvfp4_vec_kernel<XT, TRANS, false, BLOCK2D, RHT, SR>;
+  auto* encode_pass = nvfp4_vec_kernel<XT, TRANS, true, BLOCK2D, RHT, SR>;
+  // one wave per tile up to 2^16 waves (a longer loop per wave beyond that)
+  int64_t blocks = (ntiles + kT / kWave - 1) / (kT / kWave);
+  if (blocks > 16384) blocks = 16384;
+  const int64_t b1 = blocks, b2 = blocks;
   const uint8_t* xb = static_cast<const uint8_t*>(x);
   const int64_t ldb = ldx * Gm::kESize;
   zero_amax<<<1, 64, 0, s>>>(dt);
-  nvfp4_vec_kernel<XT, TRANS, false, BLOCK2D, RHT, SR><<<static_cast<unsigned>(blocks), kT, 0, s>>>(
-      xb, ldb, R, K, tiles_r, tiles_k, rs, ss, q, sc, dt);
+  amax_pass<<<static_cast<unsigned>(b1), kT, 0, s>>>(xb, ldb, R, K, tiles_r, tiles_k, rs, ss, q, sc, dt);
   finalize_enc<<<1, 64, 0, s>>>(dt);
-  nvfp4_vec_kernel<XT, TRANS, true, BLOCK2D, RHT, SR><<<static_cast<unsigned>(blocks), kT, 0, s>>>(
-      xb, ldb, R, K, tiles_r, tiles_k, rs, ss, q, sc, dt);
+  encode_pass<<<static_cast<unsigned>(b2), kT, 0, s>>>(xb, ldb, R, K, tiles_r, tiles_k, rs, ss, q, sc, dt);
   return hipGetLastError();
 }
 

@@ -135,9 +135,49 @@ __device__ __forceinline__ void adam_elem(const StepScalars& k, float g16, float
   th = th * k.decay - k.step * (m / d);
 }
 
-// Vector path: 8 elements per thread per iteration, 16-byte accesses.
-// (Measured on MI355X: plain loads/stores beat the non-temporal hints for
-// this 50/50 read/write stream.)
+// Vector path.  Each work-group owns a contiguous range of kApplyChunk
+// 8-parameter vectors (16-byte gradient words) and each thread keeps two
+// vectors' loads in flight before its first store; the once-read gradients
+// and the write-only 16-bit copy use non-temporal accesses, the state plain
+// ones.  (Measured on MI355X against the grid-stride form with one vector per
+// iteration: 5.26 vs 4.91 TB/s on the same 28 B/param stream.)
+constexpr int64_t kApplyChunk = 512;
+
+template <int GT>
+__device__ __forceinline__ void load_g8(const void* __restrict__ g_p, int64_t j, float (&gg)[8]) {
+  if constexpr (GT == AMP_F32) {
+    const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g_p) + 2 * j);
+    const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g_p) + 2 * j + 1);
+    gg[0] = a.x; gg[1] = a.y; gg[2] = a.z; gg[3] = a.w;
+    gg[4] = b.x; gg[5] = b.y; gg[6] = b.z; gg[7] = b.w;
+  } else {
+    const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(g_p) + j);
+    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (GT == AMP_BF16) {
+        gg[2 * q] = bitsf(ww[q] << 16);
+        gg[2 * q + 1] = bitsf(ww[q] & 0xffff0000u);
+      } else {
+        gg[2 * q] = f16_to_f32(ww[q] & 0xffffu);
+        gg[2 * q + 1] = f16_to_f32(ww[q] >> 16);
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void load_f8(const float* __restrict__ p, int64_t j, float (&x)[8]) {
+  const f32x4 a = reinterpret_cast<const f32x4*>(p)[2 * j];
+  const f32x4 b = reinterpret_cast<const f32x4*>(p)[2 * j + 1];
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+__device__ __forceinline__ void store_f8(float* __restrict__ p, int64_t j, const float (&x)[8]) {
+  reinterpret_cast<f32x4*>(p)[2 * j] = f32x4{x[0], x[1], x[2], x[3]};
+  reinterpret_cast<f32x4*>(p)[2 * j + 1] = f32x4{x[4], x[5], x[6], x[7]};
+}
+
 template <int GT, int WT, bool HAS_W, bool MULT>
 __global__ __launch_bounds__(kThreads) void apply_kernel(float* __restrict__ th_p,
                                                          float* __restrict__ m_p,
@@ -151,61 +191,53 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(float* __restrict__ th_
   if (st.found_inf) return;
   StepScalars k = make_scalars(st, hp);
   if constexpr (MULT) k.mult = *mult_p;
-  const int64_t tid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  const int64_t nthr = static_cast<int64_t>(gridDim.x) * kThreads;
   const int64_t nv = n / 8;
-  f32x4* th4 = reinterpret_cast<f32x4*>(th_p);
-  f32x4* m4 = reinterpret_cast<f32x4*>(m_p);
-  f32x4* v4 = reinterpret_cast<f32x4*>(v_p);
-  for (int64_t j = tid; j < nv; j += nthr) {
-    float gg[8];
-    if constexpr (GT == AMP_F32) {
-      const f32x4 a = reinterpret_cast<const f32x4*>(g_p)[2 * j];
-      const f32x4 b = reinterpret_cast<const f32x4*>(g_p)[2 * j + 1];
-      gg[0] = a.x; gg[1] = a.y; gg[2] = a.z; gg[3] = a.w;
-      gg[4] = b.x; gg[5] = b.y; gg[6] = b.z; gg[7] = b.w;
-    } else {
-      const u32x4 w = reinterpret_cast<const u32x4*>(g_p)[j];
-      const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        if constexpr (GT == AMP_BF16) {
-          gg[2 * q] = bitsf(ww[q] << 16);
-          gg[2 * q + 1] = bitsf(ww[q] & 0xffff0000u);
-        } else {
-          gg[2 * q] = f16_to_f32(ww[q] & 0xffffu);
-          gg[2 * q + 1] = f16_to_f32(ww[q] >> 16);
-        }
-      }
-    }
-    const f32x4 t0 = th4[2 * j], t1 = th4[2 * j + 1];
-    const f32x4 m0 = m4[2 * j], m1 = m4[2 * j + 1];
-    const f32x4 v0 = v4[2 * j], v1 = v4[2 * j + 1];
-    float th[8] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z, t1.w};
-    float mm[8] = {m0.x, m0.y, m0.z, m0.w, m1.x, m1.y, m1.z, m1.w};
-    float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+  const int64_t b0 = static_cast<int64_t>(blockIdx.x) * kApplyChunk;
+  const int64_t b1 = b0 + kApplyChunk < nv ? b0 + kApplyChunk : nv;
+  auto update = [&](int64_t j, float (&gg)[8], float (&th)[8], float (&mm)[8], float (&vv)[8]) {
 #pragma unroll
     for (int q = 0; q < 8; ++q) adam_elem<MULT>(k, gg[q], th[q], mm[q], vv[q]);
-    th4[2 * j] = f32x4{th[0], th[1], th[2], th[3]};
-    th4[2 * j + 1] = f32x4{th[4], th[5], th[6], th[7]};
-    m4[2 * j] = f32x4{mm[0], mm[1], mm[2], mm[3]};
-    m4[2 * j + 1] = f32x4{mm[4], mm[5], mm[6], mm[7]};
-    v4[2 * j] = f32x4{vv[0], vv[1], vv[2], vv[3]};
-    v4[2 * j + 1] = f32x4{vv[4], vv[5], vv[6], vv[7]};
+    store_f8(th_p, j, th);
+    store_f8(m_p, j, mm);
+    store_f8(v_p, j, vv);
     if constexpr (HAS_W) {
       u32x4 w;
       w.x = w16_code<WT>(th[0]) | (w16_code<WT>(th[1]) << 16);
       w.y = w16_code<WT>(th[2]) | (w16_code<WT>(th[3]) << 16);
       w.z = w16_code<WT>(th[4]) | (w16_code<WT>(th[5]) << 16);
       w.w = w16_code<WT>(th[6]) | (w16_code<WT>(th[7]) << 16);
-      reinterpret_cast<u32x4*>(w_p)[j] = w;
+      __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(w_p) + j);
     }
+  };
+  int64_t j = b0 + threadIdx.x;
+  for (; j + kThreads < b1; j += 2 * kThreads) {
+    float gg[2][8], th[2][8], mm[2][8], vv[2][8];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      load_g8<GT>(g_p, j + u * kThreads, gg[u]);
+      load_f8(th_p, j + u * kThreads, th[u]);
+      load_f8(m_p, j + u * kThreads, mm[u]);
+      load_f8(v_p, j + u * kThreads, vv[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) update(j + u * kThreads, gg[u], th[u], mm[u], vv[u]);
   }
-  for (int64_t i = nv * 8 + tid; i < n; i += nthr) {
-    float th = th_p[i], m = m_p[i], v = v_p[i];
-    adam_elem<MULT>(k, grad_at<GT>(g_p, i), th, m, v);
-    th_p[i] = th; m_p[i] = m; v_p[i] = v;
-    if constexpr (HAS_W) static_cast<uint16_t*>(w_p)[i] = static_cast<uint16_t>(w16_code<WT>(th));
+  for (; j < b1; j += kThreads) {
+    float gg[8], th[8], mm[8], vv[8];
+    load_g8<GT>(g_p, j, gg);
+    load_f8(th_p, j, th);
+    load_f8(m_p, j, mm);
+    load_f8(v_p, j, vv);
+    update(j, gg, th, mm, vv);
+  }
+  // the elements past the last whole vector belong to the last work-group
+  if (blockIdx.x + 1 == gridDim.x) {
+    for (int64_t i = nv * 8 + threadIdx.x; i < n; i += kThreads) {
+      float th = th_p[i], m = m_p[i], v = v_p[i];
+      adam_elem<MULT>(k, grad_at<GT>(g_p, i), th, m, v);
+      th_p[i] = th; m_p[i] = m; v_p[i] = v;
+      if constexpr (HAS_W) static_cast<uint16_t*>(w_p)[i] = static_cast<uint16_t>(w16_code<WT>(th));
+    }
   }
 }
 
@@ -481,6 +513,12 @@ int64_t grid_for(int64_t work_items) {
   return b < 1 ? 1 : b;
 }
 
+// One work-group per kApplyChunk vectors (at least one, for the tail).
+int64_t apply_blocks(int64_t n) {
+  const int64_t b = (n / 8 + kApplyChunk - 1) / kApplyChunk;
+  return b < 1 ? 1 : b;
+}
+
 template <int GT, int WT, bool HAS_W, bool MULT>
 hipError_t launch_apply_t(float* th, float* m, float* v, const void* g, void* w, int64_t n,
                           const amp_adamw_hparams& hp, amp_scaler_state* st, const float* mult,
@@ -488,7 +526,7 @@ hipError_t launch_apply_t(float* th, float* m, float* v, const void* g, void* w,
   const bool vec = aligned(th, 16) && aligned(m, 16) && aligned(v, 16) && aligned(g, 16) &&
                    (!HAS_W || aligned(w, 16));
   if (vec)
-    apply_kernel<GT, WT, HAS_W, MULT><<<dim3(static_cast<unsigned>(grid_for(n / 8))), kThreads, 0, s>>>(
+    apply_kernel<GT, WT, HAS_W, MULT><<<dim3(static_cast<unsigned>(apply_blocks(n))), kThreads, 0, s>>>(
         th, m, v, g, w, n, hp, st, mult);
   else
     apply_kernel_scalar<GT, WT, HAS_W, MULT><<<dim3(static_cast<unsigned>(grid_for(n))), kThreads, 0, s>>>(

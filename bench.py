@@ -32,7 +32,7 @@ Also measured in the same run (reported under "components"):
 The CPU oracle is timed on a bounded sample of the optimizer workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-components]
-                       [--no-cpu-baseline] [--calibrate-copy]
+                       [--components name,name,...] [--no-cpu-baseline] [--calibrate-copy]
 """
 from __future__ import annotations
 
@@ -706,6 +706,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-components", action="store_true")
+    ap.add_argument("--components", default="all",
+                    help="comma-separated component names to run (default all; 'none' = none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
@@ -737,27 +739,28 @@ def main():
         "what": "an overflowing step (one +inf gradient): check sweep sets the flag, the AdamW "
                 "pass writes nothing, S halves; median of 20",
         "ms": round(skip_ms, 4)}}
-    if not args.no_components:
-        log("components: BF16 block GEMMs")
-        comps["gemm_bf16_block"] = gemm_block_workload(torch, amp, fp8=False)
-        log("components: FP8 delayed-scaling block")
-        comps["gemm_fp8_block"] = gemm_block_workload(torch, amp, fp8=True)
-        log("components: FP8 block on the native FP8 instruction")
-        comps["gemm_fp8_native_block"] = gemm_block_workload(torch, amp, fp8=True, native=True)
-        log("components: cast")
-        comps["cast"] = cast_workload(torch, amp)
-        log("components: cast with transposed copy")
-        comps["cast_t"] = cast_t_workload(torch, amp)
-        log("components: NVFP4 weight-gradient quantize + GEMM")
-        comps["nvfp4_wgrad"] = nvfp4_workload(torch, amp)
-        log("components: MX GEMMs (block-scaled matrix cores)")
-        comps["mx"] = mx_workload(torch, amp)
-        log("components: fine-grained FP8 (1x128 / 128x128 scales) FFN up projection")
-        comps["blockwise_fp8"] = blockwise_workload(torch, amp)
-        log("components: delayed vs current scaling casts")
-        comps["scaling"] = scaling_workload(torch, amp)
-        log("components: gradient norm and accumulation")
-        comps["clip"] = clip_workload(torch, amp)
+    table = (
+        ("gemm_bf16_block", "BF16 block GEMMs", lambda: gemm_block_workload(torch, amp, fp8=False)),
+        ("gemm_fp8_block", "FP8 delayed-scaling block", lambda: gemm_block_workload(torch, amp, fp8=True)),
+        ("gemm_fp8_native_block", "FP8 block on the native FP8 instruction",
+         lambda: gemm_block_workload(torch, amp, fp8=True, native=True)),
+        ("cast", "cast", lambda: cast_workload(torch, amp)),
+        ("cast_t", "cast with transposed copy", lambda: cast_t_workload(torch, amp)),
+        ("nvfp4_wgrad", "NVFP4 weight-gradient quantize + GEMM", lambda: nvfp4_workload(torch, amp)),
+        ("mx", "MX GEMMs", lambda: mx_workload(torch, amp)),
+        ("blockwise_fp8", "fine-grained FP8 (1x128 / 128x128 scales) FFN up projection",
+         lambda: blockwise_workload(torch, amp)),
+        ("scaling", "delayed vs current scaling casts", lambda: scaling_workload(torch, amp)),
+        ("clip", "gradient norm and accumulation", lambda: clip_workload(torch, amp)))
+    wanted = set() if (args.no_components or args.components == "none") else (
+        {n for n, _, _ in table} if args.components == "all" else set(args.components.split(",")))
+    unknown = wanted - {n for n, _, _ in table}
+    if unknown:
+        raise SystemExit(f"bench.py: unknown components {sorted(unknown)}")
+    for name, what, fn in table:
+        if name in wanted:
+            log(f"components: {what}")
+            comps[name] = fn()
     traffic = measured_traffic()
 
     out = {

@@ -229,7 +229,11 @@ int amp_gemm_ex(int opA, int opB, int64_t M, int64_t N, int64_t K,
                 int flags, void* stream);
 
 /* amp_scaler_init -- sets scale = init_scale, growth_tracker = found_inf = 0,
- * adam_step = 0, beta pows = 1 (GradScaler(init_scale) + fresh AdamW). */
+ * adam_step = 0, beta pows = 1 (GradScaler(init_scale) + fresh AdamW).
+ * Source: itwiki "손실 스케일링" (dynamic loss scaling starts from a large
+ * scale, 65536 with GradScaler's defaults) and "FP16 학습 루프" (the loop builds
+ * GradScaler() and AdamW before training); marovi "Escalado dinámico de
+ * pérdida". */
 int amp_scaler_init(amp_scaler_state* d_state, float init_scale, void* stream);
 
 /* amp_optimizer_step -- unscale by 1/S, check every gradient for inf/NaN,
@@ -257,7 +261,10 @@ int amp_optimizer_step(float* master, float* m, float* v, const void* grads, int
 
 /* amp_check_overflow -- OR (any non-finite element of x) into
  * d_state->found_inf.  x: [n] of xt in {F16, BF16, F32}.  Used when several
- * gradient buffers feed one optimizer step (then step with SKIP_CHECK). */
+ * gradient buffers feed one optimizer step (then step with SKIP_CHECK).
+ * Source: itwiki "손실 스케일링" (after unscaling, a step whose gradients hold
+ * inf or NaN is skipped and the scale lowered); marovi "Escalado dinámico de
+ * pérdida". */
 int amp_check_overflow(const void* x, int xt, int64_t n, amp_scaler_state* d_state,
                        void* stream);
 
@@ -276,7 +283,11 @@ int amp_found_inf_from_amax(const float* d_amax, int32_t n, int yt, const float*
 
 /* amp_scaler_update -- on found_inf: scale *= backoff, tracker = 0; else
  * tracker += 1 and at growth_interval: scale *= growth, tracker = 0.  Then
- * found_inf = 0.  No floor on the scale.  p == NULL uses (2, 0.5, 2000). */
+ * found_inf = 0.  No floor on the scale.  p == NULL uses (2, 0.5, 2000).
+ * Source: itwiki "손실 스케일링" (halve on overflow, double after a run of
+ * clean steps: GradScaler's update()); marovi "Escalado dinámico de pérdida"
+ * and "Limitaciones y modos de fallo" (a collapsing scale is a symptom, not
+ * clamped). */
 int amp_scaler_update(amp_scaler_state* d_state, const amp_scaler_params* p, void* stream);
 
 /* amp_cast_current_scaling -- current (just-in-time) scaling: one pass finds
@@ -291,7 +302,10 @@ int amp_cast_current_scaling(const void* x, int xt, int64_t rows, int64_t cols, 
                              const amp_delayed_recipe* r, amp_fp8_meta* d_meta, void* stream);
 
 /* amp_fp8_meta_init -- n metas: amax_cur 0, scale = scale_inv = 1, pos 0,
- * and d_history[n * history_len] zero-filled. */
+ * and d_history[n * history_len] zero-filled.
+ * Source: hwlabs "Delayed Scaling 동작 원리" (each FP8 tensor keeps an amax
+ * history from which its scale is derived; before any history the scale is
+ * the neutral 1). */
 int amp_fp8_meta_init(amp_fp8_meta* d_metas, float* d_history, int32_t n,
                       int32_t history_len, void* stream);
 

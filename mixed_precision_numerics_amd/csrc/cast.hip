@@ -10,8 +10,9 @@
 //   y = round(fl32(x * scale)),  amax = max(amax, max|x|)  (bit-pattern max)
 //
 // Two kernels, both HBM-bound:
-//  * cast_flat: contiguous tensors, 8 elements per thread per iteration with
-//    16-byte loads, grid-stride, one atomic max per block.
+//  * cast_flat: contiguous tensors; each block converts contiguous ranges of
+//    2048 8-element vectors with non-temporal 16-byte loads, four in flight
+//    per thread, and one atomic max per block.
 //  * cast_tile: strided tensors and the optional transposed copy (the FP8
 //    dgrad / wgrad operands).  A 256-thread block owns a 128x128 tile; each
 //    thread converts an 8x8 sub-block, writes its row-major codes directly and
@@ -30,16 +31,20 @@ __device__ __forceinline__ float load_one(const void* p, int64_t i) {
   else return f16_to_f32(static_cast<const uint16_t*>(p)[i]);
 }
 
-// Load 8 consecutive elements (16-byte aligned).
-template <int XT>
+// Load 8 consecutive elements (16-byte aligned); NT marks the loads
+// non-temporal (data read once by a streaming pass).
+template <int XT, bool NT = false>
 __device__ __forceinline__ void load8(const void* p, int64_t i, float (&v)[8]) {
   if constexpr (XT == AMP_F32) {
-    const float4* q = reinterpret_cast<const float4*>(static_cast<const float*>(p) + i);
-    const float4 a = q[0], b = q[1];
+    const f32x4* q = reinterpret_cast<const f32x4*>(static_cast<const float*>(p) + i);
+    f32x4 a, b;
+    if constexpr (NT) { a = __builtin_nontemporal_load(q); b = __builtin_nontemporal_load(q + 1); }
+    else { a = q[0]; b = q[1]; }
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
   } else {
-    const uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(p) + i);
+    const u32x4* q = reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(p) + i);
+    const u32x4 w = NT ? __builtin_nontemporal_load(q) : *q;
     const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -67,19 +72,23 @@ struct CodeT { using type = uint16_t; };
 template <> struct CodeT<AMP_E4M3> { using type = uint8_t; };
 template <> struct CodeT<AMP_E5M2> { using type = uint8_t; };
 
-// Store 8 codes at y + i (8- or 16-byte aligned).
-template <int YT>
+// Store 8 codes at y + i (8- or 16-byte aligned); NT as for load8.
+template <int YT, bool NT = false>
 __device__ __forceinline__ void store8(void* y, int64_t i, const uint32_t (&c)[8]) {
   if constexpr (sizeof(typename CodeT<YT>::type) == 1) {
-    uint2 w;
+    u32x2 w;
     w.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
     w.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-    *reinterpret_cast<uint2*>(static_cast<uint8_t*>(y) + i) = w;
+    u32x2* q = reinterpret_cast<u32x2*>(static_cast<uint8_t*>(y) + i);
+    if constexpr (NT) __builtin_nontemporal_store(w, q);
+    else *q = w;
   } else {
-    uint4 w;
+    u32x4 w;
     w.x = c[0] | (c[1] << 16); w.y = c[2] | (c[3] << 16);
     w.z = c[4] | (c[5] << 16); w.w = c[6] | (c[7] << 16);
-    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(y) + i) = w;
+    u32x4* q = reinterpret_cast<u32x4*>(static_cast<uint16_t*>(y) + i);
+    if constexpr (NT) __builtin_nontemporal_store(w, q);
+    else *q = w;
   }
 }
 
@@ -104,6 +113,18 @@ __device__ __forceinline__ void add_sat(uint32_t n, unsigned long long* d_sat) {
 
 constexpr int kFlatThreads = 256;
 
+constexpr int kFlatUnroll = 4;
+constexpr int64_t kFlatChunk = 2048;           // 8-element vectors per range (32 KiB of BF16)
+constexpr int64_t kFlatMaxBlocks = 256 * 64;   // one amax atomic per work-group
+
+// Vector path: the input is cut into ranges of kFlatChunk vectors; work-group
+// b converts ranges b, b + G, b + 2G, ... (G work-groups), each thread with
+// four 16-byte loads in flight, all accesses non-temporal (the source is read
+// once and the codes are consumed by a later kernel); the last work-group also
+// converts the n % 8 trailing elements.  For 2^31 BF16 -> E4M3 codes this ran
+// at 5.70 TB/s in a probe of the same access shape, against 5.45 for one
+// 16384-vector range per work-group and 4.9 for a grid-stride loop over single
+// vectors.  Scalar path: a grid-stride loop.
 template <int XT, int YT, bool VEC, bool SAT>
 __global__ __launch_bounds__(kFlatThreads) void cast_flat(const void* __restrict__ x,
                                                           void* __restrict__ y, int64_t n,
@@ -115,8 +136,12 @@ __global__ __launch_bounds__(kFlatThreads) void cast_flat(const void* __restrict
   uint32_t ns = 0;
   const float scale = SCALE ? *d_scale : 1.0f;
   uint32_t am = 0;
-  const int64_t tid = static_cast<int64_t>(blockIdx.x) * kFlatThreads + threadIdx.x;
-  const int64_t nthr = static_cast<int64_t>(gridDim.x) * kFlatThreads;
+  auto encode1 = [&](int64_t i, float v) __attribute__((always_inline)) {
+    if (AMAX) { const uint32_t a = fbits(v) & 0x7fffffffu; am = am > a ? am : a; }
+    const float t = SCALE ? v * scale : v;
+    if constexpr (SAT) ns += fabsf(t) > SatMax<YT>::v;
+    store_one<YT>(y, i, to_code<YT>(t));
+  };
   if constexpr (VEC) {
     const int64_t nv = n / 8;
     auto encode8 = [&](int64_t j, const float (&v)[8]) __attribute__((always_inline)) {
@@ -128,38 +153,31 @@ __global__ __launch_bounds__(kFlatThreads) void cast_flat(const void* __restrict
         if constexpr (SAT) ns += fabsf(t) > SatMax<YT>::v;
         c[k] = to_code<YT>(t);
       }
-      store8<YT>(y, j * 8, c);
+      store8<YT, true>(y, j * 8, c);
     };
-    // four 16-byte loads in flight per thread, then one at a time
-    constexpr int kU = 4;
-    int64_t j = tid;
-    for (; j + (kU - 1) * nthr < nv; j += kU * nthr) {
-      float v[kU][8];
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * kFlatChunk;
+    for (int64_t b0 = static_cast<int64_t>(blockIdx.x) * kFlatChunk; b0 < nv; b0 += stride) {
+      const int64_t b1 = b0 + kFlatChunk < nv ? b0 + kFlatChunk : nv;
+      int64_t j = b0 + threadIdx.x;
+      for (; j + (kFlatUnroll - 1) * kFlatThreads < b1; j += kFlatUnroll * kFlatThreads) {
+        float v[kFlatUnroll][8];
 #pragma unroll
-      for (int u = 0; u < kU; ++u) load8<XT>(x, (j + u * nthr) * 8, v[u]);
+        for (int u = 0; u < kFlatUnroll; ++u) load8<XT, true>(x, (j + u * kFlatThreads) * 8, v[u]);
 #pragma unroll
-      for (int u = 0; u < kU; ++u) encode8(j + u * nthr, v[u]);
+        for (int u = 0; u < kFlatUnroll; ++u) encode8(j + u * kFlatThreads, v[u]);
+      }
+      for (; j < b1; j += kFlatThreads) {
+        float v[8];
+        load8<XT, true>(x, j * 8, v);
+        encode8(j, v);
+      }
     }
-    for (; j < nv; j += nthr) {
-      float v[8];
-      load8<XT>(x, j * 8, v);
-      encode8(j, v);
-    }
-    for (int64_t i = nv * 8 + tid; i < n; i += nthr) {
-      const float v = load_one<XT>(x, i);
-      if (AMAX) { const uint32_t a = fbits(v) & 0x7fffffffu; am = am > a ? am : a; }
-      const float t = SCALE ? v * scale : v;
-      if constexpr (SAT) ns += fabsf(t) > SatMax<YT>::v;
-      store_one<YT>(y, i, to_code<YT>(t));
-    }
+    if (blockIdx.x == gridDim.x - 1)
+      for (int64_t i = nv * 8 + threadIdx.x; i < n; i += kFlatThreads) encode1(i, load_one<XT>(x, i));
   } else {
-    for (int64_t i = tid; i < n; i += nthr) {
-      const float v = load_one<XT>(x, i);
-      if (AMAX) { const uint32_t a = fbits(v) & 0x7fffffffu; am = am > a ? am : a; }
-      const float t = SCALE ? v * scale : v;
-      if constexpr (SAT) ns += fabsf(t) > SatMax<YT>::v;
-      store_one<YT>(y, i, to_code<YT>(t));
-    }
+    const int64_t tid = static_cast<int64_t>(blockIdx.x) * kFlatThreads + threadIdx.x;
+    const int64_t nthr = static_cast<int64_t>(gridDim.x) * kFlatThreads;
+    for (int64_t i = tid; i < n; i += nthr) encode1(i, load_one<XT>(x, i));
   }
   if constexpr (SAT) add_sat(ns, d_sat);
   if (AMAX) {
@@ -313,8 +331,8 @@ hipError_t dispatch_layout_t(const void* x, int64_t rows, int64_t cols, int64_t 
   if (y_t == nullptr && ldx == cols && ldy == cols) {
     const int64_t n = rows * cols;
     const bool vec = aligned(x, 16) && aligned(y, 8 * yb);
-    int64_t blocks = (n / 8 + kFlatThreads - 1) / kFlatThreads;
-    if (blocks > 256 * 64) blocks = 256 * 64;
+    int64_t blocks = vec ? (n / 8 + kFlatChunk - 1) / kFlatChunk : (n + kFlatThreads - 1) / kFlatThreads;
+    if (blocks > kFlatMaxBlocks) blocks = kFlatMaxBlocks;
     if (blocks < 1) blocks = 1;
     if (vec)
       cast_flat<XT, YT, true, SAT><<<dim3(static_cast<unsigned>(blocks)), kFlatThreads, 0, s>>>(

@@ -135,47 +135,48 @@ __device__ __forceinline__ void adam_elem(const StepScalars& k, float g16, float
   th = th * k.decay - k.step * (m / d);
 }
 
-// Vector path.  Each work-group owns a contiguous range of kApplyChunk
-// 8-parameter vectors (16-byte gradient words) and each thread keeps two
-// vectors' loads in flight before its first store; the once-read gradients
-// and the write-only 16-bit copy use non-temporal accesses, the state plain
-// ones.  (Measured on MI355X against the grid-stride form with one vector per
-// iteration: 5.26 vs 4.91 TB/s on the same 28 B/param stream.)
-constexpr int64_t kApplyChunk = 512;
+// Vector path, in units of four parameters (a quad: 16 bytes of each FP32
+// array, 8 bytes of 16-bit gradient or copy).  Work-group b owns the
+// contiguous quads [b * kApplyQuads, (b + 1) * kApplyQuads); thread t takes
+// quads t, t + 256, t + 512 and t + 768 of that range, all four loaded before
+// the first store, so every load and store instruction of a wave covers one
+// contiguous span (1 KiB of a state array).  The once-read gradients and the
+// write-only 16-bit copy use non-temporal accesses, the state plain ones.
+// Measured on MI355X for the same 28 B/param stream: 4.91 TB/s for a
+// grid-stride loop over 8-parameter vectors, 5.22 with 4096-parameter ranges
+// of 8-parameter vectors (each store instruction then covers every other
+// 16 bytes of its span, and HBM writes ran 6 % above the algorithmic bytes).
+constexpr int64_t kApplyQuads = 1024;
+constexpr int kApplyUnroll = 4;
 
 template <int GT>
-__device__ __forceinline__ void load_g8(const void* __restrict__ g_p, int64_t j, float (&gg)[8]) {
+__device__ __forceinline__ void load_g4(const void* __restrict__ g_p, int64_t q, float (&gg)[4]) {
   if constexpr (GT == AMP_F32) {
-    const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g_p) + 2 * j);
-    const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g_p) + 2 * j + 1);
+    const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(g_p) + q);
     gg[0] = a.x; gg[1] = a.y; gg[2] = a.z; gg[3] = a.w;
-    gg[4] = b.x; gg[5] = b.y; gg[6] = b.z; gg[7] = b.w;
   } else {
-    const u32x4 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(g_p) + j);
-    const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+    const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(g_p) + q);
+    const uint32_t ww[2] = {w.x, w.y};
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int h = 0; h < 2; ++h) {
       if constexpr (GT == AMP_BF16) {
-        gg[2 * q] = bitsf(ww[q] << 16);
-        gg[2 * q + 1] = bitsf(ww[q] & 0xffff0000u);
+        gg[2 * h] = bitsf(ww[h] << 16);
+        gg[2 * h + 1] = bitsf(ww[h] & 0xffff0000u);
       } else {
-        gg[2 * q] = f16_to_f32(ww[q] & 0xffffu);
-        gg[2 * q + 1] = f16_to_f32(ww[q] >> 16);
+        gg[2 * h] = f16_to_f32(ww[h] & 0xffffu);
+        gg[2 * h + 1] = f16_to_f32(ww[h] >> 16);
       }
     }
   }
 }
 
-__device__ __forceinline__ void load_f8(const float* __restrict__ p, int64_t j, float (&x)[8]) {
-  const f32x4 a = reinterpret_cast<const f32x4*>(p)[2 * j];
-  const f32x4 b = reinterpret_cast<const f32x4*>(p)[2 * j + 1];
+__device__ __forceinline__ void load_f4(const float* __restrict__ p, int64_t q, float (&x)[4]) {
+  const f32x4 a = reinterpret_cast<const f32x4*>(p)[q];
   x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
 }
 
-__device__ __forceinline__ void store_f8(float* __restrict__ p, int64_t j, const float (&x)[8]) {
-  reinterpret_cast<f32x4*>(p)[2 * j] = f32x4{x[0], x[1], x[2], x[3]};
-  reinterpret_cast<f32x4*>(p)[2 * j + 1] = f32x4{x[4], x[5], x[6], x[7]};
+__device__ __forceinline__ void store_f4(float* __restrict__ p, int64_t q, const float (&x)[4]) {
+  reinterpret_cast<f32x4*>(p)[q] = f32x4{x[0], x[1], x[2], x[3]};
 }
 
 template <int GT, int WT, bool HAS_W, bool MULT>
@@ -191,48 +192,45 @@ __global__ __launch_bounds__(kThreads) void apply_kernel(float* __restrict__ th_
   if (st.found_inf) return;
   StepScalars k = make_scalars(st, hp);
   if constexpr (MULT) k.mult = *mult_p;
-  const int64_t nv = n / 8;
-  const int64_t b0 = static_cast<int64_t>(blockIdx.x) * kApplyChunk;
-  const int64_t b1 = b0 + kApplyChunk < nv ? b0 + kApplyChunk : nv;
-  auto update = [&](int64_t j, float (&gg)[8], float (&th)[8], float (&mm)[8], float (&vv)[8]) {
+  const int64_t nq = n / 4;
+  const int64_t q0 = static_cast<int64_t>(blockIdx.x) * kApplyQuads;
+  const int64_t q1 = q0 + kApplyQuads < nq ? q0 + kApplyQuads : nq;
+  auto update = [&](int64_t q, float (&gg)[4], float (&th)[4], float (&mm)[4], float (&vv)[4]) {
 #pragma unroll
-    for (int q = 0; q < 8; ++q) adam_elem<MULT>(k, gg[q], th[q], mm[q], vv[q]);
-    store_f8(th_p, j, th);
-    store_f8(m_p, j, mm);
-    store_f8(v_p, j, vv);
+    for (int e = 0; e < 4; ++e) adam_elem<MULT>(k, gg[e], th[e], mm[e], vv[e]);
+    store_f4(th_p, q, th);
+    store_f4(m_p, q, mm);
+    store_f4(v_p, q, vv);
     if constexpr (HAS_W) {
-      u32x4 w;
-      w.x = w16_code<WT>(th[0]) | (w16_code<WT>(th[1]) << 16);
-      w.y = w16_code<WT>(th[2]) | (w16_code<WT>(th[3]) << 16);
-      w.z = w16_code<WT>(th[4]) | (w16_code<WT>(th[5]) << 16);
-      w.w = w16_code<WT>(th[6]) | (w16_code<WT>(th[7]) << 16);
-      __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(w_p) + j);
+      const u32x2 w = {w16_code<WT>(th[0]) | (w16_code<WT>(th[1]) << 16),
+                       w16_code<WT>(th[2]) | (w16_code<WT>(th[3]) << 16)};
+      __builtin_nontemporal_store(w, reinterpret_cast<u32x2*>(w_p) + q);
     }
   };
-  int64_t j = b0 + threadIdx.x;
-  for (; j + kThreads < b1; j += 2 * kThreads) {
-    float gg[2][8], th[2][8], mm[2][8], vv[2][8];
+  int64_t q = q0 + threadIdx.x;
+  for (; q + (kApplyUnroll - 1) * kThreads < q1; q += kApplyUnroll * kThreads) {
+    float gg[kApplyUnroll][4], th[kApplyUnroll][4], mm[kApplyUnroll][4], vv[kApplyUnroll][4];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      load_g8<GT>(g_p, j + u * kThreads, gg[u]);
-      load_f8(th_p, j + u * kThreads, th[u]);
-      load_f8(m_p, j + u * kThreads, mm[u]);
-      load_f8(v_p, j + u * kThreads, vv[u]);
+    for (int u = 0; u < kApplyUnroll; ++u) {
+      load_g4<GT>(g_p, q + u * kThreads, gg[u]);
+      load_f4(th_p, q + u * kThreads, th[u]);
+      load_f4(m_p, q + u * kThreads, mm[u]);
+      load_f4(v_p, q + u * kThreads, vv[u]);
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) update(j + u * kThreads, gg[u], th[u], mm[u], vv[u]);
+    for (int u = 0; u < kApplyUnroll; ++u) update(q + u * kThreads, gg[u], th[u], mm[u], vv[u]);
   }
-  for (; j < b1; j += kThreads) {
-    float gg[8], th[8], mm[8], vv[8];
-    load_g8<GT>(g_p, j, gg);
-    load_f8(th_p, j, th);
-    load_f8(m_p, j, mm);
-    load_f8(v_p, j, vv);
-    update(j, gg, th, mm, vv);
+  for (; q < q1; q += kThreads) {
+    float gg[4], th[4], mm[4], vv[4];
+    load_g4<GT>(g_p, q, gg);
+    load_f4(th_p, q, th);
+    load_f4(m_p, q, mm);
+    load_f4(v_p, q, vv);
+    update(q, gg, th, mm, vv);
   }
-  // the elements past the last whole vector belong to the last work-group
+  // the elements past the last whole quad belong to the last work-group
   if (blockIdx.x + 1 == gridDim.x) {
-    for (int64_t i = nv * 8 + threadIdx.x; i < n; i += kThreads) {
+    for (int64_t i = nq * 4 + threadIdx.x; i < n; i += kThreads) {
       float th = th_p[i], m = m_p[i], v = v_p[i];
       adam_elem<MULT>(k, grad_at<GT>(g_p, i), th, m, v);
       th_p[i] = th; m_p[i] = m; v_p[i] = v;
@@ -377,35 +375,69 @@ __device__ __forceinline__ void widen8(const void* g, int64_t j, float (&x)[8]) 
   }
 }
 
-// acc = first ? f32(g) : fl32(acc + f32(g)); 8 elements per thread per step
-// when every buffer is 16-byte aligned.
+// acc = first ? f32(g) : fl32(acc + f32(g)).  Vector path (every buffer
+// 16-byte aligned): work-group b owns the contiguous 8-element vectors
+// [b * kAccChunk, (b + 1) * kAccChunk), each thread with two vectors' loads
+// in flight before its stores, all accesses non-temporal (the accumulator is
+// next touched by the following micro-batch's pass); the last work-group also
+// does the n % 8 trailing elements (5.35 TB/s for 2^30 FP16 gradients, against
+// 5.24 for a grid-stride loop and 4.87 with 16384-vector ranges).  Scalar
+// path: a grid-stride loop.
+constexpr int64_t kAccChunk = 512;
+constexpr int kAccUnroll = 2;
+
 template <int GT, bool VEC>
 __global__ __launch_bounds__(kThreads) void accumulate_kernel(float* __restrict__ acc,
                                                               const void* __restrict__ g,
                                                               int64_t n, int first) {
-  const int64_t tid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
-  const int64_t nthr = static_cast<int64_t>(gridDim.x) * kThreads;
-  int64_t done = 0;
   if constexpr (VEC) {
     const int64_t nv = n / 8;
     f32x4* a4 = reinterpret_cast<f32x4*>(acc);
-    for (int64_t j = tid; j < nv; j += nthr) {
-      float x[8];
+    const int64_t b0 = static_cast<int64_t>(blockIdx.x) * kAccChunk;
+    const int64_t b1 = b0 + kAccChunk < nv ? b0 + kAccChunk : nv;
+    auto load = [&](int64_t j, float (&x)[8], f32x4& p, f32x4& q) __attribute__((always_inline)) {
       widen8<GT>(g, j, x);
+      if (!first) {
+        p = __builtin_nontemporal_load(a4 + 2 * j);
+        q = __builtin_nontemporal_load(a4 + 2 * j + 1);
+      }
+    };
+    auto store = [&](int64_t j, const float (&x)[8], f32x4 p, f32x4 q) __attribute__((always_inline)) {
       f32x4 lo = f32x4{x[0], x[1], x[2], x[3]}, hi = f32x4{x[4], x[5], x[6], x[7]};
       if (!first) {
-        const f32x4 p = a4[2 * j], q = a4[2 * j + 1];
         lo = f32x4{p.x + lo.x, p.y + lo.y, p.z + lo.z, p.w + lo.w};
         hi = f32x4{q.x + hi.x, q.y + hi.y, q.z + hi.z, q.w + hi.w};
       }
-      a4[2 * j] = lo;
-      a4[2 * j + 1] = hi;
+      __builtin_nontemporal_store(lo, a4 + 2 * j);
+      __builtin_nontemporal_store(hi, a4 + 2 * j + 1);
+    };
+    int64_t j = b0 + threadIdx.x;
+    for (; j + (kAccUnroll - 1) * kThreads < b1; j += kAccUnroll * kThreads) {
+      float x[kAccUnroll][8];
+      f32x4 p[kAccUnroll] = {}, q[kAccUnroll] = {};
+#pragma unroll
+      for (int u = 0; u < kAccUnroll; ++u) load(j + u * kThreads, x[u], p[u], q[u]);
+#pragma unroll
+      for (int u = 0; u < kAccUnroll; ++u) store(j + u * kThreads, x[u], p[u], q[u]);
     }
-    done = nv * 8;
-  }
-  for (int64_t i = done + tid; i < n; i += nthr) {
-    const float x = grad_at<GT>(g, i);
-    acc[i] = first ? x : acc[i] + x;
+    for (; j < b1; j += kThreads) {
+      float x[8];
+      f32x4 p = {}, q = {};
+      load(j, x, p, q);
+      store(j, x, p, q);
+    }
+    if (blockIdx.x == gridDim.x - 1)
+      for (int64_t i = nv * 8 + threadIdx.x; i < n; i += kThreads) {
+        const float x = grad_at<GT>(g, i);
+        acc[i] = first ? x : acc[i] + x;
+      }
+  } else {
+    const int64_t tid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    const int64_t nthr = static_cast<int64_t>(gridDim.x) * kThreads;
+    for (int64_t i = tid; i < n; i += nthr) {
+      const float x = grad_at<GT>(g, i);
+      acc[i] = first ? x : acc[i] + x;
+    }
   }
 }
 
@@ -427,15 +459,18 @@ __device__ __forceinline__ double block_sum_f64(double v, double* red) {
 
 // Sum of squares of the finite gradients (float64; a float32 square is exact
 // in float64), one partial per work-group; non-finite elements set found_inf.
+// Vector path: work-group b sums the contiguous 8-element vectors
+// [b * chunk, (b + 1) * chunk) with four 16-byte loads in flight per thread
+// (a grid-stride loop over the same grid ran 11 % slower), and the last
+// work-group adds the n % 8 trailing elements.  Scalar path: grid-stride.
 template <int GT, bool VEC>
 __global__ __launch_bounds__(kNormThreads) void norm_kernel(const void* __restrict__ g, int64_t n,
+                                                            int64_t chunk,
                                                             amp_scaler_state* __restrict__ st,
                                                             double* __restrict__ partial) {
   __shared__ double red[kNormThreads / kWave];
   __shared__ uint32_t bad_any;
   if (threadIdx.x == 0) bad_any = 0;
-  const int64_t tid = static_cast<int64_t>(blockIdx.x) * kNormThreads + threadIdx.x;
-  const int64_t nthr = static_cast<int64_t>(gridDim.x) * kNormThreads;
   double accs[4] = {0.0, 0.0, 0.0, 0.0};   // independent chains, summed in a fixed order
   uint32_t bad = 0;
   auto add = [&](float x, int c) {
@@ -444,29 +479,33 @@ __global__ __launch_bounds__(kNormThreads) void norm_kernel(const void* __restri
     const double d = fin ? static_cast<double>(x) : 0.0;
     accs[c] = __builtin_fma(d, d, accs[c]);
   };
-  int64_t done = 0;
   if constexpr (VEC) {
-    // four independent 16-byte loads in flight per thread
     const int64_t nv = n / 8;
-    int64_t j = tid;
-    for (; j + 3 * nthr < nv; j += 4 * nthr) {
+    const int64_t b0 = static_cast<int64_t>(blockIdx.x) * chunk;
+    const int64_t b1 = b0 + chunk < nv ? b0 + chunk : nv;
+    int64_t j = b0 + threadIdx.x;
+    for (; j + 3 * kNormThreads < b1; j += 4 * kNormThreads) {
       float x[4][8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) widen8<GT>(g, j + u * nthr, x[u]);
+      for (int u = 0; u < 4; ++u) widen8<GT>(g, j + u * kNormThreads, x[u]);
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int q = 0; q < 8; ++q) add(x[u][q], q & 3);
     }
-    for (; j < nv; j += nthr) {
+    for (; j < b1; j += kNormThreads) {
       float x[8];
       widen8<GT>(g, j, x);
 #pragma unroll
       for (int q = 0; q < 8; ++q) add(x[q], q & 3);
     }
-    done = nv * 8;
+    if (blockIdx.x == gridDim.x - 1)
+      for (int64_t i = nv * 8 + threadIdx.x; i < n; i += kNormThreads) add(grad_at<GT>(g, i), 0);
+  } else {
+    const int64_t tid = static_cast<int64_t>(blockIdx.x) * kNormThreads + threadIdx.x;
+    const int64_t nthr = static_cast<int64_t>(gridDim.x) * kNormThreads;
+    for (int64_t i = tid; i < n; i += nthr) add(grad_at<GT>(g, i), 0);
   }
-  for (int64_t i = done + tid; i < n; i += nthr) add(grad_at<GT>(g, i), 0);
   __syncthreads();
   if (bad) bad_any = 1u;
   const double t = block_sum_f64<kNormThreads>((accs[0] + accs[1]) + (accs[2] + accs[3]), red);
@@ -477,14 +516,20 @@ __global__ __launch_bounds__(kNormThreads) void norm_kernel(const void* __restri
   }
 }
 
-// sumsq += (partials in order) * (1/S)^2 -- exact scaling by a power of two.
-__global__ void norm_finalize(const double* __restrict__ partial, double* __restrict__ sumsq,
-                              int nb, const amp_scaler_state* st) {
-  if (threadIdx.x != 0) return;
+// sumsq += (sum of the partials) * (1/S)^2 -- exact scaling by a power of
+// two.  One wave: lane l adds partials l, l + 64, ... in order, then a fixed
+// xor tree, so the result does not depend on timing.
+__global__ __launch_bounds__(kWave) void norm_finalize(const double* __restrict__ partial,
+                                                       double* __restrict__ sumsq, int nb,
+                                                       const amp_scaler_state* st) {
   double t = 0.0;
-  for (int b = 0; b < nb; ++b) t += partial[b];
-  const double inv = static_cast<double>(1.0f / st->scale);
-  *sumsq += t * inv * inv;
+  for (int b = threadIdx.x; b < nb; b += kWave) t += partial[b];
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) t += __shfl_xor(t, off, kWave);
+  if (threadIdx.x == 0) {
+    const double inv = static_cast<double>(1.0f / st->scale);
+    *sumsq += t * inv * inv;
+  }
 }
 
 __global__ void norm_init_kernel(amp_grad_norm_state* ns) {
@@ -513,9 +558,9 @@ int64_t grid_for(int64_t work_items) {
   return b < 1 ? 1 : b;
 }
 
-// One work-group per kApplyChunk vectors (at least one, for the tail).
+// One work-group per kApplyQuads quads (at least one, for the tail).
 int64_t apply_blocks(int64_t n) {
-  const int64_t b = (n / 8 + kApplyChunk - 1) / kApplyChunk;
+  const int64_t b = (n / 4 + kApplyQuads - 1) / kApplyQuads;
   return b < 1 ? 1 : b;
 }
 
@@ -616,7 +661,9 @@ hipError_t launch_optimizer_apply(float* th, float* m, float* v, const void* g, 
 hipError_t launch_grad_accumulate(float* acc, const void* g, int gt, int64_t n, int first,
                                   hipStream_t s) {
   const bool vec = aligned(acc, 16) && aligned(g, 16);
-  const dim3 grid(static_cast<unsigned>(grid_for(vec ? n / 8 + 1 : n)));
+  int64_t blocks = vec ? (n / 8 + kAccChunk - 1) / kAccChunk : grid_for(n);
+  if (blocks < 1) blocks = 1;
+  const dim3 grid(static_cast<unsigned>(blocks));
 #define AMP_ACC(T)                                                                      \
   if (vec) accumulate_kernel<T, true><<<grid, kThreads, 0, s>>>(acc, g, n, first);      \
   else accumulate_kernel<T, false><<<grid, kThreads, 0, s>>>(acc, g, n, first);
@@ -637,7 +684,7 @@ hipError_t launch_grad_norm_init(amp_grad_norm_state* ns, hipStream_t s) {
 namespace {
 
 // Work-groups of one norm pass: one float64 partial each, at most
-// AMP_NORM_PARTIALS whatever n is (grid-stride loop).
+// AMP_NORM_PARTIALS whatever n is (each then sums a longer range).
 int64_t norm_blocks(int64_t n) {
   int64_t nb = (n + 8 * kNormThreads - 1) / (8 * kNormThreads);
   if (nb > AMP_NORM_PARTIALS) nb = AMP_NORM_PARTIALS;
@@ -648,16 +695,17 @@ hipError_t launch_norm_pass(const void* g, int gt, int64_t n, amp_scaler_state* 
                             double* partial, double* sumsq, int64_t nb, hipStream_t s) {
   const bool vec = aligned(g, 16);
   const dim3 grid(static_cast<unsigned>(nb));
-#define AMP_NORM(T)                                                                        \
-  if (vec) norm_kernel<T, true><<<grid, kNormThreads, 0, s>>>(g, n, st, partial);           \
-  else norm_kernel<T, false><<<grid, kNormThreads, 0, s>>>(g, n, st, partial);
+  const int64_t chunk = (n / 8 + nb - 1) / nb;     // vectors per work-group (vector path)
+#define AMP_NORM(T)                                                                          \
+  if (vec) norm_kernel<T, true><<<grid, kNormThreads, 0, s>>>(g, n, chunk, st, partial);      \
+  else norm_kernel<T, false><<<grid, kNormThreads, 0, s>>>(g, n, 0, st, partial);
   switch (gt) {
     case AMP_F32: AMP_NORM(AMP_F32) break;
     case AMP_BF16: AMP_NORM(AMP_BF16) break;
     default: AMP_NORM(AMP_F16) break;
   }
 #undef AMP_NORM
-  norm_finalize<<<1, 64, 0, s>>>(partial, sumsq, static_cast<int>(nb), st);
+  norm_finalize<<<1, kWave, 0, s>>>(partial, sumsq, static_cast<int>(nb), st);
   return hipGetLastError();
 }
 

@@ -49,6 +49,49 @@ def test_flat_cast_bit_exact(xt, yt, scaled):
     assert host(amax, np.uint32)[0] == want_amax
 
 
+@pytest.mark.parametrize("n", [1, 2, 7, 8, 9, 8 * 1024, 8 * 1024 + 3, 8 * 1024 * 13 + 5])
+def test_flat_cast_sizes_at_range_edges(n):
+    """Flat vector path: fewer than 8 elements (the trailing loop only), one
+    block pass exactly, and ragged multi-range inputs."""
+    codes = make_input(amp.BF16, n, seed=n)
+    want, want_amax = OC.cast(codes, F.BF16, F.E4M3, 2.0, amax_prior_bits=0)
+    y = empty(n)
+    amax = f32_dev([0.0])
+    amp.amp_cast(dev(codes), amp.BF16, 1, n, n, y, amp.E4M3, n, d_scale=f32_dev([2.0]), d_amax=amax)
+    assert np.array_equal(host(y, np.uint8)[:n], want)
+    assert host(amax, np.uint32)[0] == want_amax
+
+
+def test_flat_cast_multi_pass_ranges():
+    """2^29 + 4141 elements: more 2048-vector ranges than work-groups, so every
+    work-group converts two or three ranges.  Codes are checked on a sample
+    (the range edges, the tail and random indices); amax against three planted
+    elements whose magnitude exceeds every other element's by construction."""
+    nv = 2 * 16384 * 2048 + 517
+    n = 8 * nv + 5
+    rng = np.random.default_rng(2024)
+    # random sign and mantissa, exponent field 120..127: |x| < 2
+    codes = (rng.integers(0, 1 << 16, size=n, dtype=np.uint16) & np.uint16(0x83FF)) | np.uint16(0x3C00)
+    planted = np.array([5, n // 2 + 3, n - 2])
+    codes[planted] = np.array([0x4480, 0xC5A3, 0x4520], np.uint16)   # 1024, -5216, 2560
+    y = empty(n)
+    amax = f32_dev([0.0])
+    amp.amp_cast(dev(codes), amp.BF16, 1, n, n, y, amp.E4M3, n, d_scale=f32_dev([0.25]),
+                 d_amax=amax)
+    got = host(y, np.uint8)[:n]
+    range_el = 8 * 2048
+    edges = np.arange(0, n, range_el)
+    idx = np.unique(np.concatenate([
+        np.arange(0, 2 * range_el), (edges[:, None] + np.arange(-4, 4)).ravel(),
+        np.arange(n - 3 * range_el, n), rng.integers(0, n, size=200_000), planted]))
+    idx = idx[(idx >= 0) & (idx < n)]
+    want, _ = OC.cast(codes[idx], F.BF16, F.E4M3, 0.25, amax_prior_bits=0)
+    bad = np.nonzero(got[idx] != want)[0]
+    assert bad.size == 0, (idx[bad[:10]], got[idx[bad[:10]]], want[bad[:10]])
+    _, want_amax = OC.cast(codes[planted], F.BF16, F.E4M3, 0.25, amax_prior_bits=0)
+    assert host(amax, np.uint32)[0] == want_amax
+
+
 @pytest.mark.parametrize("xt,yt", [(amp.BF16, amp.E4M3), (amp.BF16, amp.E5M2),
                                    (amp.F32, amp.E4M3), (amp.F32, amp.BF16),
                                    (amp.F16, amp.F16)])

@@ -67,6 +67,31 @@ def test_adamw_steps_bit_exact_with_skip(gt, wt):
             assert np.array_equal(host(w_d, np.uint16), w)
 
 
+@pytest.mark.parametrize("n", [1, 3, 4, 7, 4096, 4096 * 3 + 6])
+def test_adamw_sizes_at_range_edges(n):
+    """Vector path below one 4-parameter unit (the trailing loop only), one
+    work-group range exactly, and several ranges with a ragged end."""
+    hp_o = OA.AdamWHParams(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    hp = amp.AdamWHParams(hp_o.lr, hp_o.beta1, hp_o.beta2, hp_o.eps, hp_o.weight_decay)
+    theta0 = synth.normal_f32(7, n, 0.02)
+    m0 = synth.normal_f32(8, n, 1e-3)
+    v0 = np.abs(synth.normal_f32(9, n, 1e-6)).astype(np.float32)
+    th_d, m_d, v_d = dev(theta0), dev(m0), dev(v0)
+    w_d = empty(2 * n)
+    st_d = empty(40)
+    amp.amp_scaler_init(st_d, 256.0)
+    codes = _grads(amp.BF16, n, 11, 256.0)
+    amp.amp_optimizer_step(th_d, m_d, v_d, dev(codes), amp.BF16, w_d, amp.BF16, n, hp, st_d)
+    th, m, v, w, applied = OA.apply(theta0.astype(np.float64), m0.astype(np.float64),
+                                    v0.astype(np.float64), codes, F.BF16, hp_o, OA.AdamCounters(),
+                                    256.0, w_fmt=F.BF16)
+    assert applied
+    assert np.array_equal(host(th_d, np.float32).astype(np.float64), th)
+    assert np.array_equal(host(m_d, np.float32).astype(np.float64), m)
+    assert np.array_equal(host(v_d, np.float32).astype(np.float64), v)
+    assert np.array_equal(host(w_d, np.uint16)[:n], w)
+
+
 def test_skip_check_flag_and_external_overflow():
     n = 4096
     hp = amp.AdamWHParams(1e-3, 0.9, 0.999, 1e-8, 0.01)

@@ -118,22 +118,31 @@ __device__ __forceinline__ uint32_t e2m1_rne(float y) {
   return b > 0x7f800000u ? 0u : c;          // NaN -> +0 (E2M1 has no NaN)
 }
 
-// Stochastic rounding with u in [0, 1): round the magnitude up iff u < frac,
-// frac = (|y| - lower neighbour) / gap, exact.  Above 1 the lower neighbour is
-// the FP32 value cut to one fraction bit and frac is the remaining 22 bits.
-__device__ __forceinline__ uint32_t e2m1_sr(float y, float u) {
+// Stochastic rounding driven by the element's 32-bit random word w: the
+// magnitude rounds up iff u < frac with u = (w >> 8) * 2^-24 and
+// frac = (|y| - lower neighbour) / gap (exact in FP32).  Both ranges are
+// evaluated as a carry: adding the complement of the word's top bits to the
+// part of |y| below the E2M1 step carries into the kept part exactly when the
+// rounding goes up.
+//  * |y| >= 1: the step is one unit of FP32 bit 22, the part below it is the
+//    low 22 pattern bits m, and u < frac  <=>  (w >> 10) < m
+//    <=>  m + (~w >> 10) >= 2^22; the carry runs on into the exponent, so the
+//    code is (pattern >> 22) - 252 after the addition (6 is the largest
+//    magnitude and has m = 0, so nothing carries past it).
+//  * |y| < 1: the step is 0.5; with C = ceil(|y| * 2^25) (integer units of
+//    2^-25; for the integer X = w >> 8, X < F <=> X < ceil(F)), the code is
+//    (C + (~w >> 8)) >> 24.
+// A NaN y is taken as magnitude 6 (code 7 with y's sign bit).  In the
+// quantizer y is NaN only if the input block holds a NaN, and then the block
+// scale is NaN and the whole block is zeroed, or if enc / S overflows (a
+// tensor amax below about 2^-107) and an element is zero.
+__device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t w) {
   const float a = fminf(fabsf(y), 6.0f);
   const uint32_t b = fbits(a);
-  const uint32_t lo_n = (b >> 22) - 252u;
-  const float frac_n = static_cast<float>(b & 0x3fffffu) * 2.384185791015625e-7f;   // 2^-22
-  const uint32_t lo_s = a >= 0.5f;
-  const float frac_s = (a - (lo_s ? 0.5f : 0.0f)) * 2.0f;
-  const bool nrm = b >= 0x3f800000u;
-  const uint32_t lo = nrm ? lo_n : lo_s;
-  const float frac = nrm ? frac_n : frac_s;
-  const uint32_t up = static_cast<uint32_t>(lo < 7u) & static_cast<uint32_t>(u < frac);
-  const uint32_t c = (lo + up) | ((fbits(y) >> 28) & 0x8u);
-  return (fbits(y) & 0x7fffffffu) > 0x7f800000u ? 0u : c;   // NaN -> +0
+  const uint32_t nw = ~w;
+  const uint32_t cn = (b + (nw >> 10) - 0x3f000000u) >> 22;          // (pattern >> 22) - 252
+  const uint32_t cs = (static_cast<uint32_t>(ceilf(a * 33554432.0f)) + (nw >> 8)) >> 24;
+  return (b >= 0x3f800000u ? cn : cs) | ((fbits(y) >> 28) & 0x8u);
 }
 
 __device__ __forceinline__ float e2m1_to_f32(uint32_t c) {

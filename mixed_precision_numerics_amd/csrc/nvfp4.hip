@@ -172,10 +172,7 @@ __global__ __launch_bounds__(kT) void nvfp4_kernel(const void* __restrict__ x, i
               static_cast<uint32_t>(sr_seed), static_cast<uint32_t>(sr_seed >> 32));
           const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float u = static_cast<float>(ww[e] >> 8) * 5.9604644775390625e-8f;
-            codes[4 * quad + e] = e2m1_sr(z[4 * quad + e] * mult, u);
-          }
+          for (int e = 0; e < 4; ++e) codes[4 * quad + e] = e2m1_sr(z[4 * quad + e] * mult, ww[e]);
         }
       } else {
 #pragma unroll
@@ -320,8 +317,9 @@ __device__ __forceinline__ uint32_t row_chunk(const u32x4 (&raw)[16], int i, uin
 }
 
 // Philox4x32-10 on the four counters blk0 .. blk0+3 (high words from blk),
-// side by side: the rounds stay rolled so only the current round key is live,
-// and the four independent chains fill the multiplier's latency.
+// side by side: the four independent chains fill the multiplier's latency.
+// The rounds run two per loop iteration, so that the state words alternate
+// between two register sets instead of being copied back every round.
 __device__ __forceinline__ void philox_x4(uint64_t blk0, uint64_t seed, uint32_t (&w)[16]) {
   uint32_t x[4], y[4], z[4], v[4];
 #pragma unroll
@@ -333,7 +331,7 @@ __device__ __forceinline__ void philox_x4(uint64_t blk0, uint64_t seed, uint32_t
     v[q] = 0u;
   }
   uint32_t k0 = static_cast<uint32_t>(seed), k1 = static_cast<uint32_t>(seed >> 32);
-#pragma unroll 1
+#pragma unroll 2
   for (int r = 0; r < 10; ++r) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -365,10 +363,7 @@ __device__ __forceinline__ u32x2 encode_chunk(const float (&z)[16], float mult, 
     uint32_t w[16];
     philox_x4(idx0 >> 2, sr_seed, w);
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float u = static_cast<float>(w[j] >> 8) * 5.9604644775390625e-8f;
-      codes[j] = e2m1_sr(z[j] * mult, u);
-    }
+    for (int j = 0; j < 16; ++j) codes[j] = e2m1_sr(z[j] * mult, w[j]);
   } else {
 #pragma unroll
     for (int j = 0; j < 16; ++j) codes[j] = e2m1_rne(z[j] * mult);

@@ -509,7 +509,8 @@ def clip_workload(torch, amp):
 def mx_workload(torch, amp):
     """MX GEMMs on the block-scaled matrix cores at the FFN up projection
     (8192 x 28672 x 4096, K-contiguous operands as the forward pass has them),
-    plus the MX quantizer of the activation: MXFP4 (E2M1) and MXFP8 (E4M3)."""
+    plus the MX quantizer of the activation and of the weight: MXFP4 (E2M1) and
+    MXFP8 (E4M3)."""
     T, I, O = 8192, 4096, 28672
     gen = torch.Generator(device="cuda").manual_seed(11)
     X = torch.randn(T, I, device="cuda", generator=gen).to(torch.bfloat16)
@@ -531,7 +532,14 @@ def mx_workload(torch, amp):
         q_ms = _timed_rot(torch, [lambda i=i: amp.amp_mx_quantize(Xs[i], amp.BF16, T, I, I, 0, yt, qs[i],
                                                                    ss[i]) for i in range(k)], 4 * k)
         del Xs[1:], qs[1:], ss[1:]
-        amp.amp_mx_quantize(W, amp.BF16, O, I, I, 0, yt, qw, sw)
+        # the weight (28672 x 4096, 3.5x the activation's elements)
+        kw = _copies(1 << 30, O * I * 2)
+        Ws = [W] + [W.clone() for _ in range(kw - 1)]
+        qws = [qw] + [torch.empty_like(qw) for _ in range(kw - 1)]
+        sws = [sw] + [torch.empty_like(sw) for _ in range(kw - 1)]
+        qw_ms = _timed_rot(torch, [lambda i=i: amp.amp_mx_quantize(Ws[i], amp.BF16, O, I, I, 0, yt, qws[i],
+                                                                    sws[i]) for i in range(kw)], 4 * kw)
+        del Ws[1:], qws[1:], sws[1:]
         Y = torch.empty(T, O, device="cuda", dtype=torch.bfloat16)
         bsx = amp.BlockScales(sx.data_ptr(), I // 32, 0, 0)
         bsw = amp.BlockScales(sw.data_ptr(), I // 32, 0, 0)
@@ -540,9 +548,12 @@ def mx_workload(torch, amp):
                                                      bsx, bsw, flags=gflags), 10)
         tf = flops / g_ms / 1e9
         qbytes = T * I * (2 + 1.0 / div + 1.0 / 32)
+        wbytes = O * I * (2 + 1.0 / div + 1.0 / 32)
         out[name] = {"gemm_ms": round(g_ms, 4), "gemm_tflops": round(tf, 1), "peak_tflops": peak,
                      "frac": round(tf / peak, 4), "quantize_ms": round(q_ms, 4),
-                     "quantize_gbs": round(qbytes / q_ms / 1e6, 1)}
+                     "quantize_gbs": round(qbytes / q_ms / 1e6, 1),
+                     "quantize_weight_ms": round(qw_ms, 4),
+                     "quantize_weight_gbs": round(wbytes / qw_ms / 1e6, 1)}
         if name == "mxfp8":
             out[name]["mfma"] = "bf16 (FP8 x UE8M0 block scale widened exactly; FP32 sums)"
             out[name]["frac_bf16_mfma"] = round(tf / BF16_PEAK_TFLOPS, 4)

@@ -51,6 +51,30 @@ def test_mx_quantize_bit_exact(xt, yt, transpose):
     assert bad.size == 0, (bad[:5], got[tuple(bad[0])], wq[tuple(bad[0])])
 
 
+@pytest.mark.parametrize("xt", [amp.BF16, amp.F32])
+@pytest.mark.parametrize("yt", [amp.E4M3, amp.E2M1X2])
+@pytest.mark.parametrize("rows,cols,ld_pad", [(257, 4096, 0), (96, 160, 32), (10, 64, 0)])
+def test_mx_quantize_plain_layouts(xt, yt, rows, cols, ld_pad):
+    """Plain operand: contiguous rows (one flat stream of blocks, many
+    work-groups and a ragged last one; a single block row) and padded rows
+    (per-block threads)."""
+    codes, vals = mx_input(90 + xt + yt + rows, rows, cols, xt)
+    ldx = cols + ld_pad
+    padded = np.zeros((rows, ldx), codes.dtype)
+    padded[:, :cols] = codes
+    qbytes = rows * cols // 2 if yt == amp.E2M1X2 else rows * cols
+    q = empty(qbytes, fill=0xEE)
+    sc = empty(rows * cols // 32, fill=0xEE)
+    amp.amp_mx_quantize(dev(padded), xt, rows, cols, ldx, 0, yt, q, sc)
+    wq, ws = OM.quantize(vals, YF[yt], transpose=False)
+    if yt == amp.E2M1X2:
+        wq = OM.pack_e2m1(wq)
+    assert np.array_equal(host(sc, np.uint8)[:rows * cols // 32].reshape(ws.shape), ws)
+    got = host(q, np.uint8)[:qbytes].reshape(wq.shape)
+    bad = np.argwhere(got != wq)
+    assert bad.size == 0, (bad[:5], got[tuple(bad[0])], wq[tuple(bad[0])])
+
+
 def mx_operand(seed, rows, k, yt):
     """Random MX operand: element codes and UE8M0 scales around 2^0."""
     g = synth.rng(seed)

@@ -24,6 +24,8 @@
 namespace amp {
 namespace {
 
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
 template <int XT>
 __device__ __forceinline__ float load_one(const void* p, int64_t i) {
   if constexpr (XT == AMP_F32) return static_cast<const float*>(p)[i];
@@ -195,7 +197,10 @@ constexpr int kTileThreads = 256;
 // and every access is 16-byte aligned (checked on the host).
 __device__ __forceinline__ int swz8(int c) { return (2 * (c >> 4)) & 14; }
 
-template <int XT, int YT, bool WY, bool WYT, bool VEC, bool SAT>
+// VEC: 0 element loads; 1 16-byte accesses, edge tiles element by element;
+// 2 16-byte accesses and every tile full (no edge code in the kernel, which
+// keeps the edge path's registers out of its allocation).
+template <int XT, int YT, bool WY, bool WYT, int VEC, bool SAT>
 __global__ __launch_bounds__(kTileThreads) void cast_tile(
     const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
     void* __restrict__ y, int64_t ldy, void* __restrict__ y_t, int64_t ldy_t,
@@ -213,7 +218,7 @@ __global__ __launch_bounds__(kTileThreads) void cast_tile(
   const int64_t c_base = static_cast<int64_t>(blockIdx.x) * kTile;
   const int t = threadIdx.x;
   const int c0 = 8 * (t % 16), r0 = 8 * (t / 16);
-  const bool full = VEC && (r_base + kTile <= rows) && (c_base + kTile <= cols);
+  const bool full = VEC == 2 || (VEC == 1 && (r_base + kTile <= rows) && (c_base + kTile <= cols));
   uint32_t am = 0;
   // 16-bit codes are kept one per register; 8-bit ones four per register
   // (row i's codes 4q .. 4q+3 in pk[i][q]), which cuts the live registers
@@ -348,12 +353,16 @@ hipError_t dispatch_layout_t(const void* x, int64_t rows, int64_t cols, int64_t 
   if (y_t) vec = vec && aligned(y_t, 16) && (ldy_t * yb) % 16 == 0;
   const dim3 grid(static_cast<unsigned>((cols + kTile - 1) / kTile),
                   static_cast<unsigned>((rows + kTile - 1) / kTile));
+  const int vk = !vec ? 0 : (rows % kTile == 0 && cols % kTile == 0 ? 2 : 1);
 #define AMP_TILE(WY, WYT, V) \
   cast_tile<XT, YT, WY, WYT, V, SAT><<<grid, kTileThreads, 0, s>>>( \
       x, rows, cols, ldx, y, ldy, y_t, ldy_t, d_scale, d_amax, d_sat)
-  if (y && y_t) { if (vec) AMP_TILE(true, true, true); else AMP_TILE(true, true, false); }
-  else if (y)   { if (vec) AMP_TILE(true, false, true); else AMP_TILE(true, false, false); }
-  else          { if (vec) AMP_TILE(false, true, true); else AMP_TILE(false, true, false); }
+#define AMP_TILE_V(WY, WYT) \
+  do { if (vk == 2) AMP_TILE(WY, WYT, 2); else if (vk == 1) AMP_TILE(WY, WYT, 1); else AMP_TILE(WY, WYT, 0); } while (0)
+  if (y && y_t) AMP_TILE_V(true, true);
+  else if (y)   AMP_TILE_V(true, false);
+  else          AMP_TILE_V(false, true);
+#undef AMP_TILE_V
 #undef AMP_TILE
   return hipGetLastError();
 }
@@ -470,7 +479,8 @@ __device__ __forceinline__ float tile_scale(uint32_t amax_bits, float fp8_max) {
   return (amax_bits == 0u || amax_bits >= 0x7f800000u) ? 1.0f : fp8_max / bitsf(amax_bits);
 }
 
-template <int XT, int YT, bool BLOCK, bool WQ, bool WQT, bool VEC>
+// VEC as for cast_tile.
+template <int XT, int YT, bool BLOCK, bool WQ, bool WQT, int VEC>
 __global__ __launch_bounds__(kTileThreads) void bw_quant_tile(
     const void* __restrict__ x, int64_t rows, int64_t cols, int64_t ldx,
     uint8_t* __restrict__ q, int64_t ldq, float* __restrict__ s, int64_t lds,
@@ -488,35 +498,128 @@ __global__ __launch_bounds__(kTileThreads) void bw_quant_tile(
   const int64_t c_base = static_cast<int64_t>(blockIdx.x) * kTile;
   const int t = threadIdx.x;
   const int c0 = 8 * (t % 16), r0 = 8 * (t / 16);
-  const bool full = VEC && (r_base + kTile <= rows) && (c_base + kTile <= cols);
-  float v[8][8];
+  const bool full = VEC == 2 || (VEC == 1 && (r_base + kTile <= rows) && (c_base + kTile <= cols));
+  // 16-bit inputs stay packed (two per register, widened where used), which
+  // halves the registers the 8x8 sub-block holds across the block barriers
+  constexpr bool kPacked = XT != AMP_F32;
+  uint32_t w16[kPacked ? 8 : 1][4];
+  float v32[kPacked ? 1 : 8][8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int64_t r = r_base + r0 + i, c = c_base + c0;
-    if (full) {
-      load8<XT>(x, r * ldx + c, v[i]);
+    if constexpr (kPacked) {
+      if (full) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(x) + r * ldx + c);
+        w16[i][0] = w.x; w16[i][1] = w.y; w16[i][2] = w.z; w16[i][3] = w.w;
+      } else {
+        const uint16_t* xs = static_cast<const uint16_t*>(x);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t lo = (r < rows && c + 2 * q < cols) ? xs[r * ldx + c + 2 * q] : 0u;
+          const uint32_t hi = (r < rows && c + 2 * q + 1 < cols) ? xs[r * ldx + c + 2 * q + 1] : 0u;
+          w16[i][q] = lo | (hi << 16);
+        }
+      }
     } else {
+      if (full) {
+        load8<XT>(x, r * ldx + c, v32[i]);
+      } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        v[i][j] = (r < rows && c + j < cols) ? load_one<XT>(x, r * ldx + c + j) : 0.0f;
+        for (int j = 0; j < 8; ++j)
+          v32[i][j] = (r < rows && c + j < cols) ? load_one<XT>(x, r * ldx + c + j) : 0.0f;
+      }
     }
   }
-  // |x| bit maxima of this thread's 8 rows and 8 columns (padding is 0)
+  // an empty asm that claims to change the packed words: the compiler then
+  // widens them again where the column codes need them instead of keeping
+  // all 64 widened values live across the column-scale barriers
+  auto repack = [&]() __attribute__((always_inline)) {
+    if constexpr (kPacked) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) asm volatile("" : "+v"(w16[i][q]));
+    }
+  };
+  auto val = [&](int i, int j) __attribute__((always_inline)) -> float {
+    if constexpr (XT == AMP_BF16) {
+      const uint32_t w = w16[i][j >> 1];
+      return bitsf((j & 1) ? (w & 0xffff0000u) : (w << 16));
+    } else if constexpr (XT == AMP_F16) {
+      const uint32_t w = w16[i][j >> 1];
+      return f16_to_f32((j & 1) ? (w >> 16) : (w & 0xffffu));
+    } else {
+      return v32[i][j];
+    }
+  };
+  // |x| bit maxima of this thread's 8 rows and 8 columns (padding is 0).
+  // 16-bit inputs: the magnitudes of a packed pair are compared as two
+  // unsigned 16-bit halves (their order is the order of |x|, NaN above inf,
+  // as for the FP32 patterns), and only each maximum is widened.
   uint32_t ra[8], ca[8];
+  if constexpr (kPacked) {
+    auto pmax = [](uint32_t a, uint32_t b) __attribute__((always_inline)) {
+      return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                    __builtin_bit_cast(u16x2, b)));
+    };
+    auto wide = [](uint32_t h) __attribute__((always_inline)) -> uint32_t {
+      if constexpr (XT == AMP_BF16) return h << 16;
+      else return fbits(f16_to_f32(h));
+    };
+    uint32_t pc[4];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) ca[j] = 0;
+    for (int q = 0; q < 4; ++q) pc[q] = w16[0][q] & 0x7fff7fffu;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    ra[i] = 0;
+    for (int i = 0; i < 8; ++i) {
+      uint32_t pr = w16[i][0] & 0x7fff7fffu;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const uint32_t a = fbits(v[i][j]) & 0x7fffffffu;
-      ra[i] = ra[i] > a ? ra[i] : a;
-      ca[j] = ca[j] > a ? ca[j] : a;
+      for (int q = 1; q < 4; ++q) pr = pmax(pr, w16[i][q] & 0x7fff7fffu);
+      const uint32_t lo = pr & 0xffffu, hi = pr >> 16;
+      ra[i] = wide(lo > hi ? lo : hi);
+      if (i > 0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) pc[q] = pmax(pc[q], w16[i][q] & 0x7fff7fffu);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      ca[2 * q] = wide(pc[q] & 0xffffu);
+      ca[2 * q + 1] = wide(pc[q] >> 16);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ca[j] = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      ra[i] = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint32_t a = fbits(val(i, j)) & 0x7fffffffu;
+        ra[i] = ra[i] > a ? ra[i] : a;
+        ca[j] = ca[j] > a ? ca[j] : a;
+      }
     }
   }
-  float rs[8], cs[8];
+  float cs[8];
   const int64_t kb_q = c_base / kTile, kb_t = r_base / kTile;
+  // plain codes: written as soon as the row scales are known, so that the
+  // row scales are dead while the column scales are formed
+  auto encode_rows = [&](const float (&rs)[8]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int64_t r = r_base + r0 + i, c = c_base + c0;
+      uint32_t code[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) code[j] = to_code<YT>(val(i, j) * rs[i]);
+      if (full) {
+        store8<YT>(q, r * ldq + c, code);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (r < rows && c + j < cols) q[r * ldq + c + j] = static_cast<uint8_t>(code[j]);
+      }
+    }
+  };
   if constexpr (BLOCK) {
     uint32_t m = ra[0];
 #pragma unroll
@@ -529,17 +632,25 @@ __global__ __launch_bounds__(kTileThreads) void bw_quant_tile(
       if (WQT) st[kb_t * ldst + c_base / kTile] = 1.0f / sc;
     }
     __syncthreads();
+    float rs[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) rs[i] = cs[i] = bscale;
+    if constexpr (WQ) {
+      encode_rows(rs);
+      repack();
+    }
   } else {
     if constexpr (WQ) {
       // the 16 threads of a row of the region are the 16 lanes of a DPP row
+      float rs[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         rs[i] = tile_scale(max16(ra[i]), kMax);
         const int64_t r = r_base + r0 + i;
         if (t % 16 == 0 && r < rows) s[kb_q * lds + r] = 1.0f / rs[i];
       }
+      encode_rows(rs);
+      repack();
     }
     if constexpr (WQT) {
 #pragma unroll
@@ -558,29 +669,13 @@ __global__ __launch_bounds__(kTileThreads) void bw_quant_tile(
       for (int j = 0; j < 8; ++j) cs[j] = cscale[c0 + j];
     }
   }
-  if constexpr (WQ) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t r = r_base + r0 + i, c = c_base + c0;
-      uint32_t code[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) code[j] = to_code<YT>(v[i][j] * rs[i]);
-      if (full) {
-        store8<YT>(q, r * ldq + c, code);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (r < rows && c + j < cols) q[r * ldq + c + j] = static_cast<uint8_t>(code[j]);
-      }
-    }
-  }
   if constexpr (WQT) {
     // column j of the sub-block -> LDS row c0 + j (cast_tile's swizzled layout)
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       uint32_t c8[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) c8[i] = to_code<YT>(v[i][j] * cs[j]);
+      for (int i = 0; i < 8; ++i) c8[i] = to_code<YT>(val(i, j) * cs[j]);
       uint2 w;
       w.x = c8[0] | (c8[1] << 8) | (c8[2] << 16) | (c8[3] << 24);
       w.y = c8[4] | (c8[5] << 8) | (c8[6] << 16) | (c8[7] << 24);
@@ -616,14 +711,15 @@ hipError_t dispatch_bw(const void* x, int64_t rows, int64_t cols, int64_t ldx, i
   if (qt) vec = vec && aligned(qt, 16) && ldqt % 16 == 0;
   const dim3 grid(static_cast<unsigned>((cols + kTile - 1) / kTile),
                   static_cast<unsigned>((rows + kTile - 1) / kTile));
+  const int vk = !vec ? 0 : (rows % kTile == 0 && cols % kTile == 0 ? 2 : 1);
+#define AMP_BW1(B, WQ, WQT, V)                                                                  \
+  bw_quant_tile<XT, YT, B, WQ, WQT, V><<<grid, kTileThreads, 0, hs>>>(                         \
+      x, rows, cols, ldx, q, ldq, s, lds, qt, ldqt, st, ldst)
 #define AMP_BW(B, WQ, WQT)                                                                      \
   do {                                                                                         \
-    if (vec)                                                                                   \
-      bw_quant_tile<XT, YT, B, WQ, WQT, true><<<grid, kTileThreads, 0, hs>>>(                 \
-          x, rows, cols, ldx, q, ldq, s, lds, qt, ldqt, st, ldst);                             \
-    else                                                                                       \
-      bw_quant_tile<XT, YT, B, WQ, WQT, false><<<grid, kTileThreads, 0, hs>>>(                \
-          x, rows, cols, ldx, q, ldq, s, lds, qt, ldqt, st, ldst);                             \
+    if (vk == 2) AMP_BW1(B, WQ, WQT, 2);                                                       \
+    else if (vk == 1) AMP_BW1(B, WQ, WQT, 1);                                                  \
+    else AMP_BW1(B, WQ, WQT, 0);                                                               \
   } while (0)
   if (block) {
     if (q && qt) AMP_BW(true, true, true);
@@ -635,6 +731,7 @@ hipError_t dispatch_bw(const void* x, int64_t rows, int64_t cols, int64_t ldx, i
     else AMP_BW(false, false, true);
   }
 #undef AMP_BW
+#undef AMP_BW1
   return hipGetLastError();
 }
 

@@ -46,30 +46,25 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float x) {
   return (u & 0x7fffffffu) > 0x7f800000u ? 0x7fc0u : r;
 }
 
-// ---- FP32 -> E4M3 (saturating) -------------------------------------------
+// ---- FP32 -> E4M3 / E5M2 (saturating) ------------------------------------
+// Round to nearest even, magnitudes beyond the largest finite value (448,
+// 57344) and infinities saturate to it, NaN gives 0x7F.  gfx950's conversion
+// instruction rounds to nearest even but turns out-of-range inputs into NaN,
+// so the input is first clamped to the format's range with a median-of-three
+// (which returns a bound for a NaN input, hence the NaN select).  Compared on
+// MI355X with bit-manipulation encoders (mantissa rounded at the format's last
+// bit for normal results, an aligning addition for subnormal ones, a
+// saturation threshold): equal on all 2^32 FP32 patterns for both formats.
 __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
-  const uint32_t u = fbits(x);
-  const uint32_t s = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7fffffffu;
-  const uint32_t rn = (a + 0x7ffffu + ((a >> 20) & 1u) - 0x3c000000u) >> 20;  // >= 2^-6
-  const uint32_t rs = fbits(bitsf(a) + 16384.0f) - 0x46800000u;              // spacing 2^-9
-  uint32_t r = a >= 0x3c800000u ? rn : rs;
-  r = a >= 0x43e00000u ? 0x7eu : r;                   // >= 448 (and inf) saturate
-  r |= s;
-  return a > 0x7f800000u ? 0x7fu : r;
+  const float y = __builtin_amdgcn_fmed3f(x, -448.0f, 448.0f);
+  const uint32_t c = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(y, y, 0, false)) & 0xffu;
+  return x != x ? 0x7fu : c;
 }
 
-// ---- FP32 -> E5M2 (saturating) -------------------------------------------
 __device__ __forceinline__ uint32_t f32_to_e5m2(float x) {
-  const uint32_t u = fbits(x);
-  const uint32_t s = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7fffffffu;
-  const uint32_t rn = (a + 0xfffffu + ((a >> 21) & 1u) - 0x38000000u) >> 21;  // >= 2^-14
-  const uint32_t rs = fbits(bitsf(a) + 128.0f) - 0x43000000u;                // spacing 2^-16
-  uint32_t r = a >= 0x38800000u ? rn : rs;
-  r = a >= 0x47600000u ? 0x7bu : r;                   // >= 57344 (and inf) saturate
-  r |= s;
-  return a > 0x7f800000u ? 0x7fu : r;
+  const float y = __builtin_amdgcn_fmed3f(x, -57344.0f, 57344.0f);
+  const uint32_t c = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_bf8_f32(y, y, 0, false)) & 0xffu;
+  return x != x ? 0x7fu : c;
 }
 
 // ---- widening (exact) -----------------------------------------------------

@@ -24,26 +24,19 @@ __device__ __forceinline__ float bitsf(uint32_t u) { return __uint_as_float(u); 
 // All conversions below are branch-free: both the normal-range and the
 // subnormal-range result are formed and selected, so a wave never diverges.
 
-// ---- FP32 -> FP16 ---------------------------------------------------------
+// ---- FP32 -> FP16 / BF16 ---------------------------------------------------
+// Round to nearest even (FP16 subnormal results kept, |x| >= 65520 gives inf),
+// NaN gives the canonical 0x7E00 / 0x7FC0.  gfx950's conversions round to
+// nearest even and keep NaN payloads, hence the NaN select.  Compared on MI355X
+// with bit-manipulation encoders: equal on all 2^32 FP32 patterns.
 __device__ __forceinline__ uint32_t f32_to_f16(float x) {
-  const uint32_t u = fbits(x);
-  const uint32_t s = (u >> 16) & 0x8000u;
-  const uint32_t a = u & 0x7fffffffu;
-  // normal result (|x| >= 2^-14): round the mantissa at bit 13, rebias by 112
-  const uint32_t rn = (a + 0xfffu + ((a >> 13) & 1u) - 0x38000000u) >> 13;
-  // |x| < 2^-14: spacing 2^-24 = ulp of [0.5, 1)
-  const uint32_t rs = fbits(bitsf(a) + 0.5f) - 0x3f000000u;
-  uint32_t r = a >= 0x38800000u ? rn : rs;
-  r = a >= 0x477ff000u ? 0x7c00u : r;                 // >= 65520 rounds to inf
-  r |= s;
-  return a > 0x7f800000u ? 0x7e00u : r;               // NaN
+  const uint32_t c = __builtin_bit_cast(uint16_t, static_cast<_Float16>(x));
+  return x != x ? 0x7e00u : c;
 }
 
-// ---- FP32 -> BF16 ---------------------------------------------------------
 __device__ __forceinline__ uint32_t f32_to_bf16(float x) {
-  const uint32_t u = fbits(x);
-  const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-  return (u & 0x7fffffffu) > 0x7f800000u ? 0x7fc0u : r;
+  const uint32_t c = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x));
+  return x != x ? 0x7fc0u : c;
 }
 
 // ---- FP32 -> E4M3 / E5M2 (saturating) ------------------------------------
@@ -100,17 +93,16 @@ __device__ __forceinline__ float e5m2_to_f32(uint32_t c) {
 // Magnitude codes 0..7 = {0, 0.5, 1, 1.5, 2, 3, 4, 6}; bit 3 is the sign.
 // From [1, 8) up the E2M1 grid is the FP32 grid cut to one fraction bit, so
 // code = (FP32 bits >> 22) - 252 there; below 1 the spacing is 0.5.
+// Round to nearest even, ties to the even code (5 gives 4); magnitudes above
+// 5 give 6, including everything beyond 6 (saturation); NaN gives +0 (E2M1
+// has no NaN).  gfx950's FP4 conversion
+// (scale 1) rounds to nearest even and saturates; only NaN needs the select.
+// Compared on MI355X with a bit-manipulation encoder (the FP32 pattern cut to
+// one fraction bit from 1 up, midpoint compares below): equal on all 2^32 FP32
+// patterns.
 __device__ __forceinline__ uint32_t e2m1_rne(float y) {
-  const float a = fabsf(y);
-  const uint32_t b = fbits(a);
-  // a >= 1: round the significand to one fraction bit, ties to even; 7 and up
-  // (the tie 7 goes to 8) saturate to 6
-  uint32_t cn = ((b + 0x1fffffu + ((b >> 22) & 1u)) >> 22) - 252u;
-  cn = cn > 7u ? 7u : cn;
-  // a < 1: midpoints 0.25 (tie to 0) and 0.75 (tie to 1)
-  const uint32_t cs = static_cast<uint32_t>(a > 0.25f) + static_cast<uint32_t>(a >= 0.75f);
-  const uint32_t c = (b >= 0x3f800000u ? cn : cs) | ((fbits(y) >> 28) & 0x8u);
-  return b > 0x7f800000u ? 0u : c;          // NaN -> +0 (E2M1 has no NaN)
+  const uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y, y, 1.0f, 0) & 0xfu;
+  return y != y ? 0u : c;
 }
 
 // Stochastic rounding driven by the element's 32-bit random word w: the

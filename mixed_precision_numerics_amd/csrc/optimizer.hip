@@ -44,8 +44,12 @@ __device__ __forceinline__ uint32_t nonfinite_word(uint32_t w) {
   }
 }
 
+// Vector path: work-group b scans the contiguous 16-byte words
+// [b * chunk, (b + 1) * chunk) with four non-temporal loads in flight per
+// thread (a grid-stride loop over the same grid ran at 6.5 TB/s).
 template <int GT, bool VEC>
 __global__ __launch_bounds__(kThreads) void check_kernel(const void* __restrict__ g, int64_t n,
+                                                         int64_t chunk,
                                                          amp_scaler_state* __restrict__ st) {
   // a block that starts after the flag is already set has nothing to add;
   // one thread reads the flag so that the whole block leaves together
@@ -60,21 +64,24 @@ __global__ __launch_bounds__(kThreads) void check_kernel(const void* __restrict_
   uint32_t bad = 0;
   const int64_t tid = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
   const int64_t nthr = static_cast<int64_t>(gridDim.x) * kThreads;
-  // four 16-byte non-temporal loads in flight per thread (read-only stream)
-  int64_t i = tid;
-  for (; i + 3 * nthr < nvec; i += 4 * nthr) {
-    u32x4 w[4];
+  if constexpr (VEC) {
+    const int64_t b0 = static_cast<int64_t>(blockIdx.x) * chunk;
+    const int64_t b1 = b0 + chunk < nvec ? b0 + chunk : nvec;
+    int64_t i = b0 + threadIdx.x;
+    for (; i + 3 * kThreads < b1; i += 4 * kThreads) {
+      u32x4 w[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) w[u] = __builtin_nontemporal_load(gv + i + u * nthr);
+      for (int u = 0; u < 4; ++u) w[u] = __builtin_nontemporal_load(gv + i + u * kThreads);
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      bad |= nonfinite_word<GT>(w[u].x) | nonfinite_word<GT>(w[u].y) |
-             nonfinite_word<GT>(w[u].z) | nonfinite_word<GT>(w[u].w);
-  }
-  for (; i < nvec; i += nthr) {
-    const u32x4 w = __builtin_nontemporal_load(gv + i);
-    bad |= nonfinite_word<GT>(w.x) | nonfinite_word<GT>(w.y) | nonfinite_word<GT>(w.z) |
-           nonfinite_word<GT>(w.w);
+      for (int u = 0; u < 4; ++u)
+        bad |= nonfinite_word<GT>(w[u].x) | nonfinite_word<GT>(w[u].y) |
+               nonfinite_word<GT>(w[u].z) | nonfinite_word<GT>(w[u].w);
+    }
+    for (; i < b1; i += kThreads) {
+      const u32x4 w = __builtin_nontemporal_load(gv + i);
+      bad |= nonfinite_word<GT>(w.x) | nonfinite_word<GT>(w.y) | nonfinite_word<GT>(w.z) |
+             nonfinite_word<GT>(w.w);
+    }
   }
   // tail elements (n not a multiple of 16 bytes)
   for (int64_t e = nvec * 16 / eb + tid; e < n; e += nthr) {
@@ -634,11 +641,13 @@ hipError_t launch_check_overflow(const void* g, int gt, int64_t n, amp_scaler_st
                                  hipStream_t s) {
   // the vector loop reads 16-byte words; an unaligned buffer uses the element loop
   const bool vec = aligned(g, 16);
+  const int64_t nvec = n * dtype_bytes(gt) / 16;
   const int64_t blocks = grid_for(vec ? (n * dtype_bytes(gt) + 15) / 16 : n);
+  const int64_t chunk = (nvec + blocks - 1) / blocks;      // 16-byte words per work-group
   const dim3 grid(static_cast<unsigned>(blocks));
-#define AMP_CHECK(T)                                                       \
-  if (vec) check_kernel<T, true><<<grid, kThreads, 0, s>>>(g, n, st);      \
-  else check_kernel<T, false><<<grid, kThreads, 0, s>>>(g, n, st);
+#define AMP_CHECK(T)                                                              \
+  if (vec) check_kernel<T, true><<<grid, kThreads, 0, s>>>(g, n, chunk, st);      \
+  else check_kernel<T, false><<<grid, kThreads, 0, s>>>(g, n, 0, st);
   switch (gt) {
     case AMP_F32: AMP_CHECK(AMP_F32) break;
     case AMP_BF16: AMP_CHECK(AMP_BF16) break;

@@ -142,6 +142,12 @@ __device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
 // ---- Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11) ---------------------
 struct ctr4 { uint32_t x, y, z, w; };
 
+// a ^ b ^ c in one instruction (gfx950's three-input bit operation; 0x96 is
+// the truth table of the three-input parity).
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+  return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
 __device__ __forceinline__ ctr4 philox4x32_10(ctr4 c, uint32_t k0, uint32_t k1) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
@@ -149,7 +155,7 @@ __device__ __forceinline__ ctr4 philox4x32_10(ctr4 c, uint32_t k0, uint32_t k1) 
     const uint64_t p1 = static_cast<uint64_t>(0xCD9E8D57u) * c.z;
     const uint32_t hi0 = static_cast<uint32_t>(p0 >> 32), lo0 = static_cast<uint32_t>(p0);
     const uint32_t hi1 = static_cast<uint32_t>(p1 >> 32), lo1 = static_cast<uint32_t>(p1);
-    c = ctr4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+    c = ctr4{xor3(hi1, c.y, k0), lo1, xor3(hi0, c.w, k1), lo0};
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }

@@ -337,9 +337,9 @@ __device__ __forceinline__ void philox_x4(uint64_t blk0, uint64_t seed, uint32_t
     for (int q = 0; q < 4; ++q) {
       const uint64_t p0 = static_cast<uint64_t>(0xD2511F53u) * x[q];
       const uint64_t p1 = static_cast<uint64_t>(0xCD9E8D57u) * z[q];
-      x[q] = static_cast<uint32_t>(p1 >> 32) ^ y[q] ^ k0;
+      x[q] = xor3(static_cast<uint32_t>(p1 >> 32), y[q], k0);
       y[q] = static_cast<uint32_t>(p1);
-      z[q] = static_cast<uint32_t>(p0 >> 32) ^ v[q] ^ k1;
+      z[q] = xor3(static_cast<uint32_t>(p0 >> 32), v[q], k1);
       v[q] = static_cast<uint32_t>(p0);
     }
     k0 += 0x9E3779B9u;

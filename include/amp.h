@@ -340,7 +340,11 @@ int amp_delayed_scaling_update(amp_fp8_meta* d_metas, float* d_history, int32_t 
  *    amax is 0 or not finite), dec = 1/enc}; pass &d_tensor[2] as the GEMM
  *    alpha.
  * Element: b = block amax; S = E4M3(fl32(fl32(b/6)*enc)); y = fl32(z*fl32(enc/S));
- *    code = E2M1(y) saturating at 6 (S == 0 gives code 0). */
+ *    code = E2M1(y) saturating at 6 (S == 0 gives code 0).
+ * Range: for a tensor amax below about 2^-107 (enc = 2688/amax beyond
+ *    2^118), enc/S overflows to inf and a zero element gives y = NaN; the
+ *    code of such an element is that of magnitude 6 with an unspecified sign.
+ *    Every other input is quantized exactly as described. */
 int amp_nvfp4_quantize(const void* x, int xt, int64_t rows, int64_t cols, int64_t ldx,
                        int transpose, int block2d, int rht, uint64_t rht_seed,
                        int rnd, uint64_t sr_seed, uint8_t* q, uint8_t* scales,

@@ -185,7 +185,7 @@ __global__ __launch_bounds__(kFlatThreads) void cast_flat(const void* __restrict
   if (AMAX) {
     am = block_max_u32<kFlatThreads>(am, red);
     if (threadIdx.x == 0 && am != 0)
-      atomicMax(reinterpret_cast<unsigned int*>(d_amax), canon_amax(am));
+      amax_update(d_amax, am);
   }
 }
 
@@ -324,7 +324,7 @@ __global__ __launch_bounds__(kTileThreads) void cast_tile(
   if constexpr (SAT) add_sat(ns, d_sat);
   if (AMAX) {
     am = block_max_u32<kTileThreads>(am, red);
-    if (t == 0 && am != 0) atomicMax(reinterpret_cast<unsigned int*>(d_amax), canon_amax(am));
+    if (t == 0 && am != 0) amax_update(d_amax, am);
   }
 }
 
@@ -430,7 +430,7 @@ __global__ __launch_bounds__(kFlatThreads) void amax_kernel(const void* __restri
   }
   am = block_max_u32<kFlatThreads>(am, red);
   if (threadIdx.x == 0 && am != 0)
-    atomicMax(reinterpret_cast<unsigned int*>(d_amax), canon_amax(am));
+    amax_update(d_amax, am);
 }
 
 __global__ void meta_zero_amax(amp_fp8_meta* mt) {

@@ -41,6 +41,17 @@ __device__ __forceinline__ uint32_t canon_amax(uint32_t m) {
   return m > 0x7f800000u ? 0x7fc00000u : m;
 }
 
+// *d_amax = max(*d_amax, m) on FP32 bit patterns (m canonicalized).  The
+// stored value only grows, so a read of at least m proves the atomic
+// unneeded: work-groups whose maximum is already covered skip it, and the
+// atomics of thousands of work-groups no longer queue on one address (on a
+// 235 M-element cast they had cost 60-85 us of 200).
+__device__ __forceinline__ void amax_update(void* d_amax, uint32_t m) {
+  const uint32_t c = canon_amax(m);
+  unsigned int* p = static_cast<unsigned int*>(d_amax);
+  if (c > __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) atomicMax(p, c);
+}
+
 // Element sizes of the ABI dtypes (E2M1X2: one byte holds two elements).
 inline int dtype_bytes(int dt) {
   switch (dt) {

@@ -197,7 +197,7 @@ __global__ __launch_bounds__(kT) void nvfp4_kernel(const void* __restrict__ x, i
 
   if constexpr (!PASS2) {
     am = block_max_u32<kT>(am, red);
-    if (t == 0 && am != 0) atomicMax(reinterpret_cast<unsigned int*>(d_tensor), canon_amax(am));
+    if (t == 0 && am != 0) amax_update(d_tensor, am);
   } else {
     if (gr < R) {
       const int64_t kq = (k0 + 64 * g) / 2;           // byte offset of this thread's codes
@@ -474,7 +474,7 @@ __global__ __launch_bounds__(kT) void nvfp4_vec_kernel(
   if constexpr (!PASS2) {
     am = block_max_u32<kT>(am, red);
     if (threadIdx.x == 0 && am != 0)
-      atomicMax(reinterpret_cast<unsigned int*>(d_tensor), canon_amax(am));
+      amax_update(d_tensor, am);
   }
 }
 

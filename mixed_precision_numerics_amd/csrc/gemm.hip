@@ -606,6 +606,54 @@ __device__ __forceinline__ void sched_half() {
   }
 }
 
+// Epilogue through LDS: a wave's MB x NB accumulator blocks of 32x32 (lane l
+// holds column l%32 and rows 8*(r/4) + 4*(l/32) + r%4 in element r) leave as
+// whole rows of 16-byte non-temporal stores instead of 2- or 4-byte ones.
+// One 32-row band at a time goes through this wave's LDS region `buf` (32
+// rows; the pitch is the row's bytes + 32, which puts the two half-waves'
+// writes on disjoint banks); the block barriers around each band keep every
+// wave's region clear of the main loop's fragment reads and of the previous
+// band.  C and its rows must be 16-byte aligned.  (The output address is a
+// running per-lane pointer: computing it from the tile origin in every pass
+// left the compiler short of scalar registers for the direct-to-LDS loads.)
+template <int CT, int MB, int NB>
+__device__ __forceinline__ void store_tile_lds(const f32x16 (&acc)[MB][NB], float alpha, void* C, int64_t ldc,
+                                               int64_t row0, int64_t col0, uint8_t* buf) {
+  constexpr int kES = CT == AMP_F32 ? 4 : 2;
+  constexpr int kRow = NB * 32 * kES;
+  constexpr int kPitch = kRow + 32;
+  constexpr int kLPR = kRow / 16;   // lanes per row on the way out
+  constexpr int kRPP = 64 / kLPR;   // rows per pass
+  const int lane = threadIdx.x & 63, l32 = lane & 31, h = lane >> 5;
+  const int64_t ld_b = ldc * kES;
+  uint8_t* out = static_cast<uint8_t*>(C) + row0 * ld_b + col0 * kES + (lane / kLPR) * ld_b + (lane % kLPR) * 16;
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    __syncthreads();
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        uint8_t* p = buf + (8 * (r >> 2) + 4 * h + (r & 3)) * kPitch + (nb * 32 + l32) * kES;
+        const float x = acc[mb][nb][r] * alpha;
+        if constexpr (CT == AMP_F32) *reinterpret_cast<float*>(p) = x;
+        else if constexpr (CT == AMP_BF16) *reinterpret_cast<uint16_t*>(p) = static_cast<uint16_t>(f32_to_bf16(x));
+        else *reinterpret_cast<uint16_t*>(p) = static_cast<uint16_t>(f32_to_f16(x));
+      }
+    __syncthreads();
+#pragma unroll
+    for (int ps = 0; ps < 32 / kRPP; ++ps) {
+      const int row = ps * kRPP + lane / kLPR, seg = lane % kLPR;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(buf + row * kPitch + seg * 16);
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(out + (mb * 32 + ps * kRPP) * ld_b));
+    }
+  }
+}
+
+// LDS bytes of one wave's band in store_tile_lds
+template <int CT, int NB>
+constexpr int store_band_bytes() { return 32 * (NB * 32 * (CT == AMP_F32 ? 4 : 2) + 32); }
+
 // Every tile full; 16-bit operands may be K- or M/N-contiguous (FP8 ones are
 // K-contiguous).  Per K-step: the loads of the
 // next step go straight to the idle LDS stage; the fragments of slice s+1 are
@@ -691,26 +739,54 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
   // low 4 registers only (the high half is left undefined)
   using Frag = typename std::conditional<PATH == kPF8Native || PATH == kPMX8 || PATH == kPMX4,
                                          i32x8, u32x4>::type;
-  // MX: this lane's UE8M0 block scales of the step for its 4 rows of A and B
-  // (row wm*128 + mb*32 + l%32): 4 bytes (FP8, 4 blocks) or 8 (FP4, 8 blocks)
-  constexpr int kSW = PATH == kPMX4 ? 2 : 1;                       // scale dwords per row
-  uint32_t scA[4][kSW], scB[4][kSW], nscA[4][kSW], nscB[4][kSW];
-  auto load_scales = [&](int64_t kt, uint32_t (&a)[4][kSW], uint32_t (&b)[4][kSW]) {
-    if constexpr (kMX) {
+  // MX FP8: this lane's UE8M0 block scales of the step for its 4 rows of A and
+  // B (row wm*128 + mb*32 + l%32): 4 bytes, one per 32-K block
+  uint32_t scA[4], scB[4], nscA[4], nscB[4];
+  auto load_scales = [&](int64_t kt, uint32_t (&a)[4], uint32_t (&b)[4]) {
+    if constexpr (PATH == kPMX8 || PATH == kPMX8E) {
       const int64_t kc = kt < nk ? kt : nk - 1;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
-        const uint8_t* pa = g.sA + (m0 + wm * 128 + mb * 32 + (lane & 31)) * g.ldsA + kc * 4 * kSW;
-        const uint8_t* pb = g.sB + (n0 + wn * 128 + mb * 32 + (lane & 31)) * g.ldsB + kc * 4 * kSW;
-        if constexpr (kSW == 2) {
-          const u32x2 va = *reinterpret_cast<const u32x2*>(pa);
-          const u32x2 vb = *reinterpret_cast<const u32x2*>(pb);
-          a[mb][0] = va[0]; a[mb][kSW - 1] = va[1];
-          b[mb][0] = vb[0]; b[mb][kSW - 1] = vb[1];
-        } else {
-          a[mb][0] = *reinterpret_cast<const uint32_t*>(pa);
-          b[mb][0] = *reinterpret_cast<const uint32_t*>(pb);
-        }
+        a[mb] = *reinterpret_cast<const uint32_t*>(g.sA + (m0 + wm * 128 + mb * 32 + (lane & 31)) * g.ldsA + kc * 4);
+        b[mb] = *reinterpret_cast<const uint32_t*>(g.sB + (n0 + wn * 128 + mb * 32 + (lane & 31)) * g.ldsB + kc * 4);
+      }
+    }
+  };
+  // MXFP4: the scales of steps 2p and 2p+1 come with one 8-byte load per row
+  // and lane, lane half h reading step 2p + h (both halves used to read the
+  // same step, and these loads, one cache line per row, cost more than the
+  // tile's own).  A lane needs bytes 2ks + h (ks = 0..3) of a step's 8: the
+  // lane packs its half's bytes of the step it read into one dword, the other
+  // half's into another, and one swap across the lane halves hands each lane
+  // its bytes of the other step.  Byte ks of a packed dword is the scale of
+  // K-block 2ks + h.
+  uint32_t p4A[4][2], p4B[4][2], r4A[4][2], r4B[4][2];  // packed [mb][step & 1]; raw
+  auto load_pair = [&](int64_t p) {
+    if constexpr (PATH == kPMX4) {
+      int64_t kc = 2 * p + h;
+      kc = kc < nk ? kc : nk - 1;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const u32x2 va = *reinterpret_cast<const u32x2*>(g.sA + (m0 + wm * 128 + mb * 32 + (lane & 31)) * g.ldsA + kc * 8);
+        const u32x2 vb = *reinterpret_cast<const u32x2*>(g.sB + (n0 + wn * 128 + mb * 32 + (lane & 31)) * g.ldsB + kc * 8);
+        r4A[mb][0] = va[0]; r4A[mb][1] = va[1];
+        r4B[mb][0] = vb[0]; r4B[mb][1] = vb[1];
+      }
+    }
+  };
+  auto unpack_pair = [&]() {
+    if constexpr (PATH == kPMX4) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        // even bytes (lane half 0's) and odd bytes (half 1's) of the 8
+        const auto sa = __builtin_amdgcn_permlane32_swap(__builtin_amdgcn_perm(r4A[mb][1], r4A[mb][0], 0x06040200u),
+                                                         __builtin_amdgcn_perm(r4A[mb][1], r4A[mb][0], 0x07050301u),
+                                                         false, false);
+        const auto sb = __builtin_amdgcn_permlane32_swap(__builtin_amdgcn_perm(r4B[mb][1], r4B[mb][0], 0x06040200u),
+                                                         __builtin_amdgcn_perm(r4B[mb][1], r4B[mb][0], 0x07050301u),
+                                                         false, false);
+        p4A[mb][0] = sa[0]; p4A[mb][1] = sa[1];
+        p4B[mb][0] = sb[0]; p4B[mb][1] = sb[1];
       }
     }
   };
@@ -784,13 +860,19 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
   };
   load_part(0, 0, smem0[0]);
   load_part(0, 1, smem0[0]);
-  load_scales(0, scA, scB);
+  if constexpr (PATH == kPMX4) load_pair(0); else load_scales(0, scA, scB);
   load_nv(0, nvA, nvB);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
+  unpack_pair();
   frag(smem0[0], 0, fa[0], fb[0]);
-  auto step = [&](int64_t kt, const uint8_t* st, uint8_t* nst) __attribute__((always_inline)) {
-    load_scales(kt + 1, nscA, nscB);
+  // par = kt & 1 (a constant at every call site of the MXFP4 path)
+  auto step = [&](int64_t kt, const uint8_t* st, uint8_t* nst, int par) __attribute__((always_inline)) {
+    if constexpr (PATH == kPMX4) {
+      if (par == 0) load_pair(kt / 2 + 1);
+    } else {
+      load_scales(kt + 1, nscA, nscB);
+    }
     load_nv(kt + 1, nnvA, nnvB);
     // The next step's scales are consumed only after the closing barrier;
     // left to itself the scheduler sinks their loads to just before that
@@ -863,8 +945,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
         for (int mb = 0; mb < 4; ++mb) {
           float sa = 1.0f, sb = 1.0f;
           if constexpr (PATH == kPMX8E) {
-            sa = e8m0_scale((scA[mb][0] >> (8 * ks)) & 0xffu);
-            sb = e8m0_scale((scB[mb][0] >> (8 * ks)) & 0xffu);
+            sa = e8m0_scale((scA[mb] >> (8 * ks)) & 0xffu);
+            sb = e8m0_scale((scB[mb] >> (8 * ks)) & 0xffu);
           }
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
@@ -899,15 +981,15 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
             // byte 2ks of (scale dword >> 8*(l/32))
             constexpr int fa_ = AT == AMP_E4M3 ? 0 : 1;
             constexpr int fb_ = BT == AMP_E4M3 ? 0 : 1;
-            const int sa = static_cast<int>(scA[mb][0] >> (8 * h));
-            const int sb = static_cast<int>(scB[nb][0] >> (8 * h));
+            const int sa = static_cast<int>(scA[mb] >> (8 * h));
+            const int sb = static_cast<int>(scB[nb] >> (8 * h));
             acc[mb][nb] = mfma_scaled<fa_, fb_>(fa[cur][mb], fb[cur][nb], acc[mb][nb], sa, sb, 2 * ks);
           } else if constexpr (PATH == kPMX4) {
             // E2M1 (format 4): 16 bytes = 32 K per lane in the low 4 dwords
             const i32x8 av = fa[cur][mb], bv = fb[cur][nb];
-            const int sa = static_cast<int>(scA[mb][ks >> 1] >> (8 * h));
-            const int sb = static_cast<int>(scB[nb][ks >> 1] >> (8 * h));
-            acc[mb][nb] = mfma_scaled<4, 4>(av, bv, acc[mb][nb], sa, sb, 2 * (ks & 1));
+            const int sa = static_cast<int>(p4A[mb][par]);
+            const int sb = static_cast<int>(p4B[nb][par]);
+            acc[mb][nb] = mfma_scaled<4, 4>(av, bv, acc[mb][nb], sa, sb, ks);
           } else if constexpr (AT == AMP_F16) {
             acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, fa[cur][mb]),
                                                                  __builtin_bit_cast(f16x8_t, fb[cur][nb]),
@@ -941,14 +1023,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
     // and the register copies stay after the barrier (whose vmcnt(0) they
     // then need not add to)
     if constexpr (kMX || PATH == kPFP4D) __builtin_amdgcn_sched_barrier(0);
-    if constexpr (kMX) {
+    if constexpr (PATH == kPMX4) {
+      if (par == 1) unpack_pair();
+    } else if constexpr (kMX) {
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int w = 0; w < kSW; ++w) {
-          scA[mb][w] = nscA[mb][w];
-          scB[mb][w] = nscB[mb][w];
-        }
+      for (int mb = 0; mb < 4; ++mb) {
+        scA[mb] = nscA[mb];
+        scB[mb] = nscB[mb];
+      }
     }
     if constexpr (PATH == kPFP4D) {
 #pragma unroll
@@ -962,28 +1044,36 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
     // long step bodies without scheduling hints: one step per iteration,
     // stages chosen at run time (measured faster for the first two)
     for (int64_t kt = 0; kt < nk; ++kt)
-      step(kt, (kt & 1) ? smem1[0] : smem0[0], (kt & 1) ? smem0[0] : smem1[0]);
+      step(kt, (kt & 1) ? smem1[0] : smem0[0], (kt & 1) ? smem0[0] : smem1[0], static_cast<int>(kt & 1));
   } else {
     // two steps per iteration, each naming its stages statically
     int64_t kt = 0;
     for (; kt + 1 < nk; kt += 2) {
-      step(kt, smem0[0], smem1[0]);
-      step(kt + 1, smem1[0], smem0[0]);
+      step(kt, smem0[0], smem1[0], 0);
+      step(kt + 1, smem1[0], smem0[0], 1);
     }
-    if (kt < nk) step(kt, smem0[0], smem1[0]);
+    if (kt < nk) step(kt, smem0[0], smem1[0], 0);
   }
   const float alpha = (g.alphaA ? *g.alphaA : 1.0f) * (g.alphaB ? *g.alphaB : 1.0f);
+  constexpr int kES = CT == AMP_F32 ? 4 : 2;
+  if ((reinterpret_cast<uintptr_t>(g.C) & 15) == 0 && (g.ldc * kES) % 16 == 0) {
+    // waves 0-1 stage their bands in smem0, waves 2-3 in smem1
+    static_assert(2 * store_band_bytes<CT, 4>() <= 2 * kOperandBytes, "band staging exceeds a stage");
+    store_tile_lds<CT, 4, 4>(acc, alpha, g.C, g.ldc, m0 + wm * 128, n0 + wn * 128,
+                             (wave < 2 ? smem0[0] : smem1[0]) + (wave & 1) * store_band_bytes<CT, 4>());
+  } else {
 #pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-      const int64_t col = n0 + wn * 128 + nb * 32 + (lane & 31);
+      for (int nb = 0; nb < 4; ++nb) {
+        const int64_t col = n0 + wn * 128 + nb * 32 + (lane & 31);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * 128 + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        store_c<CT>(g.C, row * g.ldc + col, acc[mb][nb][r] * alpha);
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = m0 + wm * 128 + mb * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          store_c<CT>(g.C, row * g.ldc + col, acc[mb][nb][r] * alpha);
+        }
       }
-    }
+  }
 }
 
 // ---------------------------------------------------------------- generic
@@ -1233,17 +1323,25 @@ __global__ __launch_bounds__(kBwThreads, 1) void gemm_bw_d2l(BwArgs g) {
     step(kt + 1, smem1, smem0);
   }
   if (kt < nk) step(kt, smem0, smem1);
+  constexpr int kES = CT == AMP_F32 ? 4 : 2;
+  if ((reinterpret_cast<uintptr_t>(g.C) & 15) == 0 && (g.ldc * kES) % 16 == 0) {
+    // waves 0-3 stage their bands in smem0, waves 4-7 in smem1
+    static_assert(4 * store_band_bytes<CT, 2>() <= kStage, "band staging exceeds a stage");
+    store_tile_lds<CT, 2, 2>(acc, 1.0f, g.C, g.ldc, m0 + wm * 64, n0 + wn * 64,
+                             (wave < 4 ? smem0 : smem1) + (wave & 3) * store_band_bytes<CT, 2>());
+  } else {
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int64_t col = n0 + wn * 64 + nb * 32 + l32;
+      for (int nb = 0; nb < 2; ++nb) {
+        const int64_t col = n0 + wn * 64 + nb * 32 + l32;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t row = m0 + wm * 64 + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        store_c<CT>(g.C, row * g.ldc + col, acc[mb][nb][r]);
+        for (int r = 0; r < 16; ++r) {
+          const int64_t row = m0 + wm * 64 + mb * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          store_c<CT>(g.C, row * g.ldc + col, acc[mb][nb][r]);
+        }
       }
-    }
+  }
 }
 
 // Any shape: one output per thread; each K-block's exact products are summed

@@ -97,21 +97,27 @@ def bw_operand(seed, rows, k, fmt, block, std):
     return OB.quantize(synth.f32_bits(x), F.F32, fmt, block)
 
 
-def run_gemm(M, N, K, at, bt, a_block, b_block, ct, seed):
+def run_gemm(M, N, K, at, bt, a_block, b_block, ct, seed, ldc=None):
     ca, sa = bw_operand(seed, M, K, YF[at], a_block, 1.0)
     cb, sb = bw_operand(seed + 1, N, K, YF[bt], b_block, 0.02)
-    c = empty(M * N * 4)
+    ldc = ldc or N
+    c = empty(M * ldc * 4, fill=0x7F)
     amp.amp_gemm_blockwise(M, N, K, dev(ca), at, K, dev(sa.astype(np.float32)), sa.shape[1],
                            a_block, dev(cb), bt, K, dev(sb.astype(np.float32)), sb.shape[1],
-                           b_block, c, ct, N)
+                           b_block, c, ct, ldc)
     cref, mag = OB.gemm(ca, sa, YF[at], bool(a_block), cb, sb, YF[bt], bool(b_block))
     if ct == amp.F32:
-        got = host(c, np.float32)[:M * N].reshape(M, N)
+        full = host(c, np.float32)[:M * ldc].reshape(M, ldc)
+        got = full[:, :N]
         ok = OG.check_f32(got, cref, mag)
+        pad = host(c, np.uint32)[:M * ldc].reshape(M, ldc)[:, N:]
+        assert np.all(pad == 0x7F7F7F7F), "columns past N were written"
     else:
         fmt = F.BF16 if ct == amp.BF16 else F.F16
-        got = host(c, np.uint16)[:M * N].reshape(M, N)
+        full = host(c, np.uint16)[:M * ldc].reshape(M, ldc)
+        got = full[:, :N]
         ok = OG.check_rounded(got, fmt, cref, mag)
+        assert np.all(full[:, N:] == 0x7F7F), "columns past N were written"
     bad = np.argwhere(~ok)
     assert bad.size == 0, (bad[:5], got[tuple(bad[0])], cref[tuple(bad[0])], mag[tuple(bad[0])])
 
@@ -122,6 +128,15 @@ def run_gemm(M, N, K, at, bt, a_block, b_block, ct, seed):
 def test_gemm_blockwise_matrix_core_path(at, b_block, ct):
     # full 256x128 tiles, 5 K-blocks: several tiles in both directions
     run_gemm(512, 384, 640, at, amp.E4M3, 0, b_block, ct, seed=100 + at + 2 * b_block)
+
+
+@pytest.mark.parametrize("ct", [amp.F32, amp.BF16])
+@pytest.mark.parametrize("ldc_pad", [8, 3])
+def test_gemm_blockwise_matrix_core_path_padded_output_rows(ct, ldc_pad):
+    """Output rows longer than N: 16-byte aligned ones (pad 8) leave through
+    the LDS-staged row stores, others (pad 3) through element stores; the
+    columns past N stay untouched."""
+    run_gemm(256, 256, 384, amp.E4M3, amp.E4M3, 0, 1, ct, seed=130 + ldc_pad, ldc=256 + ldc_pad)
 
 
 @pytest.mark.parametrize("shape", [(300, 200, 333), (256, 128, 200), (64, 48, 128), (5, 7, 1)])

@@ -211,6 +211,27 @@ def test_gemm_interior_direct_to_lds_path(et, ct, opA, opB):
     check(out, ct, cref, bound, "d2l")
 
 
+@pytest.mark.parametrize("ct", [amp.F32, amp.BF16, amp.F16])
+@pytest.mark.parametrize("ldc_pad", [8, 3])
+def test_gemm_interior_padded_output_rows(ct, ldc_pad):
+    """Full tiles with output rows longer than N: 16-byte aligned rows (pad 8)
+    leave through the LDS-staged row stores, others (pad 3) through element
+    stores; the columns past N keep their fill."""
+    M, N, K = 512, 256, 192
+    ldc = N + ldc_pad
+    a = codes_16(amp.BF16, (M, K), 31)
+    b = codes_16(amp.BF16, (N, K), 32, 0.05)
+    c = empty(M * ldc * CT[ct][2], fill=0x7F)
+    amp.amp_gemm_ex(amp.OP_N, amp.OP_T, M, N, K, dev(a), amp.BF16, K, f32_dev([0.5]), dev(b),
+                    amp.BF16, K, None, c, ct, ldc)
+    full = host(c, CT[ct][1]).reshape(M, ldc)
+    A, B = ref_values(amp.OP_N, amp.OP_T, M, N, K, a, amp.BF16, b, amp.BF16)
+    cref, bound = OG.reference(A, B, alpha=0.5)
+    check(full[:, :N], ct, cref, bound, ("padded ldc", ldc_pad))
+    fill = 0x7F7F7F7F if ct == amp.F32 else 0x7F7F
+    assert np.all(full[:, N:] == fill), "columns past N were written"
+
+
 @pytest.mark.parametrize("fa,fb", [(amp.E4M3, amp.E4M3), (amp.E5M2, amp.E4M3)])
 def test_gemm_fp8_exact_interior(fa, fb):
     M, N, K = 256, 512, 512

@@ -115,7 +115,8 @@ def run_mx_gemm(M, N, K, at, bt, ct=amp.F32, seed=0, native=False, scales=None, 
     return host(c, np.float32).reshape(M, N).astype(np.float64), cref, bound
 
 
-@pytest.mark.parametrize("M,N,K", [(512, 768, 512), (256, 512, 768), (200, 100, 96)])
+@pytest.mark.parametrize("M,N,K", [(512, 768, 512), (256, 512, 768), (256, 256, 256), (256, 512, 1280),
+                                   (200, 100, 96)])
 def test_mxfp4_gemm_within_fp32_accumulation_bound(M, N, K):
     """E2M1 x E2M1 with UE8M0 scales: full tiles on the block-scaled matrix
     cores (products of E2M1 values are short, so the per-instruction sums are

@@ -318,6 +318,9 @@ def gemm_block_workload(torch, amp, fp8: bool, reps: int = 20, native: bool = Fa
 
 
 def cast_workload(torch, amp):
+    """The two flat casts of the cast-only workload, 2^31 elements each with
+    amax capture: BF16 -> E4M3 with a scale (3 B/elem) and FP32 -> FP16, the
+    master-weight recast (6 B/elem)."""
     n = 1 << 31
     x = torch.randn(n, device="cuda").to(torch.bfloat16)
     y = torch.empty(n, device="cuda", dtype=torch.uint8)
@@ -328,8 +331,17 @@ def cast_workload(torch, amp):
     del x, y
     torch.cuda.empty_cache()
     gbs = 3 * n / ms / 1e6
+    x32 = torch.randn(n, device="cuda")
+    y16 = torch.empty(n, device="cuda", dtype=torch.float16)
+    f32 = lambda: amp.amp_cast(x32, amp.F32, 1, n, n, y16, amp.F16, n, None, 0, None, am)
+    ms32 = _median_ms(torch, f32, 20)
+    del x32, y16
+    torch.cuda.empty_cache()
+    gbs32 = 6 * n / ms32 / 1e6
     return {"what": "BF16->E4M3 flat 2^31 with amax", "ms": round(ms, 4), "gbs": round(gbs, 1),
-            "frac": round(gbs / HBM_PEAK_GBS, 4)}
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "f32_to_f16": {"what": "FP32->FP16 flat 2^31 with amax (6 B/elem)", "ms": round(ms32, 4),
+                           "gbs": round(gbs32, 1), "frac": round(gbs32 / HBM_PEAK_GBS, 4)}}
 
 
 def _median_ms(torch, f, reps=20, warm=3):

@@ -94,6 +94,23 @@ __device__ __forceinline__ void store8(void* y, int64_t i, const uint32_t (&c)[8
   }
 }
 
+// Store 4 codes at y + i (4- or 8-byte aligned); NT as for load8.
+template <int YT, bool NT = false>
+__device__ __forceinline__ void store4(void* y, int64_t i, const uint32_t* c) {
+  if constexpr (sizeof(typename CodeT<YT>::type) == 1) {
+    const uint32_t w = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+    uint32_t* q = reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(y) + i);
+    if constexpr (NT) __builtin_nontemporal_store(w, q);
+    else *q = w;
+  } else {
+    u32x2 w;
+    w.x = c[0] | (c[1] << 16); w.y = c[2] | (c[3] << 16);
+    u32x2* q = reinterpret_cast<u32x2*>(static_cast<uint16_t*>(y) + i);
+    if constexpr (NT) __builtin_nontemporal_store(w, q);
+    else *q = w;
+  }
+}
+
 template <int YT>
 __device__ __forceinline__ void store_one(void* y, int64_t i, uint32_t c) {
   static_cast<typename CodeT<YT>::type*>(y)[i] = static_cast<typename CodeT<YT>::type>(c);
@@ -126,7 +143,12 @@ constexpr int64_t kFlatMaxBlocks = 256 * 64;   // one amax atomic per work-group
 // converts the n % 8 trailing elements.  For 2^31 BF16 -> E4M3 codes this ran
 // at 5.70 TB/s in a probe of the same access shape, against 5.45 for one
 // 16384-vector range per work-group and 4.9 for a grid-stride loop over single
-// vectors.  Scalar path: a grid-stride loop.
+// vectors.  FP32 input: a wave's 8 vectors of an unrolled step are its 512
+// consecutive elements, lane l taking elements 4l .. 4l+3 and 256+4l ..
+// 256+4l+3, so that every load and store instruction covers one contiguous
+// span (with 8 consecutive elements per lane the two loads of an instruction
+// pair each touched every other 16 bytes of a 2 KiB span).  Scalar path: a
+// grid-stride loop.
 template <int XT, int YT, bool VEC, bool SAT>
 __global__ __launch_bounds__(kFlatThreads) void cast_flat(const void* __restrict__ x,
                                                           void* __restrict__ y, int64_t n,
@@ -158,17 +180,45 @@ __global__ __launch_bounds__(kFlatThreads) void cast_flat(const void* __restrict
       store8<YT, true>(y, j * 8, c);
     };
     const int64_t stride = static_cast<int64_t>(gridDim.x) * kFlatChunk;
+    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
     for (int64_t b0 = static_cast<int64_t>(blockIdx.x) * kFlatChunk; b0 < nv; b0 += stride) {
       const int64_t b1 = b0 + kFlatChunk < nv ? b0 + kFlatChunk : nv;
-      int64_t j = b0 + threadIdx.x;
-      for (; j + (kFlatUnroll - 1) * kFlatThreads < b1; j += kFlatUnroll * kFlatThreads) {
+      int64_t jb = b0;   // the block's first vector of the step
+      for (; jb + kFlatUnroll * kFlatThreads <= b1; jb += kFlatUnroll * kFlatThreads) {
         float v[kFlatUnroll][8];
+        if constexpr (XT == AMP_F32) {
+          // e: this lane's first element of step u; the second four are 256 on
 #pragma unroll
-        for (int u = 0; u < kFlatUnroll; ++u) load8<XT, true>(x, (j + u * kFlatThreads) * 8, v[u]);
+          for (int u = 0; u < kFlatUnroll; ++u) {
+            const f32x4* q = reinterpret_cast<const f32x4*>(
+                static_cast<const float*>(x) + (jb + u * kFlatThreads) * 8 + 512 * wv + 4 * lane);
+            const f32x4 a = __builtin_nontemporal_load(q), b = __builtin_nontemporal_load(q + 64);
+            v[u][0] = a.x; v[u][1] = a.y; v[u][2] = a.z; v[u][3] = a.w;
+            v[u][4] = b.x; v[u][5] = b.y; v[u][6] = b.z; v[u][7] = b.w;
+          }
 #pragma unroll
-        for (int u = 0; u < kFlatUnroll; ++u) encode8(j + u * kFlatThreads, v[u]);
+          for (int u = 0; u < kFlatUnroll; ++u) {
+            uint32_t c[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              if (AMAX) { const uint32_t a = fbits(v[u][k]) & 0x7fffffffu; am = am > a ? am : a; }
+              const float t = SCALE ? v[u][k] * scale : v[u][k];
+              if constexpr (SAT) ns += fabsf(t) > SatMax<YT>::v;
+              c[k] = to_code<YT>(t);
+            }
+            const int64_t e = (jb + u * kFlatThreads) * 8 + 512 * wv + 4 * lane;
+            store4<YT, true>(y, e, c);
+            store4<YT, true>(y, e + 256, c + 4);
+          }
+        } else {
+          const int64_t j = jb + threadIdx.x;
+#pragma unroll
+          for (int u = 0; u < kFlatUnroll; ++u) load8<XT, true>(x, (j + u * kFlatThreads) * 8, v[u]);
+#pragma unroll
+          for (int u = 0; u < kFlatUnroll; ++u) encode8(j + u * kFlatThreads, v[u]);
+        }
       }
-      for (; j < b1; j += kFlatThreads) {
+      for (int64_t j = jb + threadIdx.x; j < b1; j += kFlatThreads) {
         float v[8];
         load8<XT, true>(x, j * 8, v);
         encode8(j, v);

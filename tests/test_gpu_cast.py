@@ -92,6 +92,56 @@ def test_flat_cast_multi_pass_ranges():
     assert host(amax, np.uint32)[0] == want_amax
 
 
+@pytest.mark.parametrize("xt,yt,scale", [(amp.BF16, amp.E4M3, 64.0), (amp.F32, amp.F16, None)])
+def test_flat_cast_full_size_2pow31_sampled(xt, yt, scale):
+    """The cast-only workload at its full size, 2^31 elements: BF16 -> E4M3
+    with a scale and FP32 -> FP16 (the master-weight recast), both with amax.
+    Inputs are generated on the device (uniform in [-2, 2) from a seeded
+    generator, then five planted values: three beyond every other magnitude,
+    one past the FP16 range, one below its normal range); the oracle gets the
+    same input bytes at the sampled indices by a device-to-host gather: every
+    range edge of the flat kernel's first and last ranges, a window around
+    each of 4096 evenly spaced range starts, the tail, 200,000 random indices
+    and the planted ones.  amax is checked against the planted values, which
+    exceed every other element's magnitude by construction."""
+    n = 1 << 31
+    gen = torch.Generator(device="cuda").manual_seed(31)
+    x = torch.rand(n, device="cuda", generator=gen)
+    x.mul_(4.0).sub_(2.0)
+    planted = torch.tensor([5, n // 2 + 3, n - 2, 777777, n - 99], device="cuda")
+    x[planted] = torch.tensor([1024.0, -5216.0, 2560.0, 70000.0, 1e-8], device="cuda")
+    if xt == amp.BF16:
+        x = x.to(torch.bfloat16)
+        xbits, ndt = x.view(torch.int16), np.uint16
+    else:
+        xbits, ndt = x.view(torch.int32), np.uint32
+    fin = IN[xt][0]
+    fout, odt = OUT[yt]
+    y = torch.empty(n * np.dtype(odt).itemsize, device="cuda", dtype=torch.uint8)
+    amax = f32_dev([0.0])
+    sc = f32_dev([scale]) if scale is not None else None
+    amp.amp_cast(x, xt, 1, n, n, y, yt, n, d_scale=sc, d_amax=amax)
+    rng = np.random.default_rng(31)
+    range_el = 8 * 2048
+    starts = np.linspace(0, n - range_el, 4096).astype(np.int64) // range_el * range_el
+    idx = np.unique(np.concatenate([
+        np.arange(0, 2 * range_el), (starts[:, None] + np.arange(-8, 8)).ravel(),
+        np.arange(n - 2 * range_el, n), rng.integers(0, n, size=200_000),
+        planted.cpu().numpy()]))
+    idx = idx[(idx >= 0) & (idx < n)]
+    it = torch.from_numpy(idx).to("cuda")
+    xs = xbits[it].cpu().numpy().view(ndt)
+    ybits = y.view(torch.int16) if odt == np.uint16 else y
+    ys = ybits[it].cpu().numpy().view(odt)
+    want, _ = OC.cast(xs, fin, fout, scale, amax_prior_bits=0)
+    bad = np.nonzero(ys != want)[0]
+    assert bad.size == 0, (idx[bad[:10]], ys[bad[:10]], want[bad[:10]])
+    pl = np.searchsorted(idx, planted.cpu().numpy())
+    _, want_amax = OC.cast(xs[pl], fin, fout, scale, amax_prior_bits=0)
+    assert host(amax, np.uint32)[0] == want_amax
+    del x, xbits, y
+
+
 @pytest.mark.parametrize("xt,yt", [(amp.BF16, amp.E4M3), (amp.BF16, amp.E5M2),
                                    (amp.F32, amp.E4M3), (amp.F32, amp.BF16),
                                    (amp.F16, amp.F16)])

@@ -238,7 +238,7 @@ def test_cast_structured_sweep_of_all_binades(yt, low, pats):
 
 @pytest.mark.parametrize("xt,yt,ld_pad,transposed", [
     (amp.BF16, amp.E4M3, 0, True), (amp.F32, amp.E4M3, 5, True), (amp.BF16, amp.E5M2, 0, False),
-    (amp.F16, amp.E5M2, 3, False)])
+    (amp.F16, amp.E5M2, 3, False), (amp.F32, amp.E5M2, 0, False)])
 def test_current_scaling_cast(xt, yt, ld_pad, transposed):
     """amp_cast_current_scaling: amax of this tensor, scale from it, cast with
     it -- meta and codes bit-exact (oracle recipe.current_scale + cast)."""
@@ -271,6 +271,46 @@ def test_current_scaling_cast(xt, yt, ld_pad, transposed):
     if transposed:
         assert np.array_equal(host(yt_buf, odt)[:rows * cols].reshape(cols, rows),
                               want.reshape(rows, cols).T)
+
+
+def test_current_scaling_amax_over_many_ranges():
+    """The amax pass of current scaling over 2^29 + 4141 BF16 elements (more
+    2048-vector ranges than work-groups, a ragged tail), generated on the
+    device: uniform in [-2, 2) plus three planted values, the largest in the
+    tail.  amax_cur and the scale equal the oracle's from the planted values;
+    the codes are checked at range edges, the tail and random indices."""
+    from oracle import recipe as OR
+    nv = 2 * 16384 * 2048 + 517
+    n = 8 * nv + 5
+    gen = torch.Generator(device="cuda").manual_seed(41)
+    x = torch.rand(n, device="cuda", generator=gen)
+    x.mul_(4.0).sub_(2.0)
+    planted = torch.tensor([3, n // 3, n - 1], device="cuda")
+    x[planted] = torch.tensor([-300.0, 700.0, -1500.0], device="cuda")
+    x = x.to(torch.bfloat16)
+    r = amp.DelayedRecipe(448.0, 1.0, 1024, amp.AMAX_MAX)
+    meta = empty(16)
+    y = torch.empty(n, device="cuda", dtype=torch.uint8)
+    amp.amp_cast_current_scaling(x, amp.BF16, 1, n, n, y, amp.E4M3, n, None, 0, r, meta)
+    pl = planted.cpu().numpy()
+    xb = x.view(torch.int16)
+    am = int(OC.amax_bits(OC.widen_to_f32_bits(xb[planted].cpu().numpy().view(np.uint16), F.BF16)))
+    sc, inv = OR.current_scale(am, 448.0, 1.0)
+    m = host(meta, amp.FP8_META_DTYPE)[0]
+    assert int(np.float32(m["amax_cur"]).view(np.uint32)) == am
+    assert m["scale"] == np.float32(sc) and m["scale_inv"] == np.float32(inv)
+    rng = np.random.default_rng(41)
+    range_el = 8 * 2048
+    idx = np.unique(np.concatenate([
+        np.arange(0, 2 * range_el), (np.arange(0, n, 64 * range_el)[:, None] + np.arange(-4, 4)).ravel(),
+        np.arange(n - 2 * range_el, n), rng.integers(0, n, size=100_000), pl]))
+    idx = idx[(idx >= 0) & (idx < n)]
+    it = torch.from_numpy(idx).to("cuda")
+    xs = xb[it].cpu().numpy().view(np.uint16)
+    want, _ = OC.cast(xs, F.BF16, F.E4M3, sc)
+    got = y[it].cpu().numpy()
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, (idx[bad[:10]], got[bad[:10]], want[bad[:10]])
 
 
 @pytest.mark.parametrize("fill", ["zero", "nan"])

@@ -753,9 +753,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
     }
   };
   // MXFP4: the scales of steps 2p and 2p+1 come with one 8-byte load per row
-  // and lane, lane half h reading step 2p + h (both halves used to read the
-  // same step, and these loads, one cache line per row, cost more than the
-  // tile's own).  A lane needs bytes 2ks + h (ks = 0..3) of a step's 8: the
+  // and lane, lane half h reading step 2p + h (with both halves reading the
+  // same step, every step cost one load per row and operand, each touching a
+  // different cache line).  A lane needs bytes 2ks + h (ks = 0..3) of a step's 8: the
   // lane packs its half's bytes of the step it read into one dword, the other
   // half's into another, and one swap across the lane halves hands each lane
   // its bytes of the other step.  Byte ks of a packed dword is the scale of

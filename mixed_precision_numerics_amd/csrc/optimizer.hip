@@ -382,14 +382,41 @@ __device__ __forceinline__ void widen8(const void* g, int64_t j, float (&x)[8]) 
   }
 }
 
+// Four consecutive gradients from element e (8- or 16-byte aligned), widened.
+template <int GT>
+__device__ __forceinline__ void widen4(const void* g, int64_t e, float* x) {
+  if constexpr (GT == AMP_F32) {
+    const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(static_cast<const float*>(g) + e));
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  } else {
+    const u32x2 w = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(g) + e));
+    const uint32_t ww[2] = {w.x, w.y};
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      if constexpr (GT == AMP_BF16) {
+        x[2 * q] = bitsf(ww[q] << 16);
+        x[2 * q + 1] = bitsf(ww[q] & 0xffff0000u);
+      } else {
+        x[2 * q] = f16_to_f32(ww[q] & 0xffffu);
+        x[2 * q + 1] = f16_to_f32(ww[q] >> 16);
+      }
+    }
+  }
+}
+
 // acc = first ? f32(g) : fl32(acc + f32(g)).  Vector path (every buffer
 // 16-byte aligned): work-group b owns the contiguous 8-element vectors
 // [b * kAccChunk, (b + 1) * kAccChunk), each thread with two vectors' loads
 // in flight before its stores, all accesses non-temporal (the accumulator is
 // next touched by the following micro-batch's pass); the last work-group also
 // does the n % 8 trailing elements (5.35 TB/s for 2^30 FP16 gradients, against
-// 5.24 for a grid-stride loop and 4.87 with 16384-vector ranges).  Scalar
-// path: a grid-stride loop.
+// 5.24 for a grid-stride loop and 4.87 with 16384-vector ranges).  In the
+// unrolled steps a wave's 8 vectors are its 512 consecutive elements, lane l
+// taking elements 4l .. 4l+3 and 256+4l .. 256+4l+3, so that every load and
+// store instruction covers one contiguous span (with 8 consecutive elements
+// per lane, each of a lane's two 16-byte accumulator accesses covered every
+// other 16 bytes of a 2 KiB span, and the counters showed 9 % more bytes
+// written than the accumulator holds).  Scalar path: a grid-stride loop.
 constexpr int64_t kAccChunk = 512;
 constexpr int kAccUnroll = 2;
 
@@ -418,16 +445,34 @@ __global__ __launch_bounds__(kThreads) void accumulate_kernel(float* __restrict_
       __builtin_nontemporal_store(lo, a4 + 2 * j);
       __builtin_nontemporal_store(hi, a4 + 2 * j + 1);
     };
-    int64_t j = b0 + threadIdx.x;
-    for (; j + (kAccUnroll - 1) * kThreads < b1; j += kAccUnroll * kThreads) {
+    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+    int64_t jb = b0;   // the block's first vector of the step
+    for (; jb + kAccUnroll * kThreads <= b1; jb += kAccUnroll * kThreads) {
       float x[kAccUnroll][8];
       f32x4 p[kAccUnroll] = {}, q[kAccUnroll] = {};
 #pragma unroll
-      for (int u = 0; u < kAccUnroll; ++u) load(j + u * kThreads, x[u], p[u], q[u]);
+      for (int u = 0; u < kAccUnroll; ++u) {
+        const int64_t e = (jb + u * kThreads) * 8 + 512 * wv + 4 * lane;
+        widen4<GT>(g, e, x[u]);
+        widen4<GT>(g, e + 256, x[u] + 4);
+        if (!first) {
+          p[u] = __builtin_nontemporal_load(a4 + e / 4);
+          q[u] = __builtin_nontemporal_load(a4 + (e + 256) / 4);
+        }
+      }
 #pragma unroll
-      for (int u = 0; u < kAccUnroll; ++u) store(j + u * kThreads, x[u], p[u], q[u]);
+      for (int u = 0; u < kAccUnroll; ++u) {
+        const int64_t e = (jb + u * kThreads) * 8 + 512 * wv + 4 * lane;
+        f32x4 lo = f32x4{x[u][0], x[u][1], x[u][2], x[u][3]}, hi = f32x4{x[u][4], x[u][5], x[u][6], x[u][7]};
+        if (!first) {
+          lo = f32x4{p[u].x + lo.x, p[u].y + lo.y, p[u].z + lo.z, p[u].w + lo.w};
+          hi = f32x4{q[u].x + hi.x, q[u].y + hi.y, q[u].z + hi.z, q[u].w + hi.w};
+        }
+        __builtin_nontemporal_store(lo, a4 + e / 4);
+        __builtin_nontemporal_store(hi, a4 + (e + 256) / 4);
+      }
     }
-    for (; j < b1; j += kThreads) {
+    for (int64_t j = jb + threadIdx.x; j < b1; j += kThreads) {
       float x[8];
       f32x4 p = {}, q = {};
       load(j, x, p, q);

@@ -535,17 +535,29 @@ __global__ __launch_bounds__(kNormThreads) void norm_kernel(const void* __restri
     const int64_t nv = n / 8;
     const int64_t b0 = static_cast<int64_t>(blockIdx.x) * chunk;
     const int64_t b1 = b0 + chunk < nv ? b0 + chunk : nv;
-    int64_t j = b0 + threadIdx.x;
-    for (; j + 3 * kNormThreads < b1; j += 4 * kNormThreads) {
+    // FP32 input: a wave's 8 vectors of a step are its 512 consecutive
+    // elements, lane l taking 4l .. 4l+3 and 256+4l .. 256+4l+3 (one
+    // contiguous span per load instruction, as in the accumulation pass)
+    const int lane = threadIdx.x & (kWave - 1), wv = threadIdx.x / kWave;
+    int64_t jb = b0;   // the block's first vector of the step
+    for (; jb + 4 * kNormThreads <= b1; jb += 4 * kNormThreads) {
       float x[4][8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) widen8<GT>(g, j + u * kNormThreads, x[u]);
+      for (int u = 0; u < 4; ++u) {
+        if constexpr (GT == AMP_F32) {
+          const int64_t e = (jb + u * kNormThreads) * 8 + 512 * wv + 4 * lane;
+          widen4<GT>(g, e, x[u]);
+          widen4<GT>(g, e + 256, x[u] + 4);
+        } else {
+          widen8<GT>(g, jb + u * kNormThreads + threadIdx.x, x[u]);
+        }
+      }
 #pragma unroll
       for (int u = 0; u < 4; ++u)
 #pragma unroll
         for (int q = 0; q < 8; ++q) add(x[u][q], q & 3);
     }
-    for (; j < b1; j += kNormThreads) {
+    for (int64_t j = jb + threadIdx.x; j < b1; j += kNormThreads) {
       float x[8];
       widen8<GT>(g, j, x);
 #pragma unroll

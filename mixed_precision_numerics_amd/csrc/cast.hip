@@ -463,7 +463,15 @@ __global__ __launch_bounds__(kFlatThreads) void amax_kernel(const void* __restri
     const uint32_t a = fbits(v) & 0x7fffffffu;
     am = am > a ? am : a;
   };
-  if constexpr (VEC) {       // contiguous rows (ldx == cols), 16-byte aligned
+  if constexpr (VEC && XT == AMP_F32) {   // 16 bytes (4 elements) per lane: one contiguous span per load
+    const int64_t n4 = n / 4;
+    const f32x4* x4 = static_cast<const f32x4*>(x);
+    for (int64_t j = tid; j < n4; j += nthr) {
+      const f32x4 v = x4[j];
+      take(v.x); take(v.y); take(v.z); take(v.w);
+    }
+    for (int64_t i = n4 * 4 + tid; i < n; i += nthr) take(load_one<XT>(x, i));
+  } else if constexpr (VEC) {       // contiguous rows (ldx == cols), 16-byte aligned
     const int64_t nv = n / 8;
     for (int64_t j = tid; j < nv; j += nthr) {
       float v[8];

@@ -245,13 +245,15 @@ __global__ __launch_bounds__(kT) void nvfp4_kernel(const void* __restrict__ x, i
 // In both, the CW-row groups of one 16-row block are G adjacent lanes, so a
 // 16x16 block amax is a G-lane xor-shuffle reduction.  A wave tile is
 // TILE_R op rows x TILE_K; a row of a tile writes 128 (transposed) or 256
-// (plain) contiguous code bytes.
-template <int XT, bool TRANS>
+// (plain) contiguous code bytes.  WIDE (the transposed operand's amax pass,
+// which has no blocks to encode): all 64 lanes across op rows, so that one
+// load instruction reads 1 KiB of one x row.
+template <int XT, bool TRANS, bool WIDE = false>
 struct VecGeom {
   static constexpr int kESize = XT == AMP_BF16 ? 2 : 4;
   static constexpr int kCW = 16 / kESize;          // op rows per lane
   static constexpr int kG = 16 / kCW;              // lanes per 16-row block
-  static constexpr int kLR = TRANS ? 8 : kG;       // lanes across op rows
+  static constexpr int kLR = TRANS ? (WIDE ? kWave : 8) : kG;   // lanes across op rows
   static constexpr int kLK = kWave / kLR;          // lanes across K
   static constexpr int kTileR = kLR * kCW;
   static constexpr int kSubK = 16 * kLK;
@@ -383,7 +385,7 @@ __global__ __launch_bounds__(kT) void nvfp4_vec_kernel(
     const uint8_t* __restrict__ xb, int64_t ldb, int64_t R, int64_t K, int64_t tiles_r,
     int64_t tiles_k, uint64_t rht_seed, uint64_t sr_seed, uint8_t* __restrict__ q,
     uint8_t* __restrict__ scales, float* __restrict__ d_tensor) {
-  using Gm = VecGeom<XT, TRANS>;
+  using Gm = VecGeom<XT, TRANS, TRANS && !PASS2>;
   __shared__ uint32_t red[kT / kWave];
   const int lane = threadIdx.x & (kWave - 1);
   const int lr = lane % Gm::kLR;
@@ -481,22 +483,25 @@ __global__ __launch_bounds__(kT) void nvfp4_vec_kernel(
 template <int XT, bool TRANS, bool BLOCK2D, bool RHT, bool SR>
 hipError_t run_vec(const void* x, int64_t ldx, int64_t R, int64_t K, uint64_t rs, uint64_t ss,
                    uint8_t* q, uint8_t* sc, float* dt, hipStream_t s) {
-  using Gm = VecGeom<XT, TRANS>;
+  using Gm = VecGeom<XT, TRANS>;                    // encode pass
+  using Ga = VecGeom<XT, TRANS, TRANS>;             // amax pass
   const int64_t tiles_r = (R + Gm::kTileR - 1) / Gm::kTileR;
   const int64_t tiles_k = (K + Gm::kTileK - 1) / Gm::kTileK;
-  const int64_t ntiles = tiles_r * tiles_k;
+  const int64_t atiles_r = (R + Ga::kTileR - 1) / Ga::kTileR;
+  const int64_t atiles_k = (K + Ga::kTileK - 1) / Ga::kTileK;
   auto* amax_pass = nvfp4_vec_kernel<XT, TRANS, false, BLOCK2D, RHT, SR>;
   auto* encode_pass = nvfp4_vec_kernel<XT, TRANS, true, BLOCK2D, RHT, SR>;
   // one wave per tile up to 2^16 waves (a longer loop per wave beyond that)
-  int64_t blocks = (ntiles + kT / kWave - 1) / (kT / kWave);
-  if (blocks > 16384) blocks = 16384;
-  const int64_t b1 = blocks, b2 = blocks;
+  auto grid = [](int64_t ntiles) {
+    int64_t blocks = (ntiles + kT / kWave - 1) / (kT / kWave);
+    return static_cast<unsigned>(blocks > 16384 ? 16384 : blocks);
+  };
   const uint8_t* xb = static_cast<const uint8_t*>(x);
   const int64_t ldb = ldx * Gm::kESize;
   zero_amax<<<1, 64, 0, s>>>(dt);
-  amax_pass<<<static_cast<unsigned>(b1), kT, 0, s>>>(xb, ldb, R, K, tiles_r, tiles_k, rs, ss, q, sc, dt);
+  amax_pass<<<grid(atiles_r * atiles_k), kT, 0, s>>>(xb, ldb, R, K, atiles_r, atiles_k, rs, ss, q, sc, dt);
   finalize_enc<<<1, 64, 0, s>>>(dt);
-  encode_pass<<<static_cast<unsigned>(b2), kT, 0, s>>>(xb, ldb, R, K, tiles_r, tiles_k, rs, ss, q, sc, dt);
+  encode_pass<<<grid(tiles_r * tiles_k), kT, 0, s>>>(xb, ldb, R, K, tiles_r, tiles_k, rs, ss, q, sc, dt);
   return hipGetLastError();
 }
 

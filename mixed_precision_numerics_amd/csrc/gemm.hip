@@ -739,11 +739,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
   // low 4 registers only (the high half is left undefined)
   using Frag = typename std::conditional<PATH == kPF8Native || PATH == kPMX8 || PATH == kPMX4,
                                          i32x8, u32x4>::type;
-  // MX FP8: this lane's UE8M0 block scales of the step for its 4 rows of A and
-  // B (row wm*128 + mb*32 + l%32): 4 bytes, one per 32-K block
+  // MX FP8 widened to BF16: this lane's UE8M0 block scales of the step for its
+  // 4 rows of A and B (row wm*128 + mb*32 + l%32): 4 bytes, one per 32-K block
   uint32_t scA[4], scB[4], nscA[4], nscB[4];
   auto load_scales = [&](int64_t kt, uint32_t (&a)[4], uint32_t (&b)[4]) {
-    if constexpr (PATH == kPMX8 || PATH == kPMX8E) {
+    if constexpr (PATH == kPMX8E) {
       const int64_t kc = kt < nk ? kt : nk - 1;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
@@ -752,38 +752,52 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
       }
     }
   };
-  // MXFP4: the scales of steps 2p and 2p+1 come with one 8-byte load per row
-  // and lane, lane half h reading step 2p + h (with both halves reading the
-  // same step, every step cost one load per row and operand, each touching a
-  // different cache line).  A lane needs bytes 2ks + h (ks = 0..3) of a step's 8: the
-  // lane packs its half's bytes of the step it read into one dword, the other
+  // MXFP4 and MX FP8 on the block-scaled instruction: the scales of steps 2p
+  // and 2p+1 come with one load per row and lane (8 bytes for E2M1, whose
+  // 256-K step spans 8 blocks; 4 for FP8), lane half h reading step 2p + h
+  // (with both halves reading the same step, every step cost one load per row
+  // and operand, each touching a different cache line).  A lane needs bytes
+  // 2ks + h of a step's scales (ks = 0..3 for E2M1, 0..1 for FP8): the lane
+  // packs its half's bytes of the step it read into one dword, the other
   // half's into another, and one swap across the lane halves hands each lane
   // its bytes of the other step.  Byte ks of a packed dword is the scale of
   // K-block 2ks + h.
+  constexpr bool kPair = PATH == kPMX4 || PATH == kPMX8;
   uint32_t p4A[4][2], p4B[4][2], r4A[4][2], r4B[4][2];  // packed [mb][step & 1]; raw
   auto load_pair = [&](int64_t p) {
-    if constexpr (PATH == kPMX4) {
+    if constexpr (kPair) {
+      constexpr int kSB = PATH == kPMX4 ? 8 : 4;           // scale bytes per row and step
       int64_t kc = 2 * p + h;
       kc = kc < nk ? kc : nk - 1;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
-        const u32x2 va = *reinterpret_cast<const u32x2*>(g.sA + (m0 + wm * 128 + mb * 32 + (lane & 31)) * g.ldsA + kc * 8);
-        const u32x2 vb = *reinterpret_cast<const u32x2*>(g.sB + (n0 + wn * 128 + mb * 32 + (lane & 31)) * g.ldsB + kc * 8);
-        r4A[mb][0] = va[0]; r4A[mb][1] = va[1];
-        r4B[mb][0] = vb[0]; r4B[mb][1] = vb[1];
+        const uint8_t* pa = g.sA + (m0 + wm * 128 + mb * 32 + (lane & 31)) * g.ldsA + kc * kSB;
+        const uint8_t* pb = g.sB + (n0 + wn * 128 + mb * 32 + (lane & 31)) * g.ldsB + kc * kSB;
+        if constexpr (PATH == kPMX4) {
+          const u32x2 va = *reinterpret_cast<const u32x2*>(pa);
+          const u32x2 vb = *reinterpret_cast<const u32x2*>(pb);
+          r4A[mb][0] = va[0]; r4A[mb][1] = va[1];
+          r4B[mb][0] = vb[0]; r4B[mb][1] = vb[1];
+        } else {
+          r4A[mb][0] = *reinterpret_cast<const uint32_t*>(pa); r4A[mb][1] = 0u;
+          r4B[mb][0] = *reinterpret_cast<const uint32_t*>(pb); r4B[mb][1] = 0u;
+        }
       }
     }
   };
   auto unpack_pair = [&]() {
-    if constexpr (PATH == kPMX4) {
+    if constexpr (kPair) {
+      // even bytes (lane half 0's) and odd bytes (half 1's) of the 8 (E2M1) or
+      // of the 4 (FP8; selector 0x0c gives a zero byte)
+      constexpr uint32_t kEven = PATH == kPMX4 ? 0x06040200u : 0x0c0c0200u;
+      constexpr uint32_t kOdd = PATH == kPMX4 ? 0x07050301u : 0x0c0c0301u;
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb) {
-        // even bytes (lane half 0's) and odd bytes (half 1's) of the 8
-        const auto sa = __builtin_amdgcn_permlane32_swap(__builtin_amdgcn_perm(r4A[mb][1], r4A[mb][0], 0x06040200u),
-                                                         __builtin_amdgcn_perm(r4A[mb][1], r4A[mb][0], 0x07050301u),
+        const auto sa = __builtin_amdgcn_permlane32_swap(__builtin_amdgcn_perm(r4A[mb][1], r4A[mb][0], kEven),
+                                                         __builtin_amdgcn_perm(r4A[mb][1], r4A[mb][0], kOdd),
                                                          false, false);
-        const auto sb = __builtin_amdgcn_permlane32_swap(__builtin_amdgcn_perm(r4B[mb][1], r4B[mb][0], 0x06040200u),
-                                                         __builtin_amdgcn_perm(r4B[mb][1], r4B[mb][0], 0x07050301u),
+        const auto sb = __builtin_amdgcn_permlane32_swap(__builtin_amdgcn_perm(r4B[mb][1], r4B[mb][0], kEven),
+                                                         __builtin_amdgcn_perm(r4B[mb][1], r4B[mb][0], kOdd),
                                                          false, false);
         p4A[mb][0] = sa[0]; p4A[mb][1] = sa[1];
         p4B[mb][0] = sb[0]; p4B[mb][1] = sb[1];
@@ -860,7 +874,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
   };
   load_part(0, 0, smem0[0]);
   load_part(0, 1, smem0[0]);
-  if constexpr (PATH == kPMX4) load_pair(0); else load_scales(0, scA, scB);
+  if constexpr (kPair) load_pair(0); else load_scales(0, scA, scB);
   load_nv(0, nvA, nvB);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
@@ -868,7 +882,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
   frag(smem0[0], 0, fa[0], fb[0]);
   // par = kt & 1 (a constant at every call site of the MXFP4 path)
   auto step = [&](int64_t kt, const uint8_t* st, uint8_t* nst, int par) __attribute__((always_inline)) {
-    if constexpr (PATH == kPMX4) {
+    if constexpr (kPair) {
       if (par == 0) load_pair(kt / 2 + 1);
     } else {
       load_scales(kt + 1, nscA, nscB);
@@ -978,12 +992,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
                                                                           fa_, fb_, 0, 127, 0, 127);
           } else if constexpr (PATH == kPMX8) {
             // lane l covers K block 2ks + l/32 of the step: its scale byte is
-            // byte 2ks of (scale dword >> 8*(l/32))
+            // byte ks of the packed dword
             constexpr int fa_ = AT == AMP_E4M3 ? 0 : 1;
             constexpr int fb_ = BT == AMP_E4M3 ? 0 : 1;
-            const int sa = static_cast<int>(scA[mb] >> (8 * h));
-            const int sb = static_cast<int>(scB[nb] >> (8 * h));
-            acc[mb][nb] = mfma_scaled<fa_, fb_>(fa[cur][mb], fb[cur][nb], acc[mb][nb], sa, sb, 2 * ks);
+            const int sa = static_cast<int>(p4A[mb][par]);
+            const int sb = static_cast<int>(p4B[nb][par]);
+            acc[mb][nb] = mfma_scaled<fa_, fb_>(fa[cur][mb], fb[cur][nb], acc[mb][nb], sa, sb, ks);
           } else if constexpr (PATH == kPMX4) {
             // E2M1 (format 4): 16 bytes = 32 K per lane in the low 4 dwords
             const i32x8 av = fa[cur][mb], bv = fb[cur][nb];
@@ -1023,7 +1037,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mfma_d2l(GemmArgs g) {
     // and the register copies stay after the barrier (whose vmcnt(0) they
     // then need not add to)
     if constexpr (kMX || PATH == kPFP4D) __builtin_amdgcn_sched_barrier(0);
-    if constexpr (PATH == kPMX4) {
+    if constexpr (kPair) {
       if (par == 1) unpack_pair();
     } else if constexpr (kMX) {
 #pragma unroll

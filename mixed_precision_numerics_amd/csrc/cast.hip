@@ -268,6 +268,12 @@ __global__ __launch_bounds__(kTileThreads) void cast_tile(
   const int64_t c_base = static_cast<int64_t>(blockIdx.x) * kTile;
   const int t = threadIdx.x;
   const int c0 = 8 * (t % 16), r0 = 8 * (t / 16);
+  // a thread's 8 columns: c0 .. c0+7, or for FP32 input 4c .. 4c+3 and
+  // 64+4c .. 64+4c+3 (c = t % 16), so that each 16-byte load instruction of
+  // a wave covers 256 contiguous bytes of a row (eight consecutive FP32
+  // columns per lane made each of its two loads touch every other 16 bytes)
+  constexpr bool kSplit = XT == AMP_F32;
+  auto col = [&](int j) { return kSplit ? (j < 4 ? 4 * (t % 16) + j : 64 + 4 * (t % 16) + (j - 4)) : c0 + j; };
   const bool full = VEC == 2 || (VEC == 1 && (r_base + kTile <= rows) && (c_base + kTile <= cols));
   uint32_t am = 0;
   // 16-bit codes are kept one per register; 8-bit ones four per register
@@ -283,11 +289,20 @@ __global__ __launch_bounds__(kTileThreads) void cast_tile(
     const int64_t c = c_base + c0;
     float v[8];
     if (full) {
-      load8<XT>(x, r * ldx + c, v);
+      if constexpr (kSplit) {
+        const float* xr = static_cast<const float*>(x) + r * ldx + c_base;
+        const f32x4 a = *reinterpret_cast<const f32x4*>(xr + col(0));
+        const f32x4 b = *reinterpret_cast<const f32x4*>(xr + col(4));
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+      } else {
+        load8<XT>(x, r * ldx + c, v);
+      }
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        v[j] = (r < rows && c + j < cols) ? load_one<XT>(x, r * ldx + c + j) : 0.0f;
+      for (int j = 0; j < 8; ++j) {
+        const int64_t cj = c_base + col(j);
+        v[j] = (r < rows && cj < cols) ? load_one<XT>(x, r * ldx + cj) : 0.0f;
+      }
     }
     uint32_t c8[8];
 #pragma unroll
@@ -307,25 +322,32 @@ __global__ __launch_bounds__(kTileThreads) void cast_tile(
     }
     if constexpr (WY) {
       if (full) {
-        store8<YT>(y, r * ldy + c, c8);
+        if constexpr (kSplit) {
+          store4<YT>(y, r * ldy + c_base + col(0), c8);
+          store4<YT>(y, r * ldy + c_base + col(4), c8 + 4);
+        } else {
+          store8<YT>(y, r * ldy + c, c8);
+        }
       } else {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (r < rows && c + j < cols) store_one<YT>(y, r * ldy + c + j, c8[j]);
+        for (int j = 0; j < 8; ++j) {
+          const int64_t cj = c_base + col(j);
+          if (r < rows && cj < cols) store_one<YT>(y, r * ldy + cj, c8[j]);
+        }
       }
     }
   }
 
   if constexpr (WYT) {
-    // transposed 8x8 sub-block -> LDS rows c0+j, columns r0..r0+7.  8-bit
+    // transposed 8x8 sub-block -> LDS rows col(j), columns r0..r0+7.  8-bit
     // codes: the 8-byte unit r0/8 of row c is stored at unit (r0/8) ^ sw(c),
     // sw(c) = 2*(c/16) mod 16 (even, so 16-byte pairs stay adjacent), which
     // spreads a wave's stores (rows 8 apart) and the row reads over the banks
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      Code* dst = lds + (c0 + j) * kPitch + r0;
+      Code* dst = lds + col(j) * kPitch + r0;
       if constexpr (kPack) {
-        dst = lds + (c0 + j) * kPitch + 8 * ((r0 / 8) ^ swz8(c0 + j));
+        dst = lds + col(j) * kPitch + 8 * ((r0 / 8) ^ swz8(col(j)));
         // column j = byte j%4 of pk[i][j/4] for rows i = 0..7, gathered with
         // byte permutes (selector s < 4: byte s of the second operand, 4..7:
         // byte s-4 of the first, 12: zero)

@@ -171,6 +171,55 @@ def _check(fn: str, status: int) -> None:
         raise AmpError(fn, status)
 
 
+# bytes per element of the whole-byte types (E2M1X2 packs two per byte and is
+# not size-checked here)
+_EB = {F32: 4, F16: 2, BF16: 2, E4M3: 1, E5M2: 1}
+
+
+def _mat(rows, cols, ld, dt) -> int:
+    """Bytes a row-major [rows, cols] operand with row stride ``ld`` spans."""
+    if rows <= 0 or cols <= 0 or dt not in _EB:
+        return 0
+    return ((rows - 1) * ld + cols) * _EB[dt]
+
+
+def _vec(n, dt) -> int:
+    return n * _EB[dt] if n > 0 and dt in _EB else 0
+
+
+def _room(fn: str, what: str, t, nbytes: int) -> None:
+    """Raise before the launch when a torch tensor's storage, from its data
+    pointer on, holds fewer bytes than the call will touch.  The C entry
+    points take bare pointers and cannot see allocation sizes; integer
+    pointers stay the caller's responsibility."""
+    if nbytes <= 0 or t is None or not hasattr(t, "untyped_storage"):
+        return
+    st = t.untyped_storage()
+    have = st.nbytes() - (t.data_ptr() - st.data_ptr())
+    if have < nbytes:
+        raise ValueError(f"{fn}: {what} holds {have} bytes from its data pointer; "
+                         f"the call spans {nbytes}")
+
+
+def _room_cast(fn, x, xt, rows, cols, ldx, y, yt, ldy, y_t, ldy_t) -> None:
+    _room(fn, "x", x, _mat(rows, cols, ldx, xt))
+    _room(fn, "y", y, _mat(rows, cols, ldy, yt))
+    _room(fn, "y_t", y_t, _mat(cols, rows, ldy_t, yt))
+
+
+def _room_opt(fn, master, m, v, grads, gt, w16, wt, n) -> None:
+    for what, t in (("master", master), ("m", m), ("v", v)):
+        _room(fn, what, t, _vec(n, F32))
+    _room(fn, "grads", grads, _vec(n, gt))
+    _room(fn, "w16", w16, _vec(n, wt))
+
+
+def _room_gemm(fn, opA, opB, M, N, K, A, at, lda, B, bt, ldb, C, ct, ldc) -> None:
+    _room(fn, "A", A, _mat(M, K, lda, at) if opA == OP_N else _mat(K, M, lda, at))
+    _room(fn, "B", B, _mat(K, N, ldb, bt) if opB == OP_N else _mat(N, K, ldb, bt))
+    _room(fn, "C", C, _mat(M, N, ldc, ct))
+
+
 def amp_abi_version() -> int:
     return load().amp_abi_version()
 
@@ -185,6 +234,7 @@ def amp_last_hip_error() -> int:
 
 def amp_cast(x, xt, rows, cols, ldx, y, yt, ldy, y_t=None, ldy_t=0, d_scale=None, d_amax=None,
              stream=None):
+    _room_cast("amp_cast", x, xt, rows, cols, ldx, y, yt, ldy, y_t, ldy_t)
     _check("amp_cast", load().amp_cast(_ptr(x), xt, rows, cols, ldx, _ptr(y), yt, ldy,
                                        _ptr(y_t), ldy_t, _ptr(d_scale), _ptr(d_amax),
                                        _stream(stream)))
@@ -197,6 +247,7 @@ def amp_found_inf_from_amax(d_amax, n, yt, d_scale, d_state, stream=None):
 
 def amp_cast_ex(x, xt, rows, cols, ldx, y, yt, ldy, y_t=None, ldy_t=0, d_scale=None,
                 d_amax=None, d_sat_count=None, stream=None):
+    _room_cast("amp_cast_ex", x, xt, rows, cols, ldx, y, yt, ldy, y_t, ldy_t)
     _check("amp_cast_ex", load().amp_cast_ex(_ptr(x), xt, rows, cols, ldx, _ptr(y), yt, ldy,
                                              _ptr(y_t), ldy_t, _ptr(d_scale), _ptr(d_amax),
                                              _ptr(d_sat_count), _stream(stream)))
@@ -204,6 +255,7 @@ def amp_cast_ex(x, xt, rows, cols, ldx, y, yt, ldy, y_t=None, ldy_t=0, d_scale=N
 
 def amp_gemm(opA, opB, M, N, K, A, at, lda, d_alphaA, B, bt, ldb, d_alphaB, C, ct, ldc,
              bsA=None, bsB=None, stream=None):
+    _room_gemm("amp_gemm", opA, opB, M, N, K, A, at, lda, B, bt, ldb, C, ct, ldc)
     _check("amp_gemm", load().amp_gemm(
         opA, opB, M, N, K, _ptr(A), at, lda, _ptr(d_alphaA), _ptr(B), bt, ldb, _ptr(d_alphaB),
         _ptr(C), ct, ldc, ctypes.byref(bsA) if bsA is not None else None,
@@ -212,6 +264,7 @@ def amp_gemm(opA, opB, M, N, K, A, at, lda, d_alphaA, B, bt, ldb, d_alphaB, C, c
 
 def amp_gemm_ex(opA, opB, M, N, K, A, at, lda, d_alphaA, B, bt, ldb, d_alphaB, C, ct, ldc,
                 bsA=None, bsB=None, flags=0, stream=None):
+    _room_gemm("amp_gemm_ex", opA, opB, M, N, K, A, at, lda, B, bt, ldb, C, ct, ldc)
     _check("amp_gemm_ex", load().amp_gemm_ex(
         opA, opB, M, N, K, _ptr(A), at, lda, _ptr(d_alphaA), _ptr(B), bt, ldb, _ptr(d_alphaB),
         _ptr(C), ct, ldc, ctypes.byref(bsA) if bsA is not None else None,
@@ -224,6 +277,7 @@ def amp_scaler_init(d_state, init_scale=65536.0, stream=None):
 
 def amp_optimizer_step(master, m, v, grads, gt, w16, wt, n, hp: AdamWHParams, d_state,
                        flags=0, stream=None):
+    _room_opt("amp_optimizer_step", master, m, v, grads, gt, w16, wt, n)
     _check("amp_optimizer_step", load().amp_optimizer_step(
         _ptr(master), _ptr(m), _ptr(v), _ptr(grads), gt, _ptr(w16), wt, n, ctypes.byref(hp),
         _ptr(d_state), flags, _stream(stream)))
@@ -231,6 +285,7 @@ def amp_optimizer_step(master, m, v, grads, gt, w16, wt, n, hp: AdamWHParams, d_
 
 def amp_optimizer_step_ex(master, m, v, grads, gt, w16, wt, n, hp: AdamWHParams, d_state,
                           d_grad_mult=None, flags=0, stream=None):
+    _room_opt("amp_optimizer_step_ex", master, m, v, grads, gt, w16, wt, n)
     _check("amp_optimizer_step_ex", load().amp_optimizer_step_ex(
         _ptr(master), _ptr(m), _ptr(v), _ptr(grads), gt, _ptr(w16), wt, n, ctypes.byref(hp),
         _ptr(d_state), _ptr(d_grad_mult), flags, _stream(stream)))
@@ -238,6 +293,7 @@ def amp_optimizer_step_ex(master, m, v, grads, gt, w16, wt, n, hp: AdamWHParams,
 
 def amp_cast_current_scaling(x, xt, rows, cols, ldx, y, yt, ldy, y_t, ldy_t,
                              r: "DelayedRecipe", d_meta, stream=None):
+    _room_cast("amp_cast_current_scaling", x, xt, rows, cols, ldx, y, yt, ldy, y_t, ldy_t)
     _check("amp_cast_current_scaling", load().amp_cast_current_scaling(
         _ptr(x), xt, rows, cols, ldx, _ptr(y), yt, ldy, _ptr(y_t), ldy_t, ctypes.byref(r),
         _ptr(d_meta), _stream(stream)))
@@ -264,6 +320,8 @@ def amp_mx_quantize(x, xt, rows, cols, ldx, transpose, yt, q, scales, stream=Non
 
 
 def amp_grad_accumulate(acc, grads, gt, n, first, stream=None):
+    _room("amp_grad_accumulate", "acc", acc, _vec(n, F32))
+    _room("amp_grad_accumulate", "grads", grads, _vec(n, gt))
     _check("amp_grad_accumulate", load().amp_grad_accumulate(_ptr(acc), _ptr(grads), gt, n,
                                                              int(bool(first)), _stream(stream)))
 
@@ -273,11 +331,13 @@ def amp_grad_norm_init(d_norm, stream=None):
 
 
 def amp_grad_norm_accumulate(grads, gt, n, d_state, d_norm, stream=None):
+    _room("amp_grad_norm_accumulate", "grads", grads, _vec(n, gt))
     _check("amp_grad_norm_accumulate", load().amp_grad_norm_accumulate(
         _ptr(grads), gt, n, _ptr(d_state), _ptr(d_norm), _stream(stream)))
 
 
 def amp_grad_norm_accumulate_noalloc(grads, gt, n, d_state, d_sumsq, stream=None):
+    _room("amp_grad_norm_accumulate_noalloc", "grads", grads, _vec(n, gt))
     _check("amp_grad_norm_accumulate_noalloc", load().amp_grad_norm_accumulate_noalloc(
         _ptr(grads), gt, n, _ptr(d_state), _ptr(d_sumsq), _stream(stream)))
 
@@ -288,6 +348,7 @@ def amp_clip_coefficient(d_norm, max_norm, d_state, d_out, stream=None):
 
 
 def amp_check_overflow(x, xt, n, d_state, stream=None):
+    _room("amp_check_overflow", "x", x, _vec(n, xt))
     _check("amp_check_overflow", load().amp_check_overflow(_ptr(x), xt, n, _ptr(d_state),
                                                            _stream(stream)))
 
@@ -336,6 +397,8 @@ def amp_colsum_f16(x16, rows, cols, out16, stream=None):
 
 
 def amp_stream_copy(src, dst, nbytes, stream=None):
+    _room("amp_stream_copy", "src", src, nbytes)
+    _room("amp_stream_copy", "dst", dst, nbytes)
     _check("amp_stream_copy", load().amp_stream_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
 
 

@@ -74,3 +74,33 @@ def test_invalid_arguments_rejected_before_any_device_work():
     assert lib.amp_cast(None, 0, 0, 4, 4, None, 1, 4, None, 0, None, None, None) == 0
     assert lib.amp_gemm_blockwise(0, 4, 4, None, 3, 4, None, 0, 0, None, 3, 4, None, 0, 0, None,
                                   0, 4, None) == 0
+
+
+def test_binding_rejects_tensors_smaller_than_the_extents():
+    """The binding compares each torch operand's storage with the bytes the
+    call's sizes and strides span and raises before anything is launched
+    (the C entry points see bare pointers and cannot)."""
+    import torch
+    bf, u8, f32 = torch.bfloat16, torch.uint8, torch.float32
+    x = torch.zeros(8, 64, dtype=bf)
+    with pytest.raises(ValueError, match="x holds"):
+        amp.amp_cast(x, amp.BF16, 8, 448, 448, torch.zeros(8 * 448, dtype=u8), amp.E4M3, 448)
+    with pytest.raises(ValueError, match="y_t holds"):
+        amp.amp_cast(x, amp.BF16, 8, 64, 64, torch.zeros(512, dtype=u8), amp.E5M2, 64,
+                     torch.zeros(511, dtype=u8), 8)
+    # a view's span is counted from its own data pointer
+    with pytest.raises(ValueError, match="y holds"):
+        amp.amp_cast(x, amp.BF16, 8, 64, 64, torch.zeros(513, dtype=u8)[2:], amp.E4M3, 64)
+    a, b = torch.zeros(64, 32, dtype=bf), torch.zeros(16, 32, dtype=bf)
+    with pytest.raises(ValueError, match="B holds"):
+        amp.amp_gemm(amp.OP_N, amp.OP_T, 64, 32, 32, a, amp.BF16, 32, None, b, amp.BF16, 32, None,
+                     torch.zeros(64, 32, dtype=f32), amp.F32, 32)
+    with pytest.raises(ValueError, match="C holds"):
+        amp.amp_gemm(amp.OP_N, amp.OP_N, 64, 16, 32, a, amp.BF16, 32, None, b.view(32, 16),
+                     amp.BF16, 16, None, torch.zeros(64, 15, dtype=f32), amp.F32, 16)
+    p = torch.zeros(100, dtype=f32)
+    with pytest.raises(ValueError, match="v holds"):
+        amp.amp_optimizer_step(p, p, p[1:], torch.zeros(100, dtype=torch.float16), amp.F16, None,
+                               amp.F16, 100, amp.AdamWHParams(1e-3, 0.9, 0.999, 1e-8, 0.0), None)
+    with pytest.raises(ValueError, match="src holds"):
+        amp.amp_stream_copy(torch.zeros(10, dtype=u8), torch.zeros(16, dtype=u8), 16)

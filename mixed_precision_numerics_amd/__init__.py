@@ -301,6 +301,10 @@ def amp_cast_current_scaling(x, xt, rows, cols, ldx, y, yt, ldy, y_t, ldy_t,
 
 def amp_quantize_blockwise(x, xt, rows, cols, ldx, yt, block, q, ldq, s, lds, qt=None, ldqt=0,
                            st=None, ldst=0, stream=None):
+    f = "amp_quantize_blockwise"
+    _room(f, "x", x, _mat(rows, cols, ldx, xt))
+    _room(f, "q", q, _mat(rows, cols, ldq, yt))
+    _room(f, "qt", qt, _mat(cols, rows, ldqt, yt))
     _check("amp_quantize_blockwise", load().amp_quantize_blockwise(
         _ptr(x), xt, rows, cols, ldx, yt, int(block), _ptr(q), ldq, _ptr(s), lds, _ptr(qt), ldqt,
         _ptr(st), ldst, _stream(stream)))
@@ -308,12 +312,21 @@ def amp_quantize_blockwise(x, xt, rows, cols, ldx, yt, block, q, ldq, s, lds, qt
 
 def amp_gemm_blockwise(M, N, K, A, at, lda, sA, ldsA, a_block, B, bt, ldb, sB, ldsB, b_block,
                        C, ct, ldc, stream=None):
+    f = "amp_gemm_blockwise"
+    _room(f, "A", A, _mat(M, K, lda, at))
+    _room(f, "B", B, _mat(N, K, ldb, bt))
+    _room(f, "C", C, _mat(M, N, ldc, ct))
     _check("amp_gemm_blockwise", load().amp_gemm_blockwise(
         M, N, K, _ptr(A), at, lda, _ptr(sA), ldsA, int(a_block), _ptr(B), bt, ldb, _ptr(sB),
         ldsB, int(b_block), _ptr(C), ct, ldc, _stream(stream)))
 
 
 def amp_mx_quantize(x, xt, rows, cols, ldx, transpose, yt, q, scales, stream=None):
+    R, K = (cols, rows) if transpose else (rows, cols)
+    _room("amp_mx_quantize", "x", x, _mat(rows, cols, ldx, xt))
+    if R > 0 and K > 0:
+        _room("amp_mx_quantize", "q", q, R * K // 2 if yt == E2M1X2 else R * K)
+        _room("amp_mx_quantize", "scales", scales, R * (K // 32))
     _check("amp_mx_quantize", load().amp_mx_quantize(_ptr(x), xt, rows, cols, ldx,
                                                      int(transpose), yt, _ptr(q), _ptr(scales),
                                                      _stream(stream)))
@@ -370,6 +383,12 @@ def amp_delayed_scaling_update(d_metas, d_history, n, r: DelayedRecipe, stream=N
 
 def amp_nvfp4_quantize(x, xt, rows, cols, ldx, transpose, block2d, rht, rht_seed, rnd, sr_seed,
                        q, scales, d_tensor, stream=None):
+    R, K = (cols, rows) if transpose else (rows, cols)
+    _room("amp_nvfp4_quantize", "x", x, _mat(rows, cols, ldx, xt))
+    if R > 0 and K > 0:
+        _room("amp_nvfp4_quantize", "q", q, R * (K // 2))
+        _room("amp_nvfp4_quantize", "scales", scales,
+              (R // 16) * (K // 16) if block2d else R * (K // 16))
     _check("amp_nvfp4_quantize", load().amp_nvfp4_quantize(
         _ptr(x), xt, rows, cols, ldx, int(transpose), int(block2d), int(rht), rht_seed, rnd,
         sr_seed, _ptr(q), _ptr(scales), _ptr(d_tensor), _stream(stream)))

@@ -104,3 +104,18 @@ def test_binding_rejects_tensors_smaller_than_the_extents():
                                amp.F16, 100, amp.AdamWHParams(1e-3, 0.9, 0.999, 1e-8, 0.0), None)
     with pytest.raises(ValueError, match="src holds"):
         amp.amp_stream_copy(torch.zeros(10, dtype=u8), torch.zeros(16, dtype=u8), 16)
+    q = torch.zeros(64 * 32, dtype=u8)
+    with pytest.raises(ValueError, match="qt holds"):
+        amp.amp_quantize_blockwise(torch.zeros(64, 32, dtype=bf), amp.BF16, 64, 32, 32, amp.E4M3, 0,
+                                   q, 32, torch.zeros(64), 64, q[1:], 64)
+    with pytest.raises(ValueError, match="scales holds"):
+        amp.amp_mx_quantize(torch.zeros(64, 64, dtype=bf), amp.BF16, 64, 64, 64, 1, amp.E4M3,
+                            torch.zeros(64 * 64, dtype=u8), torch.zeros(127, dtype=u8))
+    with pytest.raises(ValueError, match="q holds"):
+        amp.amp_nvfp4_quantize(torch.zeros(32, 64, dtype=bf), amp.BF16, 32, 64, 64, 1, 0, 0, 0,
+                               amp.ROUND_RNE, 0, torch.zeros(64 * 16 - 1, dtype=u8),
+                               torch.zeros(64 * 2, dtype=u8), torch.zeros(3))
+    with pytest.raises(ValueError, match="A holds"):
+        amp.amp_gemm_blockwise(128, 128, 128, torch.zeros(128 * 127, dtype=u8), amp.E4M3, 128,
+                               None, 128, 0, torch.zeros(128 * 128, dtype=u8), amp.E4M3, 128,
+                               None, 1, 1, torch.zeros(128, 128), amp.F32, 128)

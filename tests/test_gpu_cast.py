@@ -146,8 +146,11 @@ def test_flat_cast_full_size_2pow31_sampled(xt, yt, scale):
                                    (amp.F32, amp.E4M3), (amp.F32, amp.BF16),
                                    (amp.F16, amp.F16)])
 @pytest.mark.parametrize("rows,cols,ldx_pad", [(300, 260, 3), (256, 384, 0), (1, 17, 0),
-                                               (129, 127, 8)])
+                                               (129, 127, 8), (304, 264, 0)])
 def test_tile_cast_with_transpose(xt, yt, rows, cols, ldx_pad):
+    """(304, 264, 0): every row 16-byte aligned on all three operands, so the
+    16-byte path runs with partial edge tiles; the other shapes take the
+    element path ((300, 260, 3), (1, 17, 0), (129, 127, 8)) or full tiles."""
     fin, ndt = IN[xt]
     fout, odt = OUT[yt]
     ldx = cols + ldx_pad

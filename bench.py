@@ -735,7 +735,7 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
+        print(f"bench.py: the hot path here runs on one GPU only (asked for --gpus {args.gpus}); "
               "the multi-GPU sharding is a design note, not an implemented path.", file=sys.stderr)
         sys.exit(2)
 

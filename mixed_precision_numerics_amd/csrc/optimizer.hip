@@ -493,7 +493,7 @@ __global__ __launch_bounds__(kThreads) void accumulate_kernel(float* __restrict_
   }
 }
 
-constexpr int kNormThreads = 1024;
+constexpr int kNormThreads = 512;
 
 // Fixed-order float64 block sum (wave xor-tree, then waves in order).
 template <int NT>
